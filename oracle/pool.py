@@ -1,0 +1,204 @@
+"""Oracle block pool, block tables, fork, append with copy-on-write, free.
+
+Test infrastructure (see the package docstring). Written for readability, not
+speed: plain Python sets, lists and dicts.
+
+Readings of the source pages used here (the pages describe the mechanism but
+print no algorithm):
+
+* Memory is paged in fixed-size blocks (Dendrite reply, vLLM comparison).
+  A pool has ``num_blocks`` blocks of ``block_size`` token slots each.
+* A fork is a shallow copy of the parent's block table: the child's table is
+  a copy of the parent's list of block ids and every listed block gains one
+  reference. No K/V is copied (same passage: "shallow pointer copy").
+* A block that is being written may not be aliased (Dendrite reply, "Why
+  Rust?"). So when a sequence appends to a partly filled last block whose
+  count is above one, the writer first takes a fresh block, copies the
+  valid slots into it, drops one reference from the old block and points its
+  table at the copy. Later tokens then fill the copy and fresh blocks.
+* Allocation takes the free block that comes first in ``alloc_order`` (by
+  default the lowest free id), so two implementations that follow the same
+  rule produce identical tables.
+* An append is all or nothing: if the pool runs dry part-way, every change
+  it made is undone and ``OOMError`` is raised.
+* Appending zero tokens writes nothing and so copies nothing.
+"""
+
+from __future__ import annotations
+
+import copy
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+class OOMError(Exception):
+    """The pool has no free block for a required allocation."""
+
+
+class InvalidError(Exception):
+    """Unknown or already freed sequence, or a bad argument."""
+
+
+class OraclePool:
+    def __init__(self, num_blocks: int, block_size: int,
+                 alloc_order: Optional[Sequence[int]] = None):
+        if num_blocks <= 0 or block_size <= 0:
+            raise InvalidError("pool sizes must be positive")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        order = list(range(num_blocks)) if alloc_order is None else [int(b) for b in alloc_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidError("alloc_order must be a permutation of the block ids")
+        self.rank = {b: i for i, b in enumerate(order)}
+        self.free_blocks = set(range(num_blocks))
+        self.ref = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.lens: Dict[int, int] = {}
+        # materialised K/V: a list of (K, V) chunks, each [L][n][Hkv][D],
+        # marked read-only; the sequence's logical K/V is their concatenation
+        # along axis 1. Chunks are never modified, so sharing them between a
+        # parent and a child is the same, by value, as a deep copy.
+        self.mat: Dict[int, List[Tuple[np.ndarray, np.ndarray]]] = {}
+        self._next_sid = 0
+        self.cow_log: List[Tuple[int, int, int]] = []   # every (src, dst, n_valid)
+
+    # ----------------------------------------------------------- internals
+    def _alloc(self) -> int:
+        if not self.free_blocks:
+            raise OOMError("pool exhausted")
+        b = min(self.free_blocks, key=self.rank.__getitem__)
+        self.free_blocks.remove(b)
+        self.ref[b] = 1
+        return b
+
+    def _check(self, sid: int) -> None:
+        if sid not in self.tables:
+            raise InvalidError(f"unknown or freed sequence {sid}")
+
+    def _snapshot(self):
+        return (set(self.free_blocks), list(self.ref), copy.deepcopy(self.tables),
+                dict(self.lens), len(self.cow_log))
+
+    def _restore(self, snap) -> None:
+        self.free_blocks, self.ref, self.tables, self.lens, ncow = snap
+        del self.cow_log[ncow:]
+
+    # ----------------------------------------------------------- verbs
+    def create(self, sid: Optional[int] = None) -> int:
+        if sid is None:
+            sid = self._next_sid
+        if sid in self.tables:
+            raise InvalidError(f"sequence {sid} exists")
+        self._next_sid = max(self._next_sid, sid + 1)
+        self.tables[sid] = []
+        self.lens[sid] = 0
+        self.mat[sid] = []
+        return sid
+
+    def fork(self, parent: int, sid: Optional[int] = None) -> int:
+        self._check(parent)
+        child = self.create(sid)
+        self.tables[child] = list(self.tables[parent])
+        for b in self.tables[child]:
+            self.ref[b] += 1
+        self.lens[child] = self.lens[parent]
+        self.mat[child] = list(self.mat[parent])
+        return child
+
+    def append(self, sid: int, k: np.ndarray, v: np.ndarray):
+        """Append ``n = k.shape[1]`` tokens. Returns (slots, cow_ops): the slot
+        (block * block_size + offset) of each new token in order, and the
+        copy-on-write operations (src, dst, n_valid) taken."""
+        self._check(sid)
+        if k.shape != v.shape or k.ndim != 4:
+            raise InvalidError("K and V must both be [L][n][Hkv][D]")
+        n = k.shape[1]
+        if n == 0:
+            return [], []
+        bs = self.block_size
+        snap = self._snapshot()
+        try:
+            table = self.tables[sid]
+            cows = []
+            r = self.lens[sid] % bs
+            if r != 0 and self.ref[table[-1]] > 1:
+                new_b = self._alloc()
+                old_b = table[-1]
+                self.ref[old_b] -= 1
+                table[-1] = new_b
+                cows.append((old_b, new_b, r))
+            slots = []
+            for _ in range(n):
+                pos = self.lens[sid]
+                if pos % bs == 0:
+                    table.append(self._alloc())
+                slots.append(table[pos // bs] * bs + pos % bs)
+                self.lens[sid] = pos + 1
+        except OOMError:
+            self._restore(snap)
+            raise
+        kc = np.array(k, copy=True)
+        vc = np.array(v, copy=True)
+        kc.flags.writeable = False
+        vc.flags.writeable = False
+        self.mat[sid] = self.mat[sid] + [(kc, vc)]
+        self.cow_log.extend(cows)
+        return slots, cows
+
+    def free(self, sid: int) -> None:
+        self._check(sid)
+        for b in self.tables[sid]:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free_blocks.add(b)
+        del self.tables[sid]
+        del self.lens[sid]
+        del self.mat[sid]
+
+    # ----------------------------------------------------------- inspection
+    def table(self, sid: int) -> List[int]:
+        self._check(sid)
+        return list(self.tables[sid])
+
+    def length(self, sid: int) -> int:
+        self._check(sid)
+        return self.lens[sid]
+
+    def refcount(self, b: int) -> int:
+        return self.ref[b]
+
+    def live(self) -> List[int]:
+        return sorted(self.tables)
+
+    def kv(self, sid: int, layer: Optional[int] = None):
+        """The materialised (K, V) of ``sid`` as float32 arrays
+        [L][len][Hkv][D], or [len][Hkv][D] for one ``layer``."""
+        self._check(sid)
+        chunks = self.mat[sid]
+        if not chunks:
+            raise InvalidError(f"sequence {sid} is empty")
+        if layer is None:
+            return (np.concatenate([c[0] for c in chunks], axis=1),
+                    np.concatenate([c[1] for c in chunks], axis=1))
+        return (np.concatenate([c[0][layer] for c in chunks], axis=0),
+                np.concatenate([c[1][layer] for c in chunks], axis=0))
+
+
+def run_trace(pool: OraclePool, ops, kv_for_op) -> Dict[int, int]:
+    """Apply a workload's op trace to ``pool``. ``kv_for_op(i)`` gives the
+    (K, V) float arrays of the append at op index ``i``. Returns the map from
+    trace sid to pool sid (they are equal here)."""
+    for i, op in enumerate(ops):
+        if op.kind == "create":
+            pool.create(op.sid)
+        elif op.kind == "fork":
+            pool.fork(op.parent, op.sid)
+        elif op.kind == "append":
+            k, v = kv_for_op(i)
+            pool.append(op.sid, k, v)
+        elif op.kind == "free":
+            pool.free(op.sid)
+        else:
+            raise InvalidError(op.kind)
+    return {s: s for s in pool.live()}

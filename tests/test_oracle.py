@@ -1,0 +1,489 @@
+"""Pins for the CPU oracle (CPU only).
+
+The oracle is checked against things other than itself: torch's
+scaled_dot_product_attention on sequences assembled straight from the trace,
+hand-derived closed forms (tests/golden/), refcount invariants and
+closed-form refcount histograms, and brute-force equivalences. A last group
+plants mistakes in the oracle and checks that these pins catch them.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import attention as oatt
+from oracle.pool import OraclePool, run_trace
+from workloads import configs, generate, get, scaled
+from workloads.configs import Shape, replace_shape
+
+from helpers import assemble_sequences, kv_for_op, run_structure
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sdpa_decode(q_heads: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """torch SDPA in float64: q [Hq][D], K/V [len][Hkv][D] -> [Hq][D]."""
+    qt = torch.from_numpy(np.asarray(q_heads, np.float64))[None, :, None, :]
+    kt = torch.from_numpy(np.asarray(K, np.float64)).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(np.asarray(V, np.float64)).permute(1, 0, 2)[None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, scale=scale, enable_gqa=True)
+    return o[0, :, 0, :].numpy()
+
+
+def build_oracle(w, inp):
+    pool = OraclePool(w.num_blocks_bound() + 4, w.shape.BS)
+    run_trace(pool, w.ops, kv_for_op(inp))
+    return pool
+
+
+# --------------------------------------------------------------------------
+# decode vs torch SDPA on independently assembled sequences
+# --------------------------------------------------------------------------
+
+SMALL_DECODE = [
+    get("tiny_a"),
+    get("tiny_b"),
+    scaled("beam", "beam_small", shape=replace_shape(configs.BEAM, L=2, Hq=8, Hkv=2, D=32),
+           root_len=96, n_branches=3, branch_len=21),
+    scaled("mcts", "mcts_small", shape=replace_shape(configs.BEAM, L=1, Hq=4, Hkv=2, D=16),
+           root_len=40, depth=3, edge_len=5),
+    scaled("agent", "agent_small", shape=replace_shape(configs.AGENT, Hq=6, Hkv=2, D=32, BS=8),
+           root_len=37, n_branches=4, branch_len=19),
+    scaled("beam_cow", "beam_cow_small", shape=replace_shape(configs.BEAM, L=2, Hq=4, Hkv=1, D=16),
+           root_len=40, n_branches=5, branch_len=3),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_DECODE, ids=lambda w: w.name)
+def test_decode_matches_sdpa(w):
+    inp = generate(w)
+    pool = build_oracle(w, inp)
+    got = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    seqs = assemble_sequences(w, inp)
+    q = inp.q.f32()
+    for b, s in enumerate(w.query_sids):
+        K, V = seqs[s]
+        for l in range(w.shape.L):
+            want = sdpa_decode(q[l, b], K[l], V[l], w.softmax_scale)
+            np.testing.assert_allclose(got[l, b], want, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_one_matches_decode():
+    w = SMALL_DECODE[2]
+    inp = generate(w)
+    pool = build_oracle(w, inp)
+    full = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    q = inp.q.f32()
+    for (l, b, h) in [(0, 0, 0), (1, 2, 7), (1, 1, 3)]:
+        one = oracle.decode_one(pool, w.query_sids[b], q[l, b, h], l, h, w.shape.Hq, w.softmax_scale)
+        np.testing.assert_allclose(one, full[l, b, h], rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# hand-derived closed forms
+# --------------------------------------------------------------------------
+
+def _frac(s):
+    return float(Fraction(s))
+
+
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "attention_closed_forms.json")))["cases"],
+                         ids=lambda c: c["name"][:40])
+def test_golden_closed_forms(case):
+    K = np.array(case["K"], np.float64)          # [len][Hkv][D]
+    V = np.array(case["V"], np.float64)
+    q = np.array(case["q"], np.float64)           # [Hq][D]
+    n, Hkv, D = K.shape
+    pool = OraclePool(4, n)
+    s = pool.create()
+    pool.append(s, K[None], V[None])
+    got = oracle.decode(pool, [s], q[None, None], case["scale"])[0, 0]
+    want = np.array([[_frac(x) for x in row] for row in case["expected"]])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+
+
+def test_single_token_returns_its_value():
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((3, 1, 2, 8)).astype(np.float32)
+    V = rng.standard_normal((3, 1, 2, 8)).astype(np.float32)
+    pool = OraclePool(2, 16)
+    s = pool.create()
+    pool.append(s, K, V)
+    q = rng.standard_normal((3, 1, 4, 8)) * 10
+    out = oracle.decode(pool, [s], q, 0.35)
+    for l in range(3):
+        for h in range(4):
+            np.testing.assert_array_equal(out[l, 0, h], V[l, 0, h // 2].astype(np.float64))
+
+
+def test_zero_query_and_equal_keys_give_mean_of_v():
+    rng = np.random.default_rng(12)
+    n = 37
+    V = rng.standard_normal((1, n, 1, 16)).astype(np.float32)
+    K = rng.standard_normal((1, n, 1, 16)).astype(np.float32)
+    pool = OraclePool(8, 8)
+    s = pool.create()
+    pool.append(s, K, V)
+    out0 = oracle.decode(pool, [s], np.zeros((1, 1, 1, 16)), 1.0)[0, 0, 0]
+    np.testing.assert_allclose(out0, V[0, :, 0].astype(np.float64).mean(axis=0), atol=1e-14)
+    Keq = np.repeat(K[:, :1], n, axis=1)
+    pool2 = OraclePool(8, 8)
+    s2 = pool2.create()
+    pool2.append(s2, Keq, V)
+    out1 = oracle.decode(pool2, [s2], rng.standard_normal((1, 1, 1, 16)) * 5, 0.7)[0, 0, 0]
+    np.testing.assert_allclose(out1, V[0, :, 0].astype(np.float64).mean(axis=0), atol=1e-14)
+
+
+def test_fork_without_append_gives_parent_output():
+    w = get("tiny_b")
+    inp = generate(w)
+    pool = build_oracle(w, inp)
+    kid = pool.fork(w.query_sids[0])
+    q = inp.q.f32()[:, :1]
+    a = oracle.decode(pool, [w.query_sids[0]], q, 0.125)
+    b = oracle.decode(pool, [kid], q, 0.125)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_mha_when_heads_equal():
+    rng = np.random.default_rng(13)
+    K = rng.standard_normal((1, 20, 3, 8)).astype(np.float32)
+    V = rng.standard_normal((1, 20, 3, 8)).astype(np.float32)
+    pool = OraclePool(4, 8)
+    s = pool.create()
+    pool.append(s, K, V)
+    q = rng.standard_normal((1, 1, 3, 8))
+    out = oracle.decode(pool, [s], q, 0.3)[0, 0]
+    for h in range(3):
+        single = OraclePool(4, 8)
+        t = single.create()
+        single.append(t, K[:, :, h:h + 1], V[:, :, h:h + 1])
+        np.testing.assert_array_equal(oracle.decode(single, [t], q[:, :, h:h + 1], 0.3)[0, 0, 0], out[h])
+
+
+# --------------------------------------------------------------------------
+# block tables: hand derivation, invariants, closed-form histograms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_a", "tiny_b"])
+def test_tiny_tables_golden(name):
+    gold = json.load(open(os.path.join(GOLDEN, "tiny_tables.json")))[name]
+    w = get(name)
+    pool = OraclePool(16, w.shape.BS)
+    first_slots = None
+    for op in w.ops:
+        if op.kind == "create":
+            pool.create(op.sid)
+        elif op.kind == "fork":
+            pool.fork(op.parent, op.sid)
+        elif op.kind == "append":
+            slots, _ = pool.append(op.sid, *(np.zeros((1, op.n, 1, 1), np.float32),) * 2)
+            if op.sid == 1:
+                first_slots = slots
+        elif op.kind == "free":
+            pool.free(op.sid)
+    for s, t in gold["tables"].items():
+        assert pool.table(int(s)) == t
+    for b, c in gold["refcounts"].items():
+        assert pool.refcount(int(b)) == c
+    assert [list(x) for x in pool.cow_log] == gold["cow_ops"]
+    assert first_slots == gold["first_branch_slots"]
+    assert all(pool.refcount(b) == 0 for b in range(12, 16))
+
+
+def histogram(pool):
+    h = {}
+    for b in range(pool.num_blocks):
+        r = pool.refcount(b)
+        if r:
+            h[r] = h.get(r, 0) + 1
+    return h
+
+
+@pytest.mark.parametrize("name,want", [
+    ("beam", {8: 128, 1: 128}),
+    ("mcts", {64: 256, 32: 4, 16: 8, 8: 16, 4: 32, 2: 64, 1: 128}),
+    ("agent", {4: 416, 1: 4096}),
+    ("tiny_a", {4: 4, 1: 4}),
+    ("verify", {1: 4 * 1026}),
+])
+def test_refcount_closed_forms(name, want):
+    """beam: 128 prompt blocks held by 8 beams + 8 x 16 private blocks.
+    mcts: the 256 root blocks are held by all 64 leaves; an edge of depth k
+    (2**k of them, 2 blocks each) by 64 / 2**k leaves. agent: 416 shared
+    blocks by 4 requests (75% fewer prefix blocks than 4 private copies)."""
+    w = get(name)
+    pool = OraclePool(w.num_blocks_bound(), w.shape.BS)
+    run_structure(pool, w)
+    assert histogram(pool) == want
+
+
+def check_invariants(pool: OraclePool):
+    counts = [0] * pool.num_blocks
+    for s in pool.live():
+        t = pool.table(s)
+        assert len(t) == -(-pool.length(s) // pool.block_size)
+        assert len(set(t)) == len(t)
+        for b in t:
+            counts[b] += 1
+    assert counts == pool.ref                                    # I1
+    used = {b for b in range(pool.num_blocks) if pool.ref[b] > 0}
+    assert used.isdisjoint(pool.free_blocks)                     # I2
+    assert used | pool.free_blocks == set(range(pool.num_blocks))
+
+
+def random_trace_run(seed: int, nb: int, bs: int, steps: int):
+    rng = np.random.default_rng(seed)
+    order = rng.permutation(nb) if seed % 2 else None
+    pool = OraclePool(nb, bs, alloc_order=order)
+    live = []
+    for _ in range(steps):
+        act = rng.integers(4) if live else 0
+        if act == 0:
+            live.append(pool.create())
+        elif act == 1:
+            p = live[rng.integers(len(live))]
+            before_t, before_l, before_m = pool.table(p), pool.length(p), list(pool.mat[p])
+            live.append(pool.fork(p))
+            assert pool.table(p) == before_t and pool.length(p) == before_l    # I5
+            assert all(a is b for a, b in zip(pool.mat[p], before_m))
+        elif act == 2:
+            s = live[rng.integers(len(live))]
+            n = int(rng.integers(0, 2 * bs + 3))
+            k = np.full((1, n, 1, 1), float(s), np.float32)
+            snap = (pool.table(s), dict(pool.lens), list(pool.ref), set(pool.free_blocks))
+            others = {o: pool.table(o) for o in pool.live() if o != s}
+            try:
+                slots, cows = pool.append(s, k, k)
+            except oracle.OOMError:
+                assert (pool.table(s), dict(pool.lens), list(pool.ref), set(pool.free_blocks)) == snap
+                continue
+            for sl in slots:                                      # I4
+                assert pool.refcount(sl // bs) == 1
+            for o, t in others.items():                           # other sequences untouched
+                assert pool.table(o) == t
+            for src, dst, nv in cows:
+                assert 0 < nv < bs and pool.refcount(dst) == 1
+        else:
+            s = live.pop(rng.integers(len(live)))
+            pool.free(s)
+        check_invariants(pool)
+    for s in live:
+        pool.free(s)
+    assert all(r == 0 for r in pool.ref)                          # I3
+    assert pool.free_blocks == set(range(nb))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_traces_keep_invariants(seed):
+    random_trace_run(seed, nb=24 + seed, bs=4 if seed % 3 else 16, steps=300)
+
+
+def test_oom_is_atomic():
+    pool = OraclePool(3, 4)
+    s = pool.create()
+    pool.append(s, *(np.zeros((1, 6, 1, 1), np.float32),) * 2)   # blocks 0, 1 (2 of 4 in block 1)
+    c = pool.fork(s)
+    snap = (pool.table(s), pool.table(c), list(pool.ref), set(pool.free_blocks))
+    with pytest.raises(oracle.OOMError):                          # needs CoW + 1 fresh = 2 > 1 free
+        pool.append(c, *(np.zeros((1, 4, 1, 1), np.float32),) * 2)
+    assert (pool.table(s), pool.table(c), list(pool.ref), set(pool.free_blocks)) == snap
+    pool.append(c, *(np.zeros((1, 2, 1, 1), np.float32),) * 2)    # CoW only: fits
+    assert pool.table(c) == [0, 2] and pool.refcount(1) == 1
+
+
+def test_materialised_sequences_follow_the_trace():
+    w = SMALL_DECODE[3]
+    inp = generate(w)
+    pool = build_oracle(w, inp)
+    seqs = assemble_sequences(w, inp)
+    assert sorted(seqs) == pool.live()
+    for s, (K, V) in seqs.items():
+        k2, v2 = pool.kv(s)
+        np.testing.assert_array_equal(k2, K)
+        np.testing.assert_array_equal(v2, V)
+
+
+# --------------------------------------------------------------------------
+# verify
+# --------------------------------------------------------------------------
+
+def _verify_setup(ctx, N, parents_fn, seed=3, Hq=4, Hkv=2, D=16, R=2):
+    rng = np.random.default_rng(seed)
+    pool = OraclePool(64, 8)
+    reqs, data = [], []
+    for r in range(R):
+        s = pool.create()
+        K = rng.standard_normal((1, ctx + N, Hkv, D)).astype(np.float32)
+        V = rng.standard_normal((1, ctx + N, Hkv, D)).astype(np.float32)
+        pool.append(s, K[:, :ctx], V[:, :ctx])
+        pool.append(s, K[:, ctx:], V[:, ctx:])
+        reqs.append(s)
+        data.append((K[0], V[0]))
+    q = rng.standard_normal((R, N, Hq, D))
+    parents = np.stack([parents_fn(N) for _ in range(R)])
+    return pool, reqs, data, q, parents
+
+
+def test_verify_chain_equals_causal_attention():
+    ctx, N, scale = 13, 7, 0.3
+    pool, reqs, data, q, parents = _verify_setup(ctx, N, lambda n: np.arange(n) - 1)
+    got = oracle.verify(pool, reqs, parents, q, scale)
+    for r, (K, V) in enumerate(data):
+        # causal attention of the N draft rows over [context + draft]: row i sees
+        # positions < ctx + i + 1
+        qt = torch.from_numpy(q[r]).permute(1, 0, 2)[None]           # 1, Hq, N, D
+        kt = torch.from_numpy(K.astype(np.float64)).permute(1, 0, 2)[None]
+        vt = torch.from_numpy(V.astype(np.float64)).permute(1, 0, 2)[None]
+        mask = torch.zeros(N, ctx + N, dtype=torch.bool)
+        for i in range(N):
+            mask[i, :ctx + i + 1] = True
+        want = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale, enable_gqa=True)
+        np.testing.assert_allclose(got[r], want[0].permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_verify_star_sees_context_and_self():
+    ctx, N, scale = 10, 5, 0.5
+    pool, reqs, data, q, parents = _verify_setup(ctx, N, lambda n: np.full(n, -1))
+    got = oracle.verify(pool, reqs, parents, q, scale)
+    for r, (K, V) in enumerate(data):
+        for i in range(N):
+            idx = list(range(ctx)) + [ctx + i]
+            want = sdpa_decode(q[r, i], K[idx], V[idx], scale)
+            np.testing.assert_allclose(got[r, i], want, rtol=1e-12, atol=1e-12)
+
+
+def test_verify_node_equals_decode_on_its_path():
+    w = scaled("verify", "verify_small", shape=replace_shape(configs.AGENT, Hq=4, Hkv=2, D=16, BS=8),
+               n_req=2, ctx_len=29, n_nodes=12, max_depth=4)
+    inp = generate(w)
+    pool = build_oracle(w, inp)
+    q = inp.q.f32()
+    got = oracle.verify(pool, w.query_sids, inp.parents, q, w.softmax_scale)
+    seqs = assemble_sequences(w, inp)
+    for r, s in enumerate(w.query_sids):
+        K, V = seqs[s]
+        ctx = K.shape[1] - w.n_nodes
+        for i in range(w.n_nodes):
+            path = []
+            j = i
+            while j != -1:
+                path.append(j)
+                j = int(inp.parents[r, j])
+            path = path[::-1]
+            dp = OraclePool(64, 8)
+            t = dp.create()
+            dp.append(t, K[:, :ctx], V[:, :ctx])
+            dp.append(t, K[:, [ctx + j for j in path]], V[:, [ctx + j for j in path]])
+            want = oracle.decode(dp, [t], q[r, i][None, None], w.softmax_scale)[0, 0]
+            np.testing.assert_allclose(got[r, i], want, rtol=1e-12, atol=1e-13)
+
+
+def test_verify_parents_are_best_first_and_bounded():
+    from workloads import verify_parents
+    for r in range(4):
+        p = verify_parents(4, r, 48, 8)
+        assert p[0] == -1
+        for i in range(1, 48):
+            assert 0 <= p[i] < i
+            assert len(oracle.ancestors(p, i)) <= 8
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each must be caught by one of the pins above
+# --------------------------------------------------------------------------
+
+def _no_scale(Q, K, V, scale):
+    return _orig_attend(Q, K, V, 1.0)
+
+
+def _no_max_shift_wrong_sign(Q, K, V, scale):
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
+    x = -(Q @ K.T) * scale
+    p = np.exp(x - x.max(axis=1, keepdims=True))
+    return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
+def _drop_last_key(Q, K, V, scale):
+    return _orig_attend(Q, K[:-1], V[:-1], scale) if len(K) > 1 else _orig_attend(Q, K, V, scale)
+
+
+def _v_unnormalised(Q, K, V, scale):
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
+    x = (Q @ K.T) * scale
+    p = np.exp(x - x.max(axis=1, keepdims=True))
+    return p @ V
+
+
+_orig_attend = oatt._softmax_attend
+
+
+@pytest.mark.parametrize("mutant", [_no_scale, _no_max_shift_wrong_sign, _drop_last_key, _v_unnormalised],
+                         ids=lambda f: f.__name__)
+def test_planted_attention_mistakes_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(oatt, "_softmax_attend", mutant)
+    with pytest.raises(AssertionError):
+        test_decode_matches_sdpa(SMALL_DECODE[0])
+
+
+def test_planted_gqa_mapping_mistake_is_caught(monkeypatch):
+    def wrong_decode(pool, sids, q, scale, layers=None):
+        L, B, Hq, D = q.shape
+        out = np.empty((L, B, Hq, D))
+        for b, s in enumerate(sids):
+            for l in range(L):
+                K, V = pool.kv(s, layer=l)
+                Hkv = K.shape[1]
+                for h in range(Hq):
+                    out[l, b, h] = _orig_attend(q[l, b, h][None], K[:, h % Hkv], V[:, h % Hkv], scale)[0]
+        return out
+    monkeypatch.setattr(oracle, "decode", wrong_decode)
+    case = json.load(open(os.path.join(GOLDEN, "attention_closed_forms.json")))["cases"][2]
+    with pytest.raises(AssertionError):
+        test_golden_closed_forms(case)
+
+
+def test_planted_cow_mistake_is_caught(monkeypatch):
+    """A pool that writes into the shared tail instead of copying it."""
+    orig_append = OraclePool.append
+
+    def no_cow_append(self, sid, k, v):
+        n = k.shape[1]
+        if n == 0:
+            return [], []
+        t = self.tables[sid]
+        slots = []
+        for _ in range(n):
+            pos = self.lens[sid]
+            if pos % self.block_size == 0:
+                t.append(self._alloc())
+            slots.append(t[pos // self.block_size] * self.block_size + pos % self.block_size)
+            self.lens[sid] = pos + 1
+        return slots, []
+    monkeypatch.setattr(OraclePool, "append", no_cow_append)
+    with pytest.raises(AssertionError):
+        test_tiny_tables_golden("tiny_b")
+    monkeypatch.setattr(OraclePool, "append", orig_append)
+
+
+def test_planted_verify_mask_mistake_is_caught(monkeypatch):
+    """Ancestors without the node itself."""
+    def no_self(parents, i):
+        j = int(parents[i])
+        res = []
+        while j != -1:
+            res.append(j)
+            j = int(parents[j])
+        return sorted(res) if res else [i]
+    monkeypatch.setattr(oatt, "ancestors", no_self)
+    with pytest.raises(AssertionError):
+        test_verify_chain_equals_causal_attention()
