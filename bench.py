@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Throughput of the copy-on-write paged KV cache on one MI355X.
+
+Default workload (beam search decode step): 8 beams forked from a
+2048-token prompt, each holding 255 private tokens; every step forks each
+beam, appends the beam's next token to the fork (its last block is shared
+and partly filled, so the append copies it on write), runs decode attention
+for all 8 forks over all 32 layers (32 query heads / 8 KV heads, head_dim
+128, block_size 16, bf16 K/V and q), then frees the forks. So one step runs
+every stage of the path: block alloc/free, fork, the append planner with
+copy-on-write, cow_copy, kv_write, the segment planner, paged attention and
+the log-sum-exp combine. The attended sequences are exactly 2048 shared +
+256 private tokens per beam.
+
+Prints one JSON line. ``value`` = unique K/V bytes the step's attention must
+read (distinct blocks x valid slots x 4096 B x 32 layers = 512 MiB) divided
+by the wall time of a step, in GB/s. ``roofline`` prices the attention
+kernel alone: the same bytes over its average duration, measured with HIP
+events on the launch stream. ``cpu_baseline`` times the CPU oracle on a
+sample of layers of the same inputs.
+
+Other workloads (``--workload mcts|agent|verify``) time the attention call
+alone on those trees; they are measurements, not the headline line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "unique-KV HBM GB/s (% of peak) and branch-queries/sec, paged decode attn"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", "kernels.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed counter runs, if they were
+    taken on the current kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("kernel_hash") != kernel_source_hash() or rec.get("kernel") != kernel:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def to_dev(t):
+    import torch
+    if t.dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(t.raw)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(t.raw).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def unique_tokens(cache, seqs) -> int:
+    valid = {}
+    for s in seqs:
+        n = cache.length(s)
+        for j, b in enumerate(cache.table(s)):
+            valid[b] = min(cache.BS, n - j * cache.BS)
+    return sum(valid.values())
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+# ------------------------------------------------------------------ beam
+
+def setup_beam(pkv, torch):
+    from workloads import generate, get
+    w = get("beam")
+    sh = w.shape
+    inp = generate(w)
+    nb = 128 + 8 * 16 + 8 + 16
+    c = pkv.PagedKVCache(nb, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D, dtype=sh.dtype)
+    root_k, root_v = inp.appends[0][2], inp.appends[0][3]
+    root = c.create()
+    c.append([root], [2048], to_dev(root_k), to_dev(root_v))
+    beams = [c.fork(root) for _ in range(8)]
+    c.free(root)
+    step_k, step_v = [], []
+    for i, b in enumerate(beams):
+        k, v = inp.appends[1 + i][2], inp.appends[1 + i][3]
+        kd, vd = to_dev(k), to_dev(v)
+        c.append([b], [255], kd[:, :255].contiguous(), vd[:, :255].contiguous())
+        step_k.append(kd[:, 255:256])
+        step_v.append(vd[:, 255:256])
+    step_k = torch.cat(step_k, dim=1).contiguous()     # [L][8][Hkv][D]
+    step_v = torch.cat(step_v, dim=1).contiguous()
+    q = to_dev(inp.q)
+    out = torch.empty((sh.L, 8, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    return w, inp, c, beams, step_k, step_v, q, out
+
+
+def beam_step(c, beams, step_k, step_v, q, out, scale, keep=False):
+    kids = [c.fork(b) for b in beams]
+    c.append(kids, [1] * len(kids), step_k, step_v)
+    c.decode(kids, q, scale=scale, out=out)
+    if keep:
+        return kids
+    for k in kids:
+        c.free(k)
+    return None
+
+
+def cpu_baseline_beam(w, inp, budget_s: float):
+    """The oracle (float64 numpy) on the same inputs, a sample of layers."""
+    import oracle
+    from oracle.pool import OraclePool, run_trace
+    kv = {i: (k, v) for i, _s, k, v in inp.appends}
+    pool = OraclePool(w.num_blocks_bound() + 8, w.shape.BS)
+    run_trace(pool, w.ops, lambda i: (kv[i][0].f32(), kv[i][1].f32()))
+    q = inp.q.f32()
+    sids = list(w.query_sids)
+    # whole passes over all layers until the time budget is used (at least one)
+    layers = list(range(w.shape.L))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode(pool, sids, q, w.softmax_scale, layers=layers)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or dt / reps * (reps + 1) > 2 * budget_s:
+            break
+    return reps, dt
+
+
+def run_beam(args, pkv, torch):
+    w, inp, c, beams, step_k, step_v, q, out = setup_beam(pkv, torch)
+    sh = w.shape
+    scale = w.softmax_scale
+    # plan facts, from a step kept alive
+    kids = beam_step(c, beams, step_k, step_v, q, out, scale, keep=True)
+    torch.cuda.synchronize()
+    uniq_tok = unique_tokens(c, kids)
+    info = c.plan_info(kids)
+    assert info["unique_tokens"] == uniq_tok, (info, uniq_tok)
+    for k in kids:
+        c.free(k)
+    uniq_bytes = uniq_tok * sh.token_kv_bytes * sh.L
+    for _ in range(args.warmup):
+        beam_step(c, beams, step_k, step_v, q, out, scale)
+    torch.cuda.synchronize()
+    for kname in ("attention", "combine", "cow_copy", "kv_write"):
+        c.timing_read(kname)
+    c.set_option("timing", 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        beam_step(c, beams, step_k, step_v, q, out, scale)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    c.set_option("timing", 0)
+    ktimes = {k: c.timing_read(k) for k in ("attention", "combine", "cow_copy", "kv_write")}
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+    ms_step = dt / args.steps * 1e3
+    value = uniq_bytes / (dt / args.steps) / 1e9
+    attn_ms, attn_n = ktimes["attention"]
+    attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
+    achieved = uniq_bytes / attn_avg_s / 1e9
+    traffic = measured_traffic("beam", "attn_mfma_kernel")
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "beam search decode step: 8 beams x (2048 shared + 256 private tokens), "
+                               "fork + copy-on-write append + attention over 32 layers + free",
+                   "beams": 8, "shared_prompt_tokens": 2048, "private_tokens": 256, "layers": 32,
+                   "q_heads": sh.Hq, "kv_heads": sh.Hkv, "head_dim": sh.D, "block_size": sh.BS,
+                   "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "branch_queries_per_s": round(8 * sh.L / (dt / args.steps), 1),
+        "unique_kv_bytes_per_step": uniq_bytes,
+        "kernel_ms": {k: round(v[0] / max(v[1], 1), 5) for k, v in ktimes.items()},
+        "plan": info,
+        "roofline": {"bound": "hbm", "kernel": "attn_mfma_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    c.close()
+    if not args.no_cpu_baseline:
+        reps, t = cpu_baseline_beam(w, inp, args.cpu_budget)
+        res["cpu_baseline"] = {
+            "value": round(uniq_bytes * reps / t / 1e9, 4), "unit": "GB/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{reps} full oracle decode pass(es) of the 8 beams x 32 layers "
+                      f"({t:.1f} s), same inputs, float64 numpy",
+            "branch_queries_per_s": round(8 * sh.L * reps / t, 1)}
+    return res
+
+
+def calibrate_copy(torch):
+    """A plain device copy of known size, for scaling the HBM counters."""
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------- other trees
+
+def run_tree(args, pkv, torch):
+    from workloads import generate, get
+    w = get(args.workload)
+    sh = w.shape
+    inp = generate(w)
+    c = pkv.PagedKVCache(w.num_blocks_bound() + 8, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D, dtype=sh.dtype)
+    kv = {i: (k, v) for i, _s, k, v in inp.appends}
+    h = {}
+    for i, op in enumerate(w.ops):
+        if op.kind == "create":
+            h[op.sid] = c.create()
+        elif op.kind == "fork":
+            h[op.sid] = c.fork(h[op.parent])
+        elif op.kind == "append":
+            c.append([h[op.sid]], [op.n], to_dev(kv[i][0]), to_dev(kv[i][1]))
+        else:
+            c.free(h.pop(op.sid))
+    seqs = [h[s] for s in w.query_sids]
+    q = to_dev(inp.q)
+    uniq_bytes = unique_tokens(c, seqs) * sh.token_kv_bytes * sh.L
+    if w.kind == "verify":
+        out = torch.empty((len(seqs), w.n_nodes, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+        fn = lambda: c.verify(seqs, inp.parents, q, scale=w.softmax_scale, out=out)  # noqa: E731
+        n_queries = len(seqs) * w.n_nodes
+        kernel = "attn_mfma_kernel"
+    else:
+        out = torch.empty((sh.L, len(seqs), sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+        fn = lambda: c.decode(seqs, q, scale=w.softmax_scale, out=out)  # noqa: E731
+        n_queries = len(seqs) * sh.L
+        kernel = "attn_mfma_kernel"
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    c.timing_read("attention")
+    c.timing_read("combine")
+    c.set_option("timing", 1)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    c.set_option("timing", 0)
+    am, an = c.timing_read("attention")
+    cm, cn = c.timing_read("combine")
+    attn_s = am / max(an, 1) / 1e3
+    achieved = uniq_bytes / attn_s / 1e9
+    res = {
+        "metric": METRIC, "value": round(uniq_bytes / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.note}", "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * uniq_bytes / dt / 1e9 / HBM_PEAK_GBS, 2),
+        "branch_queries_per_s": round(n_queries / dt, 1),
+        "unique_kv_bytes_per_step": uniq_bytes,
+        "kernel_ms": {"attention": round(am / max(an, 1), 5), "combine": round(cm / max(cn, 1), 5)},
+        "plan": c.plan_info(seqs) if w.kind == "decode" else None,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, kernel)},
+    }
+    c.close()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="beam", choices=["beam", "mcts", "agent", "verify"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_amd as pkv
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    if args.workload == "beam":
+        res = run_beam(args, pkv, torch)
+    else:
+        res = run_tree(args, pkv, torch)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,260 @@
+/*
+ * pkv.h -- C ABI of libpkv: a copy-on-write paged KV cache for
+ * tree-structured decoding (beam search, MCTS, speculative draft trees,
+ * agents sharing a prompt) on AMD MI355X (gfx950).
+ *
+ * Sources for the semantics (the pages describe the mechanism, not an API):
+ *   [D1] Dendrite author's reply, "How is this different from vLLM's paged
+ *        attention?": KV memory paged in fixed blocks; forking a beam or MCTS
+ *        node is a shallow copy of the block table through copy-on-write,
+ *        not a copy of the cache.
+ *   [D2] Dendrite author's reply, "Why Rust?": a block that is being written
+ *        must never be aliased.
+ *   [F4] Ferrite project page, section 04 "DFlash2 verify trees and copy
+ *        rows": drafted tokens are verified as best-first trees in one pass
+ *        of the model.
+ *
+ * Conventions (every call):
+ *   - Return value: PKV_OK (0) or a negative PKV_E_* code. On error a
+ *     message is available from pkv_last_error() (thread-local) and -- for
+ *     every host-side call -- the pool is left exactly as it was.
+ *   - No C++ exception crosses this interface.
+ *   - Ownership: the caller owns every device buffer (the K/V arenas, q,
+ *     out, new K/V, the attention workspace) and the stream. The library
+ *     owns its host metadata, a pinned host staging ring and a small device
+ *     buffer for per-call metadata (block lists, slots, copy ops), all freed
+ *     by pkv_pool_destroy.
+ *   - Device work is enqueued on the given stream (NULL = the null stream)
+ *     and is asynchronous: kernel faults surface at the caller's next
+ *     synchronisation. Use one stream per pool: a block freed on the host
+ *     may be handed out again by the next append, and only stream order
+ *     keeps earlier kernels from seeing the reuse.
+ *   - A pool is not thread-safe; serialise calls on it.
+ *
+ * Device memory layout (element type = kv_dtype):
+ *   K arena: [num_layers][num_blocks][num_kv_heads][block_size][head_dim]
+ *   V arena: [num_layers][num_blocks][num_kv_heads][head_dim][block_size]
+ *   One (layer, block, kv-head) tile is contiguous in both. V tiles are
+ *   stored transposed (token index fastest) because the token index is the
+ *   contracted index of P.V: the attention kernels then read V straight into
+ *   matrix-core operand registers with 16-byte loads. A slot id is
+ *   block * block_size + offset.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_E_INVALID (-1)     /* bad or stale handle, bad shape, double free */
+#define PKV_E_OOM (-2)         /* the pool has too few free blocks */
+#define PKV_E_HIP (-3)         /* a HIP runtime call failed */
+#define PKV_E_UNSUPPORTED (-4) /* dtype / head_dim / block_size not built */
+#define PKV_E_WORKSPACE (-5)   /* the attention workspace is too small */
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef struct pkv_pool pkv_pool; /* opaque */
+
+/* A sequence handle. A freed handle's generation no longer matches, so a
+ * stale handle is rejected with PKV_E_INVALID. */
+typedef struct {
+  int32_t index;
+  uint32_t generation;
+} pkv_seq;
+
+/* One copy-on-write copy: slots [0, n_valid) of every layer and KV head of
+ * block src are copied into block dst. */
+typedef struct {
+  int32_t src;
+  int32_t dst;
+  int32_t n_valid;
+} pkv_cow_op;
+
+typedef struct {
+  int32_t num_blocks;   /* blocks in the pool, > 0 */
+  int32_t block_size;   /* token slots per block: 16, 32 or 64 for attention */
+  int32_t num_layers;   /* layers held by the arenas, > 0 */
+  int32_t num_kv_heads; /* KV heads, > 0 */
+  int32_t num_q_heads;  /* query heads, a multiple of num_kv_heads */
+  int32_t head_dim;     /* 64, 128 or 256 for attention */
+  int32_t kv_dtype;     /* pkv_dtype; q uses the same type */
+  /* Optional host array (copied at create): a permutation of
+   * [0, num_blocks). Allocation hands out the free block that comes first
+   * in this order. NULL = lowest free id first. */
+  const int32_t* alloc_order;
+  /* Device arenas, laid out as above. May be NULL for a pool used only for
+   * host-side table work; device calls then fail with PKV_E_INVALID. */
+  void* k_arena;
+  void* v_arena;
+} pkv_pool_desc;
+
+typedef struct {
+  int32_t num_blocks;
+  int32_t free_blocks;
+  int32_t live_seqs;
+  int32_t reserved;
+  int64_t total_refs; /* sum of all block reference counts */
+} pkv_stats;
+
+/* ---------------------------------------------------------------- pool */
+
+/* Create a pool of fixed-size blocks [D1]; all blocks start free. */
+int pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out);
+/* Free the host metadata, staging and metadata buffers; waits for the
+ * library's own pending copies. The arenas stay the caller's. */
+int pkv_pool_destroy(pkv_pool* pool);
+
+/* Raw block verbs. alloc: take one free block (count 1) per the allocation
+ * order. release: drop one reference; the block is free again at 0.
+ * Releasing a free block is PKV_E_INVALID. */
+int pkv_block_alloc(pkv_pool* pool, int32_t* id);
+int pkv_block_release(pkv_pool* pool, int32_t id);
+
+/* ------------------------------------------------------------ sequences */
+
+/* A new, empty sequence. */
+int pkv_seq_create(pkv_pool* pool, pkv_seq* out);
+/* Fork [D1]: the child's table is a copy of the parent's list of block ids
+ * and every listed block gains one reference. The parent is unchanged and
+ * no K/V is copied. Cost is linear in the number of blocks, independent of
+ * the bytes they hold. */
+int pkv_seq_fork(pkv_pool* pool, pkv_seq parent, pkv_seq* child);
+/* Drop one reference from each block of the sequence (blocks reaching 0
+ * become free) and invalidate the handle. */
+int pkv_seq_free(pkv_pool* pool, pkv_seq seq);
+
+/* Plan an append of n >= 0 tokens to seq [D1, D2], all or nothing:
+ *  1. if the last block is partly filled and shared (count > 1), take a
+ *     fresh block, record the copy {last, fresh, len % block_size}, drop one
+ *     reference from the old block and point the table at the fresh one;
+ *  2. for each new token, open a fresh block when the position is a
+ *     multiple of block_size; the token's slot is
+ *     table[pos / block_size] * block_size + pos % block_size.
+ * The table and length are updated; no device work is done. slots_out
+ * (host, n entries) receives the slots in token order; cow_out (host, room
+ * for 1) the copy if one was taken, with *n_cow set to 0 or 1. n == 0
+ * changes nothing. On PKV_E_OOM nothing changes. Never writes a block whose
+ * count is above one. */
+int pkv_seq_append_plan(pkv_pool* pool, pkv_seq seq, int32_t n, int64_t* slots_out,
+                        pkv_cow_op* cow_out, int32_t* n_cow);
+
+/* Device: perform copy-on-write copies (host array of n ops) for every
+ * layer and KV head, K and V, on the stream. */
+int pkv_cow_copy(pkv_pool* pool, const pkv_cow_op* ops, int32_t n, void* stream);
+
+/* Device: scatter n tokens of new K/V into their slots. slots: host array of
+ * n slot ids (block * block_size + offset, each in range). k_new, v_new:
+ * device, [num_layers][n][num_kv_heads][head_dim] in kv_dtype. */
+int pkv_write_kv(pkv_pool* pool, const int64_t* slots, int32_t n, const void* k_new,
+                 const void* v_new, void* stream);
+
+/* Plan + copy-on-write + write for several sequences in one go: sequence
+ * seqs[i] appends counts[i] tokens (each sequence at most once per call).
+ * Equivalent to calling pkv_seq_append_plan for seqs[0], seqs[1], ... in
+ * order and then copying and writing; all or nothing on PKV_E_OOM. k_new,
+ * v_new: device [num_layers][sum(counts)][num_kv_heads][head_dim], the
+ * sequences' tokens concatenated in seqs order. */
+int pkv_append_kv_batch(pkv_pool* pool, const pkv_seq* seqs, const int32_t* counts,
+                        int32_t n_seqs, const void* k_new, const void* v_new, void* stream);
+/* One sequence: pkv_append_kv_batch with n_seqs = 1. */
+int pkv_seq_append_kv(pkv_pool* pool, pkv_seq seq, int32_t n, const void* k_new,
+                      const void* v_new, void* stream);
+
+/* ----------------------------------------------------------- inspection */
+
+int pkv_seq_info(const pkv_pool* pool, pkv_seq seq, int32_t* len, int32_t* n_blocks);
+/* Copy up to cap block ids of the sequence's table into out (host). */
+int pkv_seq_blocks(const pkv_pool* pool, pkv_seq seq, int32_t* out, int32_t cap);
+int pkv_block_refcount(const pkv_pool* pool, int32_t id, int32_t* count);
+int pkv_pool_stats(const pkv_pool* pool, pkv_stats* stats);
+/* Bytes of device memory one arena (K or V) must have for this desc. */
+int pkv_arena_bytes(const pkv_pool_desc* desc, size_t* bytes);
+
+/* ------------------------------------------------------------ attention */
+
+/* Shape of an attention plan, for inspection and accounting. */
+typedef struct {
+  int32_t n_segments;     /* runs of blocks with one holder set */
+  int32_t n_chunks;       /* segments cut for the grid */
+  int32_t n_items;        /* work items per (layer, KV head) */
+  int32_t partial_rows;   /* partial states per (layer, KV head) */
+  int64_t unique_tokens;  /* distinct token slots read per (layer, KV head) */
+  int64_t workspace_bytes;
+} pkv_plan_info;
+
+/* Plans decode attention for these sequences (as pkv_decode_workspace_size
+ * does) and describes the plan. Host only. */
+int pkv_decode_plan_info(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t n_layers,
+                         pkv_plan_info* info);
+
+/* Workspace bytes pkv_decode_attn needs for these sequences and n_layers.
+ * The schedule built here is cached and reused by a following attention
+ * call on the same sequences if no table has changed in between. */
+int pkv_decode_workspace_size(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs,
+                              int32_t n_layers, size_t* bytes);
+
+/* Decode attention [D1]: for layer l in [layer0, layer0 + n_layers), each
+ * sequence b and query head h,
+ *   out[l - layer0][b][h][:] = softmax(scale * K_b q^T) V_b
+ * over all tokens sequence b holds, with K_b, V_b the tokens of KV head
+ * h / (num_q_heads / num_kv_heads) of layer l. Blocks that several of the
+ * sequences share are read from HBM once per call and used for all of
+ * them. q: device [n_layers][n_seqs][num_q_heads][head_dim] in kv_dtype;
+ * out: device float32, same shape. ws: device workspace of ws_bytes >=
+ * pkv_decode_workspace_size(...) bytes (256-byte aligned). Every sequence
+ * must be non-empty (else PKV_E_INVALID). */
+int pkv_decode_attn(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t layer0,
+                    int32_t n_layers, const void* q, float* out, float scale, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* Workspace bytes pkv_tree_verify_attn needs. */
+int pkv_verify_workspace_size(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
+                              int32_t n_nodes, size_t* bytes);
+
+/* Draft-tree verify attention [F4], one layer: request r's last n_nodes
+ * tokens are the nodes of a draft tree, node j at position
+ * len_r - n_nodes + j. Node i of request r attends, for every query head,
+ * to all positions below len_r - n_nodes (the context) and to the nodes on
+ * its own path to the root, itself included. parents: host int32
+ * [n_req][n_nodes], parents[r][j] in {-1, 0 .. j-1}. q: device
+ * [n_req][n_nodes][num_q_heads][head_dim] in kv_dtype; out: device float32,
+ * same shape. 1 <= n_nodes <= 64. Requires kv_dtype == PKV_BF16 (the
+ * contraction runs on the matrix cores). */
+int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
+                         const int32_t* parents, int32_t n_nodes, int32_t layer, const void* q,
+                         float* out, float scale, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- misc */
+
+/* Tuning knobs of the attention planner (defaults in parentheses):
+ *   "path"              0 automatic (1 = vector ALUs, 2 = matrix cores)
+ *   "chunk_tokens"      0 automatic: tokens per chunk of a shared segment
+ *   "rows_per_item"     64: query rows one workgroup serves
+ *   "target_workgroups" 2048: chunks are shortened until the grid has this many
+ *   "timing"            0: 1 records a pair of HIP events around every kernel
+ *                       launch on its stream (read with pkv_timing_read)
+ * Unknown keys or out-of-range values are PKV_E_INVALID. */
+int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value);
+
+/* Device time of the kernels launched since the last read (with the
+ * "timing" option on): kernel is "attention", "combine", "cow_copy" or
+ * "kv_write". Waits for the last recorded launch, returns the summed
+ * milliseconds and the launch count, and resets both. */
+int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_t* launches);
+
+/* Last error message of this thread ("" if none). */
+const char* pkv_last_error(void);
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,96 @@
+"""Builds libpkv.so (HIP for gfx950) in the package directory.
+
+    python paged_kv_cache_amd/build.py [-i] [-v]
+
+(run as a script: importing the package loads the library this builds)
+
+compiles csrc/*.hip and csrc/*.cpp with hipcc into objects under
+``_build/`` and links them into ``paged_kv_cache_amd/libpkv.so``. All device
+code is built with ``-target-feature -packed-fp32-ops`` (no packed fp32
+arithmetic is generated).
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpkv.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libpkv)")
+
+
+def sources():
+    return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def compile_cmd(src: str, obj: str):
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-function", "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd[1:1] = ["-x", "hip"]
+    return cmd
+
+
+def _stale(src: str, obj: str) -> bool:
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".h", ".hpp"))]
+    deps.append(os.path.join(ROOT, "include", "pkv.h"))
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compiles every source (with ``incremental``, only those whose object
+    is older than the source or any header) and links libpkv.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = []
+    for s in srcs:
+        obj = os.path.join(BUILD, s + ".o")
+        jobs.append((os.path.join(CSRC, s), obj))
+    todo = [j for j in jobs if not incremental or _stale(*j)]
+
+    def run(job):
+        src, obj = job
+        cmd = compile_cmd(src, obj)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+                        if "packed-fp32-ops" not in l)
+        return src, r.returncode, out
+
+    with ThreadPoolExecutor(max_workers=max(1, min(8, len(todo)))) as ex:
+        results = list(ex.map(run, todo))
+    bad = [(s, out) for s, rc, out in results if rc != 0]
+    for s, rc, out in results:
+        if out.strip() and (verbose or rc != 0):
+            print(f"--- {os.path.basename(s)}\n{out}", file=sys.stderr)
+    if bad:
+        raise RuntimeError("libpkv build failed: " + ", ".join(os.path.basename(s) for s, _ in bad))
+    tmp = LIB + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("libpkv link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv, incremental="-i" in sys.argv))

@@ -1,0 +1,668 @@
+// C ABI of libpkv (declared in include/pkv.h): argument checks, the host
+// pool, host-to-device staging and kernel launches. No exception leaves
+// this file.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "pkv.h"
+#include "pool.hpp"
+#include "schedule.hpp"
+
+using namespace pkv;
+
+namespace {
+
+constexpr int kRing = 8;
+
+// A slot of the pinned staging ring: the host writes the next upload only
+// after the copy that last read this slot has finished.
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PKV_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+// Event pairs bracketing kernel launches, per kernel kind.
+struct KernelTimer {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> used, spare;
+  ~KernelTimer() {
+    for (auto& v : {&used, &spare})
+      for (auto& pr : *v) {
+        (void)hipEventDestroy(pr.first);
+        (void)hipEventDestroy(pr.second);
+      }
+  }
+  int start(hipStream_t s, hipEvent_t* stop) {
+    std::pair<hipEvent_t, hipEvent_t> pr;
+    if (!spare.empty()) {
+      pr = spare.back();
+      spare.pop_back();
+    } else {
+      hipError_t e;
+      if ((e = hipEventCreate(&pr.first)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+      if ((e = hipEventCreate(&pr.second)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    used.push_back(pr);
+    hipError_t e = hipEventRecord(pr.first, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    *stop = pr.second;
+    return PKV_OK;
+  }
+  int read(double* ms, int64_t* n) {
+    double tot = 0;
+    for (auto& pr : used) {
+      hipError_t e = hipEventSynchronize(pr.second);
+      if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      float t = 0;
+      if ((e = hipEventElapsedTime(&t, pr.first, pr.second)) != hipSuccess)
+        return hip_fail(e, "hipEventElapsedTime");
+      tot += t;
+    }
+    *ms = tot;
+    *n = (int64_t)used.size();
+    spare.insert(spare.end(), used.begin(), used.end());
+    used.clear();
+    return PKV_OK;
+  }
+};
+
+enum { T_ATTN = 0, T_COMBINE = 1, T_COW = 2, T_WRITE = 3, T_KINDS = 4 };
+
+struct pkv_pool {
+  explicit pkv_pool(const pkv_pool_desc& d) : pool(d) {}
+  bool timing = false;
+  KernelTimer timers[T_KINDS];
+
+  // Launches `launch` (returning hipError_t), bracketed by timing events
+  // when timing is on.
+  template <typename F>
+  int timed(int kind, hipStream_t s, F&& launch, const char* what) {
+    hipEvent_t stop = nullptr;
+    if (timing) {
+      int rc = timers[kind].start(s, &stop);
+      if (rc) return rc;
+    }
+    hipError_t e = launch();
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (stop) {
+      if ((e = hipEventRecord(stop, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    return PKV_OK;
+  }
+
+  Pool pool;
+  Staging ring[kRing];
+  int ring_next = 0;
+  void* dmeta = nullptr;  // device copy of per-call metadata (slots, copy ops)
+  size_t dmeta_cap = 0;
+  PlannerScratch scratch;
+  SchedOptions opt;
+  int path = 0;  // 0 auto, 1 VALU, 2 matrix cores
+
+  // schedule cache
+  bool cache_valid = false;
+  int cache_kind = -1;  // 0 decode, 1 verify
+  uint64_t cache_mut = 0;
+  int32_t cache_layers = 0, cache_layer0 = 0, cache_nodes = 0;
+  bool cache_mfma = false;
+  std::vector<pkv_seq> cache_seqs;
+  std::vector<int32_t> cache_parents;
+  Schedule sched;
+
+  ~pkv_pool() {
+    for (Staging& s : ring) {
+      if (s.ev) {
+        if (s.pending) (void)hipEventSynchronize(s.ev);
+        (void)hipEventDestroy(s.ev);
+      }
+      if (s.host) (void)hipHostFree(s.host);
+    }
+    if (dmeta) (void)hipFree(dmeta);
+  }
+
+  // Copies `bytes` from the pinned slot filled by `fill` to device `dst`.
+  template <typename F>
+  int upload(void* dst, size_t bytes, hipStream_t stream, F&& fill) {
+    if (bytes == 0) return PKV_OK;
+    Staging& s = ring[ring_next];
+    ring_next = (ring_next + 1) % kRing;
+    hipError_t e;
+    if (!s.ev) {
+      if ((e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "hipEventCreate");
+    }
+    if (s.pending) {
+      if ((e = hipEventSynchronize(s.ev)) != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+      s.pending = false;
+    }
+    if (s.cap < bytes) {
+      if (s.host) (void)hipHostFree(s.host);
+      s.host = nullptr;
+      s.cap = 0;
+      size_t want = bytes < 65536 ? 65536 : bytes + bytes / 2;
+      if ((e = hipHostMalloc(&s.host, want, hipHostMallocDefault)) != hipSuccess)
+        return hip_fail(e, "hipHostMalloc");
+      s.cap = want;
+    }
+    fill((uint8_t*)s.host);
+    if ((e = hipMemcpyAsync(dst, s.host, bytes, hipMemcpyHostToDevice, stream)) != hipSuccess)
+      return hip_fail(e, "hipMemcpyAsync");
+    if ((e = hipEventRecord(s.ev, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    s.pending = true;
+    return PKV_OK;
+  }
+
+  int ensure_dmeta(size_t bytes, hipStream_t stream) {
+    if (dmeta_cap >= bytes) return PKV_OK;
+    hipError_t e;
+    if (dmeta) {
+      // earlier kernels on the stream may still read the old buffer
+      if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      (void)hipFree(dmeta);
+      dmeta = nullptr;
+      dmeta_cap = 0;
+    }
+    size_t want = bytes < 65536 ? 65536 : bytes + bytes / 2;
+    if ((e = hipMalloc(&dmeta, want)) != hipSuccess) return hip_fail(e, "hipMalloc");
+    dmeta_cap = want;
+    return PKV_OK;
+  }
+};
+
+namespace {
+
+bool pool_ok(const pkv_pool* p) { return p != nullptr; }
+
+int check_desc(const pkv_pool_desc* d) {
+  if (!d) return fail(PKV_E_INVALID, "null desc");
+  if (d->num_blocks <= 0 || d->block_size <= 0 || d->num_layers <= 0 || d->num_kv_heads <= 0 ||
+      d->num_q_heads <= 0 || d->head_dim <= 0)
+    return fail(PKV_E_INVALID, "pool sizes must be positive");
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(PKV_E_INVALID, "num_q_heads must be a multiple of num_kv_heads");
+  if (d->kv_dtype != PKV_F32 && d->kv_dtype != PKV_BF16) return fail(PKV_E_INVALID, "bad kv_dtype");
+  if ((int64_t)d->num_blocks * d->block_size > (int64_t)INT32_MAX)
+    return fail(PKV_E_INVALID, "num_blocks * block_size overflows a slot id");
+  const size_t es = d->kv_dtype == PKV_F32 ? 4 : 2;
+  if ((d->head_dim * es) % 16)
+    return fail(PKV_E_INVALID, "head_dim * element size must be a multiple of 16 bytes");
+  if (d->alloc_order) {
+    std::vector<char> seen(d->num_blocks, 0);
+    for (int32_t i = 0; i < d->num_blocks; ++i) {
+      int32_t b = d->alloc_order[i];
+      if (b < 0 || b >= d->num_blocks || seen[b])
+        return fail(PKV_E_INVALID, "alloc_order is not a permutation of the block ids");
+      seen[b] = 1;
+    }
+  }
+  return PKV_OK;
+}
+
+size_t elem_size(const pkv_pool_desc& d) { return d.kv_dtype == PKV_F32 ? 4 : 2; }
+
+bool has_arenas(const pkv_pool_desc& d) { return d.k_arena && d.v_arena; }
+
+int enqueue_cow(pkv_pool* p, const std::vector<pkv_cow_op>& ops, hipStream_t stream) {
+  if (ops.empty()) return PKV_OK;
+  const pkv_pool_desc& d = p->pool.desc();
+  const size_t bytes = ops.size() * sizeof(pkv_cow_op);
+  int rc = p->ensure_dmeta(bytes, stream);
+  if (rc) return rc;
+  rc = p->upload(p->dmeta, bytes, stream,
+                 [&](uint8_t* h) { std::memcpy(h, ops.data(), bytes); });
+  if (rc) return rc;
+  return p->timed(
+      T_COW, stream,
+      [&] {
+        return launch_cow_copy(d.kv_dtype, d.k_arena, d.v_arena, (const int32_t*)p->dmeta,
+                               (int)ops.size(), d.num_layers, d.num_blocks, d.num_kv_heads,
+                               d.head_dim, d.block_size, stream);
+      },
+      "cow_copy launch");
+}
+
+int enqueue_write(pkv_pool* p, const int64_t* slots, int32_t n, const void* k_new,
+                  const void* v_new, hipStream_t stream) {
+  if (n == 0) return PKV_OK;
+  const pkv_pool_desc& d = p->pool.desc();
+  const size_t bytes = (size_t)n * sizeof(int64_t);
+  int rc = p->ensure_dmeta(bytes, stream);
+  if (rc) return rc;
+  rc = p->upload(p->dmeta, bytes, stream, [&](uint8_t* h) { std::memcpy(h, slots, bytes); });
+  if (rc) return rc;
+  return p->timed(
+      T_WRITE, stream,
+      [&] {
+        return launch_kv_write(d.kv_dtype, k_new, v_new, d.k_arena, d.v_arena,
+                               (const int64_t*)p->dmeta, n, d.num_layers, d.num_blocks,
+                               d.num_kv_heads, d.head_dim, d.block_size, stream);
+      },
+      "kv_write launch");
+}
+
+bool use_mfma(const pkv_pool* p) {
+  const pkv_pool_desc& d = p->pool.desc();
+  if (p->path == 1) return false;
+  return attn_supported(true, d.kv_dtype, d.head_dim, d.block_size);
+}
+
+// Builds (or reuses) the decode schedule for these arguments.
+int decode_schedule(pkv_pool* p, const pkv_seq* seqs, int32_t n, int32_t layer0, int32_t n_layers) {
+  const bool mfma = use_mfma(p);
+  if (p->cache_valid && p->cache_kind == 0 && p->cache_mut == p->pool.mutation() &&
+      p->cache_layers == n_layers && p->cache_layer0 == layer0 && p->cache_mfma == mfma &&
+      (int32_t)p->cache_seqs.size() == n &&
+      std::memcmp(p->cache_seqs.data(), seqs, sizeof(pkv_seq) * n) == 0)
+    return PKV_OK;
+  p->cache_valid = false;
+  SchedOptions o = p->opt;
+  if (!mfma) o.rows_per_item = std::min<int32_t>(o.rows_per_item, 16);
+  int rc = build_decode_schedule(p->pool, seqs, n, n_layers, layer0, o, &p->scratch, &p->sched);
+  if (rc) return rc;
+  p->cache_valid = true;
+  p->cache_kind = 0;
+  p->cache_mut = p->pool.mutation();
+  p->cache_layers = n_layers;
+  p->cache_layer0 = layer0;
+  p->cache_mfma = mfma;
+  p->cache_seqs.assign(seqs, seqs + n);
+  return PKV_OK;
+}
+
+int verify_schedule(pkv_pool* p, const pkv_seq* reqs, int32_t n_req, const int32_t* parents,
+                    int32_t n_nodes) {
+  const size_t np = (size_t)n_req * (size_t)(n_nodes > 0 ? n_nodes : 0);
+  if (p->cache_valid && p->cache_kind == 1 && p->cache_mut == p->pool.mutation() &&
+      p->cache_nodes == n_nodes && (int32_t)p->cache_seqs.size() == n_req &&
+      std::memcmp(p->cache_seqs.data(), reqs, sizeof(pkv_seq) * n_req) == 0 &&
+      p->cache_parents.size() == np &&
+      std::memcmp(p->cache_parents.data(), parents, np * sizeof(int32_t)) == 0)
+    return PKV_OK;
+  p->cache_valid = false;
+  int rc = build_verify_schedule(p->pool, reqs, n_req, parents, n_nodes, p->opt, &p->sched);
+  if (rc) return rc;
+  p->cache_valid = true;
+  p->cache_kind = 1;
+  p->cache_mut = p->pool.mutation();
+  p->cache_nodes = n_nodes;
+  p->cache_seqs.assign(reqs, reqs + n_req);
+  p->cache_parents.assign(parents, parents + np);
+  return PKV_OK;
+}
+
+// Uploads the schedule into the workspace and launches attention + combine.
+int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* out, float scale,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  const pkv_pool_desc& d = p->pool.desc();
+  const Schedule& S = p->sched;
+  if (!ws || ws_bytes < S.total_bytes)
+    return fail(PKV_E_WORKSPACE, "workspace too small: need " + std::to_string(S.total_bytes) +
+                                     " bytes, got " + std::to_string(ws_bytes));
+  if ((uintptr_t)ws % 256) return fail(PKV_E_INVALID, "workspace must be 256-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_E_INVALID, "scale must be finite");
+  uint8_t* w = (uint8_t*)ws;
+  int rc = p->upload(w, S.meta_bytes, stream, [&](uint8_t* h) { S.pack_meta(h); });
+  if (rc) return rc;
+  AttnParams a;
+  a.k_arena = d.k_arena;
+  a.v_arena = d.v_arena;
+  a.q = q;
+  a.part_ml = (float*)(w + S.off_ml);
+  a.part_acc = (float*)(w + S.off_acc);
+  a.items = (const WorkItem*)(w + S.off_items);
+  a.blk = (const int32_t*)(w + S.off_blk);
+  a.holders = (const int32_t*)(w + S.off_holders);
+  a.anc = (const uint64_t*)(w + S.off_anc);
+  a.n_items = (int32_t)S.items.size();
+  a.n_layers = S.n_layers;
+  a.layer0 = layer0;
+  a.num_blocks = d.num_blocks;
+  a.Hkv = d.num_kv_heads;
+  a.G = d.num_q_heads / d.num_kv_heads;
+  a.Hq = d.num_q_heads;
+  a.n_branch = S.n_branch;
+  a.P = S.P;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  rc = p->timed(
+      T_ATTN, stream, [&] { return launch_attn(mfma, d.kv_dtype, d.head_dim, d.block_size, a, stream); },
+      "attention launch");
+  if (rc) return rc;
+  CombineParams c;
+  c.part_ml = a.part_ml;
+  c.part_acc = a.part_acc;
+  c.comb_ptr = (const int32_t*)(w + S.off_comb_ptr);
+  c.comb_rows = (const int32_t*)(w + S.off_comb_rows);
+  c.out = out;
+  c.n_layers = S.n_layers;
+  c.n_branch = S.n_branch;
+  c.Hkv = a.Hkv;
+  c.G = a.G;
+  c.Hq = a.Hq;
+  c.P = S.P;
+  return p->timed(T_COMBINE, stream, [&] { return launch_combine(d.head_dim, c, stream); },
+                  "combine launch");
+}
+
+}  // namespace
+
+#define PKV_GUARD_BEGIN \
+  clear_error();        \
+  try {
+#define PKV_GUARD_END                                         \
+  }                                                           \
+  catch (const std::bad_alloc&) {                             \
+    return fail(PKV_E_OOM, "host allocation failed");         \
+  }                                                           \
+  catch (...) {                                               \
+    return fail(PKV_E_INVALID, "unexpected internal error");  \
+  }
+
+extern "C" {
+
+int pkv_pool_create(const pkv_pool_desc* desc, pkv_pool** out) {
+  PKV_GUARD_BEGIN
+  if (!out) return fail(PKV_E_INVALID, "null output");
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  *out = new pkv_pool(*desc);
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_pool_destroy(pkv_pool* pool) {
+  PKV_GUARD_BEGIN
+  if (!pool) return fail(PKV_E_INVALID, "null pool");
+  delete pool;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_block_alloc(pkv_pool* pool, int32_t* id) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.block_alloc(id);
+  PKV_GUARD_END
+}
+
+int pkv_block_release(pkv_pool* pool, int32_t id) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.block_release(id);
+  PKV_GUARD_END
+}
+
+int pkv_seq_create(pkv_pool* pool, pkv_seq* out) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.seq_create(out);
+  PKV_GUARD_END
+}
+
+int pkv_seq_fork(pkv_pool* pool, pkv_seq parent, pkv_seq* child) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.seq_fork(parent, child);
+  PKV_GUARD_END
+}
+
+int pkv_seq_free(pkv_pool* pool, pkv_seq seq) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.seq_free(seq);
+  PKV_GUARD_END
+}
+
+int pkv_seq_append_plan(pkv_pool* pool, pkv_seq seq, int32_t n, int64_t* slots_out,
+                        pkv_cow_op* cow_out, int32_t* n_cow) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  if (n < 0) return fail(PKV_E_INVALID, "append: negative token count");
+  if ((n > 0 && !slots_out) || !cow_out || !n_cow) return fail(PKV_E_INVALID, "append: null buffer");
+  std::vector<int64_t> slots;
+  std::vector<pkv_cow_op> cows;
+  int rc = pool->pool.append_plan_batch(&seq, &n, 1, &slots, &cows);
+  if (rc) return rc;
+  if (n) std::memcpy(slots_out, slots.data(), sizeof(int64_t) * slots.size());
+  *n_cow = (int32_t)cows.size();
+  if (!cows.empty()) *cow_out = cows[0];
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_cow_copy(pkv_pool* pool, const pkv_cow_op* ops, int32_t n, void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  const pkv_pool_desc& d = pool->pool.desc();
+  if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  if (n < 0 || (n > 0 && !ops)) return fail(PKV_E_INVALID, "cow_copy: bad op list");
+  std::vector<pkv_cow_op> v(ops, ops + n);
+  for (const pkv_cow_op& o : v)
+    if (o.src < 0 || o.src >= d.num_blocks || o.dst < 0 || o.dst >= d.num_blocks || o.n_valid < 0 ||
+        o.n_valid > d.block_size)
+      return fail(PKV_E_INVALID, "cow_copy: op out of range");
+  return enqueue_cow(pool, v, (hipStream_t)stream);
+  PKV_GUARD_END
+}
+
+int pkv_write_kv(pkv_pool* pool, const int64_t* slots, int32_t n, const void* k_new,
+                 const void* v_new, void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  const pkv_pool_desc& d = pool->pool.desc();
+  if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  if (n < 0 || (n > 0 && (!slots || !k_new || !v_new))) return fail(PKV_E_INVALID, "write_kv: bad arguments");
+  const int64_t max_slot = (int64_t)d.num_blocks * d.block_size;
+  for (int32_t i = 0; i < n; ++i)
+    if (slots[i] < 0 || slots[i] >= max_slot) return fail(PKV_E_INVALID, "write_kv: slot out of range");
+  return enqueue_write(pool, slots, n, k_new, v_new, (hipStream_t)stream);
+  PKV_GUARD_END
+}
+
+int pkv_append_kv_batch(pkv_pool* pool, const pkv_seq* seqs, const int32_t* counts, int32_t n_seqs,
+                        const void* k_new, const void* v_new, void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  const pkv_pool_desc& d = pool->pool.desc();
+  if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  int64_t total = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) total += counts ? counts[i] : 0;
+  if (total > 0 && (!k_new || !v_new)) return fail(PKV_E_INVALID, "append: null K/V");
+  if (total > INT32_MAX) return fail(PKV_E_INVALID, "append: too many tokens");
+  std::vector<int64_t> slots;
+  std::vector<pkv_cow_op> cows;
+  slots.reserve((size_t)total);
+  int rc = pool->pool.append_plan_batch(seqs, counts, n_seqs, &slots, &cows);
+  if (rc) return rc;
+  // The tables are updated; a device failure below leaves them updated
+  // (the error is PKV_E_HIP, after which the device state is unknown).
+  hipStream_t s = (hipStream_t)stream;
+  rc = enqueue_cow(pool, cows, s);
+  if (rc) return rc;
+  return enqueue_write(pool, slots.data(), (int32_t)slots.size(), k_new, v_new, s);
+  PKV_GUARD_END
+}
+
+int pkv_seq_append_kv(pkv_pool* pool, pkv_seq seq, int32_t n, const void* k_new, const void* v_new,
+                      void* stream) {
+  return pkv_append_kv_batch(pool, &seq, &n, 1, k_new, v_new, stream);
+}
+
+int pkv_seq_info(const pkv_pool* pool, pkv_seq seq, int32_t* len, int32_t* n_blocks) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.seq_info(seq, len, n_blocks);
+  PKV_GUARD_END
+}
+
+int pkv_seq_blocks(const pkv_pool* pool, pkv_seq seq, int32_t* out, int32_t cap) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.seq_blocks(seq, out, cap);
+  PKV_GUARD_END
+}
+
+int pkv_block_refcount(const pkv_pool* pool, int32_t id, int32_t* count) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.refcount(id, count);
+  PKV_GUARD_END
+}
+
+int pkv_pool_stats(const pkv_pool* pool, pkv_stats* stats) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.stats(stats);
+  PKV_GUARD_END
+}
+
+int pkv_arena_bytes(const pkv_pool_desc* desc, size_t* bytes) {
+  PKV_GUARD_BEGIN
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!bytes) return fail(PKV_E_INVALID, "null output");
+  *bytes = (size_t)desc->num_layers * desc->num_blocks * desc->num_kv_heads * desc->block_size *
+           desc->head_dim * elem_size(*desc);
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_decode_workspace_size(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t n_layers,
+                              size_t* bytes) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool) || !bytes) return fail(PKV_E_INVALID, "null argument");
+  int rc = decode_schedule(pool, seqs, n_seqs, 0, n_layers);
+  if (rc) return rc;
+  *bytes = pool->sched.total_bytes;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_decode_plan_info(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t n_layers,
+                         pkv_plan_info* info) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool) || !info) return fail(PKV_E_INVALID, "null argument");
+  int rc = decode_schedule(pool, seqs, n_seqs, 0, n_layers);
+  if (rc) return rc;
+  const Schedule& S = pool->sched;
+  info->n_segments = S.n_segments;
+  info->n_chunks = S.n_chunks;
+  info->n_items = (int32_t)S.items.size();
+  info->partial_rows = S.P;
+  info->unique_tokens = S.unique_tokens;
+  info->workspace_bytes = (int64_t)S.total_bytes;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_decode_attn(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t layer0,
+                    int32_t n_layers, const void* q, float* out, float scale, void* ws,
+                    size_t ws_bytes, void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  const pkv_pool_desc& d = pool->pool.desc();
+  if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  if (!q || !out) return fail(PKV_E_INVALID, "decode: null q or out");
+  const bool mfma = use_mfma(pool);
+  if (!attn_supported(mfma, d.kv_dtype, d.head_dim, d.block_size))
+    return fail(PKV_E_UNSUPPORTED, "decode: head_dim must be 64/128/256 and block_size 16/32/64");
+  // the workspace-size query plans layer0 = 0; the plan does not depend on it
+  int rc = decode_schedule(pool, seqs, n_seqs, 0, n_layers);
+  if (rc) return rc;
+  if (layer0 < 0 || layer0 + n_layers > d.num_layers)
+    return fail(PKV_E_INVALID, "decode: layer range outside the pool");
+  return run_attention(pool, mfma, layer0, q, out, scale, ws, ws_bytes, (hipStream_t)stream);
+  PKV_GUARD_END
+}
+
+int pkv_verify_workspace_size(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req, int32_t n_nodes,
+                              size_t* bytes) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool) || !bytes) return fail(PKV_E_INVALID, "null argument");
+  // the plan depends on the tree only through the masks, not on its sizes
+  const size_t np = (size_t)(n_req > 0 ? n_req : 0) * (n_nodes > 0 ? n_nodes : 0);
+  std::vector<int32_t> chain(np);
+  for (size_t i = 0; i < np; ++i) chain[i] = (int32_t)(i % n_nodes) - 1;
+  Schedule s;
+  int rc = build_verify_schedule(pool->pool, reqs, n_req, chain.data(), n_nodes, pool->opt, &s);
+  if (rc) return rc;
+  *bytes = s.total_bytes;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req, const int32_t* parents,
+                         int32_t n_nodes, int32_t layer, const void* q, float* out, float scale,
+                         void* ws, size_t ws_bytes, void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  const pkv_pool_desc& d = pool->pool.desc();
+  if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  if (!q || !out) return fail(PKV_E_INVALID, "verify: null q or out");
+  if (layer < 0 || layer >= d.num_layers) return fail(PKV_E_INVALID, "verify: layer outside the pool");
+  if (!attn_supported(true, d.kv_dtype, d.head_dim, d.block_size))
+    return fail(PKV_E_UNSUPPORTED, "verify: needs bf16 K/V, head_dim 64/128/256, block_size 16/32/64");
+  int rc = verify_schedule(pool, reqs, n_req, parents, n_nodes);
+  if (rc) return rc;
+  return run_attention(pool, true, layer, q, out, scale, ws, ws_bytes, (hipStream_t)stream);
+  PKV_GUARD_END
+}
+
+int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool) || !key) return fail(PKV_E_INVALID, "null argument");
+  const std::string k(key);
+  if (k == "path") {
+    if (value < 0 || value > 2) return fail(PKV_E_INVALID, "path must be 0, 1 or 2");
+    pool->path = (int)value;
+  } else if (k == "chunk_tokens") {
+    if (value < 0 || value > (1 << 24)) return fail(PKV_E_INVALID, "chunk_tokens out of range");
+    pool->opt.chunk_tokens = (int32_t)value;
+  } else if (k == "rows_per_item") {
+    if (value < 1 || value > 64) return fail(PKV_E_INVALID, "rows_per_item must be 1..64");
+    pool->opt.rows_per_item = (int32_t)value;
+  } else if (k == "timing") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "timing must be 0 or 1");
+    pool->timing = value != 0;
+  } else if (k == "target_workgroups") {
+    if (value < 1 || value > (1 << 24)) return fail(PKV_E_INVALID, "target_workgroups out of range");
+    pool->opt.target_workgroups = (int32_t)value;
+  } else {
+    return fail(PKV_E_INVALID, "unknown option " + k);
+  }
+  pool->cache_valid = false;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_t* launches) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool) || !kernel || !total_ms || !launches) return fail(PKV_E_INVALID, "null argument");
+  const std::string k(kernel);
+  int kind = k == "attention" ? T_ATTN
+             : k == "combine" ? T_COMBINE
+             : k == "cow_copy" ? T_COW
+             : k == "kv_write" ? T_WRITE
+                               : -1;
+  if (kind < 0) return fail(PKV_E_INVALID, "unknown kernel " + k);
+  return pool->timers[kind].read(total_ms, launches);
+  PKV_GUARD_END
+}
+
+const char* pkv_last_error(void) { return last_error(); }
+
+const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+}  // extern "C"

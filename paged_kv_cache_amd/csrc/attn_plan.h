@@ -1,0 +1,67 @@
+// Attention schedule shared by the host planner (schedule.cpp) and the
+// device kernels (kernels.hip). Plain data, int32 indices.
+//
+// A *segment* is a maximal run of blocks that the same set of sequences
+// (its holders) reference at the same logical positions; forks share
+// prefixes, so the segments of a batch form a tree. A segment is cut into
+// *chunks* of whole blocks, and a chunk's rows (holder x query head of one
+// KV-head group) are cut into *work items* of at most 64 rows. The grid
+// replicates every work item over (layer, KV head): one workgroup reads the
+// chunk's K/V tiles once and applies them to all of its rows.
+#pragma once
+
+#include <cstdint>
+
+namespace pkv {
+
+struct WorkItem {
+  int32_t blk_off;    // index in blk[] of the chunk's first block
+  int32_t n_tok;      // valid tokens in the chunk (> 0)
+  int32_t t0;         // logical position of the chunk's first token
+  int32_t hold_off;   // index in holders[] of the chunk's first holder
+  int32_t r0;         // first chunk row handled (chunk row = holder * G + g)
+  int32_t n_rows;     // rows handled by this item (1 .. 64)
+  int32_t part_row;   // partial-state row of this item's first row, per plane
+  int32_t mask_from;  // first logical position under the draft-tree mask (INT32_MAX: none)
+};
+static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
+
+// Device-side pointers to a decode / verify schedule and its partials.
+// Partial states are stored per plane (layer, KV head): P rows each.
+struct AttnParams {
+  const void* k_arena;      // [L][NB][Hkv][BS][D]
+  const void* v_arena;      // [L][NB][Hkv][D][BS]
+  const void* q;            // [n_layers][n_branch][Hq][D]
+  float* part_ml;           // [n_layers * Hkv][P][2]: running max (log2 units), sum
+  float* part_acc;          // [n_layers * Hkv][P][D]
+  const WorkItem* items;    // [n_items]
+  const int32_t* blk;       // block ids, per chunk padded to a whole 32-token step
+  const int32_t* holders;   // branch index of each holder
+  const uint64_t* anc;      // [n_branch] ancestor-or-self bits (verify only)
+  int32_t n_items;
+  int32_t n_layers;
+  int32_t layer0;
+  int32_t num_blocks;
+  int32_t Hkv;
+  int32_t G;
+  int32_t Hq;
+  int32_t n_branch;
+  int32_t P;
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+struct CombineParams {
+  const float* part_ml;
+  const float* part_acc;
+  const int32_t* comb_ptr;   // [n_branch + 1]
+  const int32_t* comb_rows;  // partial row of q-head group offset 0, in logical order
+  float* out;                // [n_layers][n_branch][Hq][D]
+  int32_t n_layers;
+  int32_t n_branch;
+  int32_t Hkv;
+  int32_t G;
+  int32_t Hq;
+  int32_t P;
+};
+
+}  // namespace pkv

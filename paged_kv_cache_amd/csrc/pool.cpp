@@ -1,0 +1,265 @@
+// Host block pool, block tables, fork / free and the append planner.
+// See pool.hpp for the mechanism and its source.
+#include "pool.hpp"
+
+#include <algorithm>
+#include <unordered_map>
+
+namespace pkv {
+
+namespace {
+thread_local std::string g_err;
+}
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+void clear_error() { g_err.clear(); }
+const char* last_error() { return g_err.c_str(); }
+
+// ------------------------------------------------------------------ FreeSet
+
+void FreeSet::init(int n) {
+  n_ = n;
+  count_ = n;
+  lv_.clear();
+  int bits = n;
+  do {
+    int words = (bits + 63) / 64;
+    std::vector<uint64_t> w(words, ~0ull);
+    if (bits % 64) w.back() = (1ull << (bits % 64)) - 1;
+    lv_.push_back(std::move(w));
+    bits = words;
+  } while (bits > 1);
+}
+
+int FreeSet::pop_lowest() {
+  if (count_ == 0) return -1;
+  // descend from the top summary level
+  int idx = 0;
+  for (int k = (int)lv_.size() - 1; k >= 0; --k) {
+    uint64_t w = lv_[k][idx];
+    idx = idx * 64 + __builtin_ctzll(w);
+  }
+  int rank = idx;
+  // clear the leaf bit and propagate emptiness upward
+  int i = rank;
+  for (size_t k = 0; k < lv_.size(); ++k) {
+    uint64_t& w = lv_[k][i / 64];
+    w &= ~(1ull << (i % 64));
+    if (w != 0) break;
+    i /= 64;
+  }
+  --count_;
+  return rank;
+}
+
+void FreeSet::insert(int rank) {
+  int i = rank;
+  for (size_t k = 0; k < lv_.size(); ++k) {
+    uint64_t& w = lv_[k][i / 64];
+    bool was_empty = (w == 0);
+    w |= 1ull << (i % 64);
+    if (!was_empty) break;
+    i /= 64;
+  }
+  ++count_;
+}
+
+bool FreeSet::contains(int rank) const { return (lv_[0][rank / 64] >> (rank % 64)) & 1ull; }
+
+// --------------------------------------------------------------------- Pool
+
+Pool::Pool(const pkv_pool_desc& d) : d_(d) {
+  const int nb = d.num_blocks;
+  order_.resize(nb);
+  rank_of_.resize(nb);
+  for (int i = 0; i < nb; ++i) order_[i] = d.alloc_order ? d.alloc_order[i] : i;
+  for (int i = 0; i < nb; ++i) rank_of_[order_[i]] = i;
+  d_.alloc_order = nullptr;  // copied; do not keep the caller's pointer
+  ref_.assign(nb, 0);
+  free_.init(nb);
+}
+
+int32_t Pool::take_block() {
+  int rank = free_.pop_lowest();
+  int32_t b = order_[rank];
+  ref_[b] = 1;
+  ++total_refs_;
+  return b;
+}
+
+int Pool::block_alloc(int32_t* id) {
+  if (!id) return fail(PKV_E_INVALID, "block_alloc: null output");
+  if (free_.count() == 0) return fail(PKV_E_OOM, "block_alloc: pool exhausted");
+  *id = take_block();
+  ++mutation_;
+  return PKV_OK;
+}
+
+int Pool::block_release(int32_t id) {
+  if (id < 0 || id >= d_.num_blocks) return fail(PKV_E_INVALID, "block_release: id out of range");
+  if (ref_[id] <= 0) return fail(PKV_E_INVALID, "block_release: block is already free");
+  --total_refs_;
+  if (--ref_[id] == 0) free_.insert(rank_of_[id]);
+  ++mutation_;
+  return PKV_OK;
+}
+
+const Seq* Pool::get(pkv_seq s) const {
+  if (s.index < 0 || s.index >= (int32_t)seqs_.size() || !seqs_[s.index].live ||
+      seqs_[s.index].gen != s.generation) {
+    fail(PKV_E_INVALID, "invalid or stale sequence handle");
+    return nullptr;
+  }
+  return &seqs_[s.index];
+}
+
+Seq* Pool::get_mut(pkv_seq s) { return const_cast<Seq*>(get(s)); }
+
+int Pool::seq_create(pkv_seq* out) {
+  if (!out) return fail(PKV_E_INVALID, "seq_create: null output");
+  int32_t idx;
+  if (!free_seq_slots_.empty()) {
+    idx = free_seq_slots_.back();
+    free_seq_slots_.pop_back();
+  } else {
+    idx = (int32_t)seqs_.size();
+    seqs_.emplace_back();
+  }
+  Seq& s = seqs_[idx];
+  s.live = true;
+  s.len = 0;
+  s.blocks.clear();
+  ++live_;
+  ++mutation_;
+  *out = pkv_seq{idx, s.gen};
+  return PKV_OK;
+}
+
+int Pool::seq_fork(pkv_seq parent, pkv_seq* child) {
+  if (!child) return fail(PKV_E_INVALID, "seq_fork: null output");
+  if (!get(parent)) return PKV_E_INVALID;
+  pkv_seq c;
+  int rc = seq_create(&c);  // may grow seqs_: re-fetch the parent after
+  if (rc) return rc;
+  const Seq& p = seqs_[parent.index];
+  Seq& k = seqs_[c.index];
+  k.blocks = p.blocks;  // shallow: block ids only
+  k.len = p.len;
+  for (int32_t b : k.blocks) ++ref_[b];
+  total_refs_ += (int64_t)k.blocks.size();
+  *child = c;
+  return PKV_OK;
+}
+
+int Pool::seq_free(pkv_seq h) {
+  Seq* s = get_mut(h);
+  if (!s) return PKV_E_INVALID;
+  for (int32_t b : s->blocks) {
+    if (--ref_[b] == 0) free_.insert(rank_of_[b]);
+  }
+  total_refs_ -= (int64_t)s->blocks.size();
+  s->blocks.clear();
+  s->len = 0;
+  s->live = false;
+  ++s->gen;
+  free_seq_slots_.push_back(h.index);
+  --live_;
+  ++mutation_;
+  return PKV_OK;
+}
+
+int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t n,
+                            std::vector<int64_t>* slots, std::vector<pkv_cow_op>* cows) {
+  if (n < 0 || (n > 0 && (!seqs || !counts))) return fail(PKV_E_INVALID, "append: bad arguments");
+  const int64_t bs = d_.block_size;
+  // Pass 1: validate and count the blocks the whole batch needs, following
+  // the same order the execution pass takes (a copy made by an earlier
+  // sequence lowers the count of a tail that a later one may share).
+  std::unordered_map<int32_t, int32_t> dropped;  // block -> refs dropped by earlier copies
+  std::vector<int32_t> seen;
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = get(seqs[i]);
+    if (!s) return PKV_E_INVALID;
+    if (counts[i] < 0) return fail(PKV_E_INVALID, "append: negative token count");
+    if (std::find(seen.begin(), seen.end(), seqs[i].index) != seen.end())
+      return fail(PKV_E_INVALID, "append: a sequence appears twice in one batch");
+    seen.push_back(seqs[i].index);
+    if (counts[i] == 0) continue;
+    if ((int64_t)s->len + counts[i] > (int64_t)INT32_MAX)
+      return fail(PKV_E_INVALID, "append: sequence length overflow");
+    if (s->len % bs != 0) {
+      int32_t last = s->blocks.back();
+      int32_t live_refs = ref_[last] - dropped[last];
+      if (live_refs > 1) {
+        ++need;
+        ++dropped[last];
+      }
+    }
+    int64_t before = (s->len + bs - 1) / bs, after = (s->len + counts[i] + bs - 1) / bs;
+    need += after - before;
+  }
+  if (need > free_.count())
+    return fail(PKV_E_OOM, "append: pool has " + std::to_string(free_.count()) +
+                               " free blocks, the append needs " + std::to_string(need));
+  // Pass 2: execute (cannot fail).
+  for (int32_t i = 0; i < n; ++i) {
+    if (counts[i] == 0) continue;
+    Seq& s = seqs_[seqs[i].index];
+    int32_t r = (int32_t)(s.len % bs);
+    if (r != 0 && ref_[s.blocks.back()] > 1) {
+      int32_t old = s.blocks.back();
+      int32_t fresh = take_block();
+      --ref_[old];
+      --total_refs_;
+      s.blocks.back() = fresh;
+      if (cows) cows->push_back(pkv_cow_op{old, fresh, r});
+    }
+    for (int32_t t = 0; t < counts[i]; ++t) {
+      int64_t pos = s.len;
+      if (pos % bs == 0) s.blocks.push_back(take_block());
+      if (slots) slots->push_back((int64_t)s.blocks[pos / bs] * bs + pos % bs);
+      ++s.len;
+    }
+  }
+  if (need || n) ++mutation_;
+  return PKV_OK;
+}
+
+int Pool::seq_info(pkv_seq h, int32_t* len, int32_t* nblk) const {
+  const Seq* s = get(h);
+  if (!s) return PKV_E_INVALID;
+  if (len) *len = s->len;
+  if (nblk) *nblk = (int32_t)s->blocks.size();
+  return PKV_OK;
+}
+
+int Pool::seq_blocks(pkv_seq h, int32_t* out, int32_t cap) const {
+  const Seq* s = get(h);
+  if (!s) return PKV_E_INVALID;
+  if (cap < 0 || (cap > 0 && !out)) return fail(PKV_E_INVALID, "seq_blocks: bad buffer");
+  int32_t m = std::min<int32_t>(cap, (int32_t)s->blocks.size());
+  std::copy(s->blocks.begin(), s->blocks.begin() + m, out);
+  return PKV_OK;
+}
+
+int Pool::refcount(int32_t id, int32_t* rc) const {
+  if (id < 0 || id >= d_.num_blocks || !rc) return fail(PKV_E_INVALID, "refcount: bad block id");
+  *rc = ref_[id];
+  return PKV_OK;
+}
+
+int Pool::stats(pkv_stats* st) const {
+  if (!st) return fail(PKV_E_INVALID, "stats: null output");
+  st->num_blocks = d_.num_blocks;
+  st->free_blocks = free_.count();
+  st->live_seqs = live_;
+  st->reserved = 0;
+  st->total_refs = total_refs_;
+  return PKV_OK;
+}
+
+}  // namespace pkv

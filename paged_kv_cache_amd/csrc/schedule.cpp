@@ -1,0 +1,343 @@
+// Attention planner: segments, chunks, work items and combine lists.
+//
+// Sharing comes from forks, which copy a table prefix; so two sequences that
+// hold the same block hold it at the same logical position, and the blocks a
+// set of sequences shares form a common prefix of each of their tables.
+// Grouping consecutive blocks by their holder set therefore cuts the batch
+// into a tree of segments; each segment's K/V is read by one set of work
+// items and applied to every row (holder x query head) that needs it.
+#include "schedule.hpp"
+
+#include <algorithm>
+#include <cstring>
+
+namespace pkv {
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int32_t round_up(int32_t x, int32_t m) { return (x + m - 1) / m * m; }
+
+struct Segment {
+  std::vector<int32_t> blocks;  // logical order
+  int32_t t0 = 0;               // logical position of the first token
+  int32_t n_tok = 0;
+  int32_t hold_off = 0;         // into Schedule::holders
+  int32_t n_hold = 0;
+  int32_t chunk_begin = 0, chunk_end = 0;  // into the chunk list
+  int32_t mask_from = 0x7fffffff;          // draft-tree mask start (verify)
+};
+
+struct Chunk {
+  int32_t seg;
+  int32_t blk_off, n_tok, t0, part_base;
+};
+
+// Step granularity of the attention kernels, in tokens and in blocks.
+int32_t step_tokens(int32_t bs) { return bs > 32 ? bs : 32; }
+
+// Cuts every segment into chunks and every chunk's rows into work items.
+std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G, int32_t n_layers,
+                               int32_t Hkv, const SchedOptions& opt, Schedule* S) {
+  const int32_t step = step_tokens(bs);
+  const int32_t step_blocks = step / bs;
+  const int32_t rpi = std::max<int32_t>(1, opt.rows_per_item);
+  // chunk length per segment: long enough that the partial states a chunk
+  // writes stay small next to the K/V it reads (rows * (D + 2) floats vs
+  // tokens * 2 * D elements), short enough to fill the machine
+  auto base_len = [&](const Segment& s) {
+    if (opt.chunk_tokens > 0) return round_up(opt.chunk_tokens, step);
+    int32_t rows = s.n_hold * G;
+    int32_t t = round_up(std::max(opt.min_chunk_tokens, opt.tokens_per_row * rows), step);
+    return std::min(t, round_up(opt.max_chunk_tokens, step));
+  };
+  auto count_wgs = [&](int32_t div) {
+    int64_t w = 0;
+    for (const Segment& s : segs) {
+      int32_t len = std::max(round_up(opt.min_chunk_tokens, step), round_up(base_len(s) / div, step));
+      if (opt.chunk_tokens > 0) len = base_len(s);
+      int64_t chunks = (s.n_tok + len - 1) / len;
+      int64_t items = (s.n_hold * G + rpi - 1) / rpi;
+      w += chunks * items;
+    }
+    return w * n_layers * Hkv;
+  };
+  int32_t div = 1;
+  if (opt.chunk_tokens <= 0) {
+    while (div < 64 && count_wgs(div) < opt.target_workgroups &&
+           count_wgs(div * 2) > count_wgs(div))
+      div *= 2;
+  }
+  std::vector<Chunk> chunks;
+  for (size_t si = 0; si < segs.size(); ++si) {
+    Segment& s = segs[si];
+    int32_t len = opt.chunk_tokens > 0
+                      ? base_len(s)
+                      : std::max(round_up(opt.min_chunk_tokens, step), round_up(base_len(s) / div, step));
+    const int32_t nb = (int32_t)s.blocks.size();
+    int32_t k = (s.n_tok + len - 1) / len;
+    // equal chunks of whole steps
+    int32_t per = round_up((nb + k - 1) / k, step_blocks);
+    s.chunk_begin = (int32_t)chunks.size();
+    for (int32_t b0 = 0; b0 < nb; b0 += per) {
+      int32_t b1 = std::min(nb, b0 + per);
+      Chunk c;
+      c.seg = (int32_t)si;
+      c.blk_off = (int32_t)S->blk.size();
+      c.t0 = s.t0 + b0 * bs;
+      c.n_tok = std::min(s.n_tok, (b1 - b0) * bs + b0 * bs) - b0 * bs;
+      for (int32_t b = b0; b < b1; ++b) S->blk.push_back(s.blocks[b]);
+      while ((S->blk.size() - c.blk_off) % step_blocks) S->blk.push_back(s.blocks[b1 - 1]);
+      c.part_base = S->P;
+      S->P += s.n_hold * G;
+      chunks.push_back(c);
+    }
+    s.chunk_end = (int32_t)chunks.size();
+  }
+  S->n_chunks = (int32_t)chunks.size();
+  for (const Chunk& c : chunks) {
+    const Segment& s = segs[c.seg];
+    const int32_t rows = s.n_hold * G;
+    for (int32_t r0 = 0; r0 < rows; r0 += rpi) {
+      WorkItem w;
+      w.blk_off = c.blk_off;
+      w.n_tok = c.n_tok;
+      w.t0 = c.t0;
+      w.hold_off = s.hold_off;
+      w.r0 = r0;
+      w.n_rows = std::min(rpi, rows - r0);
+      w.part_row = c.part_base + r0;
+      w.mask_from = s.mask_from;
+      S->items.push_back(w);
+    }
+  }
+  // longest chunks first, so the tail of the grid holds the short ones
+  std::stable_sort(S->items.begin(), S->items.end(),
+                   [](const WorkItem& a, const WorkItem& b) { return a.n_tok > b.n_tok; });
+  return chunks;
+}
+
+}  // namespace
+
+void Schedule::layout(int Hkv, int D) {
+  size_t o = 0;
+  off_items = o;
+  o = align256(o + items.size() * sizeof(WorkItem));
+  off_blk = o;
+  o = align256(o + blk.size() * sizeof(int32_t));
+  off_holders = o;
+  o = align256(o + holders.size() * sizeof(int32_t));
+  off_comb_ptr = o;
+  o = align256(o + comb_ptr.size() * sizeof(int32_t));
+  off_comb_rows = o;
+  o = align256(o + comb_rows.size() * sizeof(int32_t));
+  off_anc = o;
+  o = align256(o + anc.size() * sizeof(uint64_t));
+  meta_bytes = o;
+  const size_t planes = (size_t)n_layers * Hkv;
+  off_ml = o;
+  o = align256(o + planes * P * 2 * sizeof(float));
+  off_acc = o;
+  o = align256(o + planes * P * (size_t)D * sizeof(float));
+  total_bytes = o;
+}
+
+void Schedule::pack_meta(uint8_t* dst) const {
+  std::memset(dst, 0, meta_bytes);
+  std::memcpy(dst + off_items, items.data(), items.size() * sizeof(WorkItem));
+  std::memcpy(dst + off_blk, blk.data(), blk.size() * sizeof(int32_t));
+  std::memcpy(dst + off_holders, holders.data(), holders.size() * sizeof(int32_t));
+  std::memcpy(dst + off_comb_ptr, comb_ptr.data(), comb_ptr.size() * sizeof(int32_t));
+  std::memcpy(dst + off_comb_rows, comb_rows.data(), comb_rows.size() * sizeof(int32_t));
+  if (!anc.empty()) std::memcpy(dst + off_anc, anc.data(), anc.size() * sizeof(uint64_t));
+}
+
+void PlannerScratch::ensure(int nb) {
+  if ((int)stamp.size() < nb) {
+    stamp.assign(nb, 0);
+    cnt.assign(nb, 0);
+    pos.assign(nb, 0);
+    valid.assign(nb, 0);
+    off.assign(nb, 0);
+    fill.assign(nb, 0);
+    seg.assign(nb, -1);
+    epoch = 0;
+  }
+  if (++epoch == 0) {  // wrapped: clear stamps
+    std::fill(stamp.begin(), stamp.end(), 0);
+    epoch = 1;
+  }
+}
+
+int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int32_t n_layers,
+                          int32_t layer0, const SchedOptions& opt, PlannerScratch* X,
+                          Schedule* S) {
+  const pkv_pool_desc& d = pool.desc();
+  const int32_t bs = d.block_size, G = d.num_q_heads / d.num_kv_heads;
+  if (n <= 0 || !seqs) return fail(PKV_E_INVALID, "decode: empty batch");
+  if (n_layers <= 0 || layer0 < 0 || layer0 + n_layers > d.num_layers)
+    return fail(PKV_E_INVALID, "decode: layer range outside the pool");
+  std::vector<const Seq*> sv(n);
+  for (int32_t i = 0; i < n; ++i) {
+    sv[i] = pool.get(seqs[i]);
+    if (!sv[i]) return PKV_E_INVALID;
+    if (sv[i]->len <= 0) return fail(PKV_E_INVALID, "decode: a sequence is empty");
+  }
+  *S = Schedule();
+  S->n_branch = n;
+  S->n_layers = n_layers;
+  X->ensure(d.num_blocks);
+  const uint32_t ep = X->epoch;
+  // pass 1: holder counts, logical position and valid slots of every block
+  std::vector<int32_t> distinct;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = *sv[i];
+    for (int32_t j = 0; j < (int32_t)s.blocks.size(); ++j) {
+      const int32_t b = s.blocks[j];
+      const int32_t v = std::min(bs, s.len - j * bs);
+      if (X->stamp[b] != ep) {
+        X->stamp[b] = ep;
+        X->cnt[b] = 0;
+        X->pos[b] = j;
+        X->valid[b] = v;
+        X->seg[b] = -1;
+        distinct.push_back(b);
+      } else if (X->pos[b] != j || X->valid[b] != v) {
+        return fail(PKV_E_INVALID, "decode: a shared block differs between its holders");
+      }
+      ++X->cnt[b];
+    }
+  }
+  // holder lists (ascending batch index) in one array
+  std::vector<int32_t> hold_all;
+  {
+    int32_t o = 0;
+    for (int32_t b : distinct) {
+      X->off[b] = o;
+      X->fill[b] = 0;
+      o += X->cnt[b];
+    }
+    hold_all.resize(o);
+    for (int32_t i = 0; i < n; ++i)
+      for (int32_t b : sv[i]->blocks) hold_all[X->off[b] + X->fill[b]++] = i;
+  }
+  auto same_holders = [&](int32_t a, int32_t b) {
+    return X->cnt[a] == X->cnt[b] &&
+           std::equal(hold_all.begin() + X->off[a], hold_all.begin() + X->off[a] + X->cnt[a],
+                      hold_all.begin() + X->off[b]);
+  };
+  // segments: maximal runs with one holder set, found by the first holder
+  std::vector<Segment> segs;
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = *sv[i];
+    int32_t cur = -1, prev = -1;
+    for (int32_t j = 0; j < (int32_t)s.blocks.size(); ++j) {
+      const int32_t b = s.blocks[j];
+      if (X->seg[b] >= 0) {
+        cur = -1;
+        prev = b;
+        continue;
+      }
+      if (cur >= 0 && same_holders(b, prev)) {
+        segs[cur].blocks.push_back(b);
+        segs[cur].n_tok += X->valid[b];
+      } else {
+        Segment sg;
+        sg.blocks.push_back(b);
+        sg.t0 = j * bs;
+        sg.n_tok = X->valid[b];
+        sg.hold_off = (int32_t)S->holders.size();
+        sg.n_hold = X->cnt[b];
+        S->holders.insert(S->holders.end(), hold_all.begin() + X->off[b],
+                          hold_all.begin() + X->off[b] + X->cnt[b]);
+        segs.push_back(std::move(sg));
+        cur = (int32_t)segs.size() - 1;
+      }
+      X->seg[b] = cur;
+      prev = b;
+    }
+  }
+  S->n_segments = (int32_t)segs.size();
+  for (const Segment& sg : segs) S->unique_tokens += sg.n_tok;
+  const std::vector<Chunk> chunks = emit_chunks(segs, bs, G, n_layers, d.num_kv_heads, opt, S);
+  // combine lists: for each branch, its segments in logical order, each
+  // segment's chunks in order; the entry is the partial row of q-head
+  // offset 0 of this branch in the chunk
+  S->comb_ptr.resize(n + 1);
+  for (int32_t i = 0; i < n; ++i) {
+    S->comb_ptr[i] = (int32_t)S->comb_rows.size();
+    int32_t last = -1;
+    for (int32_t b : sv[i]->blocks) {
+      const int32_t sgi = X->seg[b];
+      if (sgi == last) continue;
+      last = sgi;
+      const Segment& sg = segs[sgi];
+      const int32_t* h0 = S->holders.data() + sg.hold_off;
+      const int32_t hidx = (int32_t)(std::lower_bound(h0, h0 + sg.n_hold, i) - h0);
+      for (int32_t c = sg.chunk_begin; c < sg.chunk_end; ++c)
+        S->comb_rows.push_back(chunks[c].part_base + hidx * G);
+    }
+  }
+  S->comb_ptr[n] = (int32_t)S->comb_rows.size();
+  (void)layer0;
+  S->layout(d.num_kv_heads, d.head_dim);
+  return PKV_OK;
+}
+
+int build_verify_schedule(const Pool& pool, const pkv_seq* reqs, int32_t n_req,
+                          const int32_t* parents, int32_t n_nodes, const SchedOptions& opt,
+                          Schedule* S) {
+  const pkv_pool_desc& d = pool.desc();
+  const int32_t bs = d.block_size, G = d.num_q_heads / d.num_kv_heads;
+  if (n_req <= 0 || !reqs || !parents) return fail(PKV_E_INVALID, "verify: empty batch");
+  if (n_nodes < 1 || n_nodes > 64) return fail(PKV_E_UNSUPPORTED, "verify: n_nodes must be 1..64");
+  *S = Schedule();
+  S->n_branch = n_req * n_nodes;
+  S->n_layers = 1;
+  S->anc.resize((size_t)n_req * n_nodes);
+  std::vector<Segment> segs;
+  std::vector<int32_t> ctx(n_req);
+  for (int32_t r = 0; r < n_req; ++r) {
+    const Seq* s = pool.get(reqs[r]);
+    if (!s) return PKV_E_INVALID;
+    if (s->len < n_nodes) return fail(PKV_E_INVALID, "verify: request shorter than its tree");
+    for (int32_t q = 0; q < r; ++q)
+      if (reqs[q].index == reqs[r].index) return fail(PKV_E_INVALID, "verify: request repeated");
+    const int32_t* par = parents + (size_t)r * n_nodes;
+    for (int32_t j = 0; j < n_nodes; ++j) {
+      if (par[j] < -1 || par[j] >= j)
+        return fail(PKV_E_INVALID, "verify: parents[j] must be -1 or an earlier node");
+      uint64_t a = 1ull << j;
+      if (par[j] >= 0) a |= S->anc[(size_t)r * n_nodes + par[j]];
+      S->anc[(size_t)r * n_nodes + j] = a;
+    }
+    ctx[r] = s->len - n_nodes;
+    Segment sg;
+    sg.blocks = s->blocks;
+    sg.t0 = 0;
+    sg.n_tok = s->len;
+    sg.hold_off = (int32_t)S->holders.size();
+    sg.n_hold = n_nodes;
+    for (int32_t j = 0; j < n_nodes; ++j) S->holders.push_back(r * n_nodes + j);
+    segs.push_back(std::move(sg));
+  }
+  S->n_segments = n_req;
+  for (const Segment& sg : segs) S->unique_tokens += sg.n_tok;
+  for (int32_t r = 0; r < n_req; ++r) segs[r].mask_from = ctx[r];
+  const std::vector<Chunk> chunks = emit_chunks(segs, bs, G, 1, d.num_kv_heads, opt, S);
+  // combine: node j of request r reads every chunk of r, holder index j
+  S->comb_ptr.resize(S->n_branch + 1);
+  for (int32_t r = 0; r < n_req; ++r)
+    for (int32_t j = 0; j < n_nodes; ++j) {
+      const int32_t b = r * n_nodes + j;
+      S->comb_ptr[b] = (int32_t)S->comb_rows.size();
+      for (int32_t c = segs[r].chunk_begin; c < segs[r].chunk_end; ++c)
+        S->comb_rows.push_back(chunks[c].part_base + j * G);
+    }
+  S->comb_ptr[S->n_branch] = (int32_t)S->comb_rows.size();
+  S->layout(d.num_kv_heads, d.head_dim);
+  return PKV_OK;
+}
+
+}  // namespace pkv

@@ -1,0 +1,63 @@
+// Host planner for the attention kernels: from the block tables of a batch
+// of sequences to segments (runs of blocks shared by the same set of
+// sequences), chunks and work items, plus the per-branch list of partial
+// states the combine step merges. See attn_plan.h for the device-side records.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "pool.hpp"
+#include "attn_plan.h"
+
+namespace pkv {
+
+struct SchedOptions {
+  int32_t chunk_tokens = 0;        // 0 = automatic
+  int32_t rows_per_item = 64;      // matrix-core path; 16 for the VALU path
+  int32_t target_workgroups = 2048;
+  int32_t min_chunk_tokens = 256;
+  int32_t max_chunk_tokens = 4096;
+  int32_t tokens_per_row = 40;     // chunk length per query row (keeps partial traffic ~5%)
+};
+
+struct Schedule {
+  std::vector<WorkItem> items;
+  std::vector<int32_t> blk;
+  std::vector<int32_t> holders;
+  std::vector<int32_t> comb_ptr;
+  std::vector<int32_t> comb_rows;
+  std::vector<uint64_t> anc;
+  int32_t P = 0;         // partial rows per (layer, KV head) plane
+  int32_t n_branch = 0;  // query rows' branches (sequences, or requests x nodes)
+  int32_t n_layers = 0;
+  int32_t n_segments = 0;
+  int32_t n_chunks = 0;
+  int64_t unique_tokens = 0;  // distinct (block, slot) token positions read per plane
+
+  // byte offsets inside the workspace
+  size_t off_items = 0, off_blk = 0, off_holders = 0, off_comb_ptr = 0, off_comb_rows = 0,
+         off_anc = 0, meta_bytes = 0, off_ml = 0, off_acc = 0, total_bytes = 0;
+
+  void layout(int Hkv, int D);
+  void pack_meta(uint8_t* dst) const;  // writes meta_bytes bytes
+};
+
+// Scratch arrays sized by the pool's block count, reused between calls.
+struct PlannerScratch {
+  std::vector<uint32_t> stamp;
+  std::vector<int32_t> cnt, pos, valid, off, fill, seg;
+  uint32_t epoch = 0;
+  void ensure(int nb);
+};
+
+int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int32_t n_layers,
+                          int32_t layer0, const SchedOptions& opt, PlannerScratch* scratch,
+                          Schedule* out);
+
+int build_verify_schedule(const Pool& pool, const pkv_seq* reqs, int32_t n_req,
+                          const int32_t* parents, int32_t n_nodes, const SchedOptions& opt,
+                          Schedule* out);
+
+}  // namespace pkv

@@ -1,0 +1,374 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tables and K/V bytes: bit-exact. Attention outputs: max |error| <= 2e-3 and
+relative L2 error <= 1e-2 against the oracle's float64 values (bf16 K/V,
+fp32 arithmetic). The relative guard matters at long contexts, where
+outputs are small (|o| ~ sqrt(e/N)) and 2e-3 alone would be loose.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from workloads import configs, generate, get, scaled  # noqa: E402
+from workloads.configs import replace_shape  # noqa: E402
+from workloads.gen import Tensor, draw  # noqa: E402
+
+from gpu_helpers import (arena_bits, build_library, build_oracle, errors, gather,  # noqa: E402
+                         raw_bits, to_device)
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-3
+REL_L2 = 1e-2
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_close(got, want, what):
+    ma, rl = errors(got, want)
+    note(f"{what}: max_abs={ma:.3e} rel_l2={rl:.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert ma <= MAX_ABS and rl <= REL_L2, (what, ma, rl)
+    return ma, rl
+
+
+B16 = configs.BEAM
+AG = configs.AGENT
+
+SMALL_DECODE = [
+    get("tiny_a"),
+    get("tiny_b"),
+    scaled("beam", "beam_s", shape=replace_shape(B16, L=3, Hq=8, Hkv=2), root_len=200,
+           n_branches=5, branch_len=37),
+    scaled("mcts", "mcts_s", shape=replace_shape(B16, L=2, Hq=8, Hkv=2), root_len=100, depth=3,
+           edge_len=21),
+    scaled("agent", "agent_s", shape=replace_shape(AG, Hq=12, Hkv=2), root_len=300, n_branches=3,
+           branch_len=170),
+    scaled("beam_cow", "cow_d64", shape=replace_shape(B16, L=2, Hq=4, Hkv=1, D=64), root_len=40,
+           n_branches=5, branch_len=3),
+    scaled("beam", "bs64_d64", shape=replace_shape(B16, L=2, Hq=6, Hkv=3, D=64, BS=64), root_len=130,
+           n_branches=3, branch_len=70),
+    scaled("agent", "gqa1_d128_bs32", shape=replace_shape(AG, Hq=2, Hkv=2, D=128), root_len=33,
+           n_branches=2, branch_len=1),
+]
+
+
+def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None):
+    inp = generate(w)
+    c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    c.set_option("path", path)
+    c.set_option("chunk_tokens", chunk_tokens)
+    if rows_per_item:
+        c.set_option("rows_per_item", rows_per_item)
+    seqs = [h[s] for s in w.query_sids]
+    q = to_device(inp.q)
+    out = c.decode(seqs, q, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    c.close()
+    return inp, res
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _lib(pkv):
+    pytest.pkv = pkv
+
+
+@pytest.mark.parametrize("w", SMALL_DECODE, ids=lambda w: w.name)
+@pytest.mark.parametrize("path,chunk", [(0, 0), (0, 64), (1, 0), (1, 64)],
+                         ids=["auto", "auto_split64", "valu", "valu_split64"])
+def test_decode_matches_oracle(w, path, chunk):
+    note(f"decode {w.name} path={path} chunk={chunk}")
+    inp, got = run_decode(w, path=path, chunk_tokens=chunk)
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"{w.name} path={path} chunk={chunk}")
+
+
+@pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[3], SMALL_DECODE[4]], ids=lambda w: w.name)
+def test_page_layout_does_not_change_output(w):
+    """A permuted allocation order moves every block; the plan depends only
+    on the logical structure, so the output is bit-identical."""
+    note(f"layout {w.name}")
+    _, a = run_decode(w)
+    order = np.random.default_rng(7).permutation(w.num_blocks_bound() + 8)
+    _, b = run_decode(w, order=order)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[4]], ids=lambda w: w.name)
+def test_split_and_row_grouping_agree(w):
+    note(f"splits {w.name}")
+    inp, base = run_decode(w)
+    for chunk, rpi in [(32, None), (96, 16), (0, 8), (0, 48)]:
+        _, other = run_decode(w, chunk_tokens=chunk, rows_per_item=rpi)
+        ma, _ = errors(other, base)
+        assert ma <= 1e-4, (chunk, rpi, ma)
+
+
+@pytest.mark.parametrize("name,keep_root", [("tiny_a", True), ("tiny_b", True), ("tiny_b", False)])
+def test_cow_and_writes_bit_exact(name, keep_root):
+    """Every live sequence, read through the library's table from the device
+    arenas, holds exactly its materialised tokens; the root keeps its own
+    tokens while the branches copy and append (a fork never changes the
+    parent)."""
+    w = get(name)
+    inp = generate(w)
+    c, h = build_library(pytest.pkv, w, inp, free_ops=not keep_root)
+    pool = build_oracle(w, inp, free_ops=not keep_root)
+    kb, vb = arena_bits(c.k_arena), arena_bits(c.v_arena)
+    for sid in pool.live():
+        K, V = gather(c, kb, vb, h[sid])
+        Ko, Vo = pool.kv(sid)
+        assert np.array_equal(K, raw_bits(Ko, w.shape.dtype)), sid
+        assert np.array_equal(V, raw_bits(Vo, w.shape.dtype)), sid
+    c.close()
+
+
+@pytest.mark.parametrize("seed,dtype,bs", [(0, "bf16", 16), (1, "f32", 16), (2, "bf16", 32), (3, "bf16", 64)])
+def test_random_traces_device_bit_exact(pkv, seed, dtype, bs):
+    """Random create / fork / append / free traces with real K/V: tables and
+    the bytes every live sequence reads equal the oracle's."""
+    note(f"random device trace seed={seed} {dtype} bs={bs}")
+    rng = np.random.default_rng(1000 + seed)
+    L, Hkv, Hq, D = 2, 2, 4, 64
+    nb = 400   # large enough that the trace never runs dry (OOM is tested on the host)
+    order = rng.permutation(nb).tolist() if seed % 2 else None
+    c = pkv.PagedKVCache(nb, bs, L, Hkv, Hq, D, dtype=dtype, device="cuda", alloc_order=order)
+    pool = oracle.OraclePool(nb, bs, alloc_order=order)
+    h = {}
+    sh = configs.Shape(L=L, Hq=Hq, Hkv=Hkv, D=D, BS=bs, dtype=dtype)
+    for step in range(120):
+        act = int(rng.integers(5)) if h else 0
+        if act == 0 and len(h) < 10:
+            sid = pool.create()
+            h[sid] = c.create()
+        elif act == 1 and len(h) < 10:
+            p = list(h)[rng.integers(len(h))]
+            sid = pool.fork(p)
+            h[sid] = c.fork(h[p])
+        elif act in (2, 3):
+            sids = list(rng.choice(list(h), size=min(len(h), int(rng.integers(1, 4))), replace=False))
+            counts = [int(rng.integers(0, bs + 5)) for _ in sids]
+            ks, vs = [], []
+            for n in counts:
+                k = draw(rng, (L, n, Hkv, D), dtype)
+                v = draw(rng, (L, n, Hkv, D), dtype)
+                ks.append(k)
+                vs.append(v)
+            for s, k, v in zip(sids, ks, vs):
+                pool.append(int(s), k.f32(), v.f32())
+            kcat = np.concatenate([k.raw for k in ks], axis=1)
+            vcat = np.concatenate([v.raw for v in vs], axis=1)
+            if sum(counts):
+                c.append([h[int(s)] for s in sids], counts, to_device(Tensor(kcat, dtype)),
+                         to_device(Tensor(vcat, dtype)))
+        elif h:
+            sid = list(h)[rng.integers(len(h))]
+            pool.free(sid)
+            c.free(h.pop(sid))
+    torch.cuda.synchronize()
+    kb, vb = arena_bits(c.k_arena), arena_bits(c.v_arena)
+    checked = 0
+    for sid in pool.live():
+        assert c.table(h[sid]) == pool.table(sid)
+        if pool.length(sid) == 0:
+            continue
+        K, V = gather(c, kb, vb, h[sid])
+        Ko, Vo = pool.kv(sid)
+        assert np.array_equal(K, raw_bits(Ko, dtype))
+        assert np.array_equal(V, raw_bits(Vo, dtype))
+        checked += 1
+    assert checked > 0
+    c.close()
+
+
+# ------------------------------------------------------------------ verify
+
+def run_verify(w, order=None, chunk_tokens=0, parents=None):
+    inp = generate(w)
+    if parents is not None:
+        inp.parents = parents
+    c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    c.set_option("chunk_tokens", chunk_tokens)
+    reqs = [h[s] for s in w.query_sids]
+    out = c.verify(reqs, inp.parents, to_device(inp.q), scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    c.close()
+    return inp, res
+
+
+SMALL_VERIFY = [
+    scaled("verify", "verify_s", shape=replace_shape(AG, Hq=12, Hkv=2), n_req=2, ctx_len=200,
+           n_nodes=13, max_depth=4),
+    scaled("verify", "verify_d128_bs16", shape=replace_shape(B16, L=1, Hq=8, Hkv=2), n_req=3,
+           ctx_len=77, n_nodes=48, max_depth=8),
+    scaled("verify", "verify_64nodes", shape=replace_shape(AG, Hq=4, Hkv=1, D=64, BS=64), n_req=1,
+           ctx_len=64, n_nodes=64, max_depth=64),
+    scaled("verify", "verify_1node", shape=replace_shape(AG, Hq=6, Hkv=1, D=128), n_req=2, ctx_len=5,
+           n_nodes=1, max_depth=1),
+    scaled("verify", "verify_noctx", shape=replace_shape(AG, Hq=6, Hkv=3, D=128), n_req=2, ctx_len=0,
+           n_nodes=20, max_depth=5),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_VERIFY, ids=lambda w: w.name)
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_verify_matches_oracle(w, chunk):
+    note(f"verify {w.name} chunk={chunk}")
+    inp, got = run_verify(w, chunk_tokens=chunk)
+    pool = build_oracle(w, inp)
+    want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"verify {w.name} chunk={chunk}")
+
+
+def test_verify_chain_and_star_trees():
+    w = SMALL_VERIFY[0]
+    N = w.n_nodes
+    for name, par in [("chain", np.arange(N) - 1), ("star", np.full(N, -1))]:
+        parents = np.stack([par] * len(w.query_sids)).astype(np.int32)
+        inp, got = run_verify(w, parents=parents)
+        pool = build_oracle(w, inp)
+        want = oracle.verify(pool, w.query_sids, parents, inp.q.f32(), w.softmax_scale)
+        check_close(got, want, f"verify {name}")
+
+
+# --------------------------------------------------------- errors, edges
+
+def test_errors_are_reported(pkv):
+    c = pkv.PagedKVCache(8, 16, 1, 1, 2, 64, dtype="bf16", device="cuda")
+    s = c.create()
+    q = torch.zeros((1, 1, 2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pkv.PkvError) as e:          # empty sequence
+        c.decode([s], q)
+    assert e.value.code == pkv.PKV_E_INVALID
+    k = torch.zeros((1, 3, 1, 64), dtype=torch.bfloat16, device="cuda")
+    c.append([s], [3], k, k)
+    with pytest.raises(pkv.PkvError):               # layer range
+        c.decode([s], q, layer0=1, n_layers=1)
+    with pytest.raises(pkv.PkvError) as e:          # 65 tree nodes
+        c.verify([s], np.full((1, 65), -1), torch.zeros((1, 65, 2, 64), dtype=torch.bfloat16,
+                                                        device="cuda"))
+    with pytest.raises(pkv.PkvError):               # bad parent pointer
+        c.verify([s], np.array([[0, 0, 1]]), torch.zeros((1, 3, 2, 64), dtype=torch.bfloat16,
+                                                          device="cuda"))
+    from paged_kv_cache_amd import binding
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, 1, 2, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(pkv.PkvError) as e:
+        binding.pkv_decode_attn(c.handle, [s], 0, 1, q, out, 0.1, small)
+    assert e.value.code == pkv.PKV_E_WORKSPACE
+    f = pkv.PagedKVCache(8, 16, 1, 1, 1, 64, dtype="f32", device="cuda")
+    t = f.create()
+    kf = torch.zeros((1, 2, 1, 64), dtype=torch.float32, device="cuda")
+    f.append([t], [2], kf, kf)
+    with pytest.raises(pkv.PkvError) as e:          # verify needs bf16
+        f.verify([t], np.array([[-1]]), torch.zeros((1, 1, 1, 64), device="cuda"))
+    assert e.value.code == pkv.PKV_E_UNSUPPORTED
+    c.close()
+    f.close()
+
+
+def test_single_token_returns_its_value(pkv):
+    c = pkv.PagedKVCache(4, 16, 2, 2, 6, 128, dtype="bf16", device="cuda")
+    s = c.create()
+    rng = np.random.default_rng(3)
+    k = draw(rng, (2, 1, 2, 128), "bf16")
+    v = draw(rng, (2, 1, 2, 128), "bf16")
+    c.append([s], [1], to_device(k), to_device(v))
+    q = to_device(draw(rng, (2, 1, 6, 128), "bf16"))
+    out = c.decode([s, s], torch.cat([q, q], dim=1)).cpu().numpy()
+    want = v.f32()[:, 0]                            # [L][Hkv][D]
+    for l in range(2):
+        for hh in range(6):
+            assert np.array_equal(out[l, 0, hh], want[l, hh // 3])
+            assert np.array_equal(out[l, 1, hh], want[l, hh // 3])
+    c.close()
+
+
+# ------------------------------------------------ full-size, sampled outputs
+
+def sampled_decode(name, n_samples=48, seed=0):
+    w = get(name)
+    note(f"full-size {name}: generating inputs")
+    inp = generate(w)
+    c, h = build_library(pytest.pkv, w, inp)
+    seqs = [h[s] for s in w.query_sids]
+    q = to_device(inp.q)
+    out = c.decode(seqs, q, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    info = c.plan_info(seqs)
+    c.close()
+    note(f"full-size {name}: plan {info}")
+    pool = build_oracle(w, inp)
+    rng = np.random.default_rng(seed)
+    qf = inp.q.f32()
+    L, B, Hq, D = got.shape
+    worst = 0.0
+    gs, ws = [], []
+    for _ in range(n_samples):
+        l, b, hh = int(rng.integers(L)), int(rng.integers(B)), int(rng.integers(Hq))
+        want = oracle.decode_one(pool, w.query_sids[b], qf[l, b, hh], l, hh, Hq, w.softmax_scale)
+        gs.append(got[l, b, hh])
+        ws.append(want)
+    check_close(np.stack(gs), np.stack(ws), f"full-size {name} ({n_samples} sampled rows)")
+    assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("name", ["beam", "mcts", "agent"])
+def test_full_size_decode_sampled(name):
+    sampled_decode(name)
+
+
+def test_full_size_verify_sampled():
+    w = get("verify")
+    note("full-size verify: generating inputs")
+    inp = generate(w)
+    c, h = build_library(pytest.pkv, w, inp)
+    reqs = [h[s] for s in w.query_sids]
+    out = c.verify(reqs, inp.parents, to_device(inp.q), scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    c.close()
+    pool = build_oracle(w, inp)
+    qf = inp.q.f32()
+    rng = np.random.default_rng(1)
+    gs, ws = [], []
+    for _ in range(24):
+        r, i, hh = int(rng.integers(4)), int(rng.integers(w.n_nodes)), int(rng.integers(w.shape.Hq))
+        K, V = pool.kv(w.query_sids[r], layer=0)
+        ctx = K.shape[0] - w.n_nodes
+        idx = list(range(ctx)) + [ctx + j for j in oracle.ancestors(inp.parents[r], i)]
+        g = hh // w.shape.G
+        want = oracle.attention._softmax_attend(qf[r, i, hh][None], K[idx, g], V[idx, g],
+                                                w.softmax_scale)[0]
+        gs.append(got[r, i, hh])
+        ws.append(want)
+    check_close(np.stack(gs), np.stack(ws), "full-size verify (24 sampled rows)")
+    assert np.all(np.isfinite(got))
+
+
+def test_full_size_beam_cow_bit_exact():
+    w = get("beam_cow")
+    inp = generate(w)
+    c, h = build_library(pytest.pkv, w, inp, free_ops=False)
+    pool = build_oracle(w, inp, free_ops=False)
+    assert len(pool.cow_log) == 8
+    kb, vb = arena_bits(c.k_arena), arena_bits(c.v_arena)
+    for sid in pool.live():
+        K, V = gather(c, kb, vb, h[sid])
+        Ko, Vo = pool.kv(sid)
+        assert np.array_equal(K, raw_bits(Ko, "bf16")) and np.array_equal(V, raw_bits(Vo, "bf16"))
+    c.close()

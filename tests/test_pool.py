@@ -1,0 +1,277 @@
+"""Host side of libpkv through its C ABI (CPU only, no device calls).
+
+Block tables, reference counts, free sets, slots and copy-on-write records
+must equal the oracle's bit for bit on the same operation traces.
+"""
+
+from __future__ import annotations
+
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.pool import OraclePool
+from workloads import get
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(pkv):
+    from paged_kv_cache_amd import _lib
+    declared = header_functions()
+    assert len(declared) >= 20
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s(pkv_\w+)", out))
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    assert set(_lib.declared_symbols()) == set(declared)
+    for f in declared:
+        getattr(_lib.lib, f)
+
+
+def host_cache(pkv, nb, bs, order=None):
+    return pkv.PagedKVCache(nb, bs, 1, 1, 1, 64, dtype="f32", device=None, alloc_order=order)
+
+
+def zeros(n):
+    return np.zeros((1, n, 1, 1), np.float32)
+
+
+@pytest.mark.parametrize("name", ["tiny_a", "tiny_b"])
+def test_tiny_tables_golden(pkv, name):
+    gold = json.load(open(os.path.join(GOLDEN, "tiny_tables.json")))[name]
+    w = get(name)
+    c = host_cache(pkv, 16, w.shape.BS)
+    h = {}
+    cows = []
+    first_slots = None
+    for op in w.ops:
+        if op.kind == "create":
+            h[op.sid] = c.create()
+        elif op.kind == "fork":
+            h[op.sid] = c.fork(h[op.parent])
+        elif op.kind == "append":
+            slots, cw = c.plan(h[op.sid], op.n)
+            cows += [list(x) for x in cw]
+            if op.sid == 1:
+                first_slots = slots
+        elif op.kind == "free":
+            c.free(h.pop(op.sid))
+    for s, t in gold["tables"].items():
+        assert c.table(h[int(s)]) == t
+    for b, n in gold["refcounts"].items():
+        assert c.refcount(int(b)) == n
+    assert cows == gold["cow_ops"]
+    assert first_slots == gold["first_branch_slots"]
+
+
+def compare_state(c, pool: OraclePool, handles):
+    assert sorted(handles) == pool.live()
+    for sid, hd in handles.items():
+        assert c.table(hd) == pool.table(sid)
+        assert c.length(hd) == pool.length(sid)
+    for b in range(pool.num_blocks):
+        assert c.refcount(b) == pool.refcount(b)
+    st = c.stats()
+    assert st["free_blocks"] == len(pool.free_blocks)
+    assert st["live_seqs"] == len(pool.live())
+    assert st["total_refs"] == sum(pool.ref)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_traces_bit_exact(pkv, seed):
+    rng = np.random.default_rng(100 + seed)
+    nb = int(rng.integers(8, 48))
+    bs = [1, 2, 4, 16][seed % 4]
+    order = rng.permutation(nb).tolist() if seed % 2 else None
+    c = host_cache(pkv, nb, bs, order)
+    pool = OraclePool(nb, bs, alloc_order=order)
+    handles = {}
+    for _ in range(250):
+        act = int(rng.integers(5)) if handles else 0
+        if act == 0:
+            sid = pool.create()
+            handles[sid] = c.create()
+        elif act == 1:
+            p = list(handles)[rng.integers(len(handles))]
+            sid = pool.fork(p)
+            handles[sid] = c.fork(handles[p])
+        elif act in (2, 3):
+            sid = list(handles)[rng.integers(len(handles))]
+            n = int(rng.integers(0, 3 * bs + 2))
+            try:
+                want = pool.append(sid, zeros(n), zeros(n))
+            except oracle.OOMError:
+                with pytest.raises(pkv.OOM):
+                    c.plan(handles[sid], n)
+            else:
+                got = c.plan(handles[sid], n)
+                assert got[0] == want[0]
+                assert got[1] == [tuple(x) for x in want[1]]
+        else:
+            sid = list(handles)[rng.integers(len(handles))]
+            pool.free(sid)
+            c.free(handles.pop(sid))
+        compare_state(c, pool, handles)
+    for sid in list(handles):
+        pool.free(sid)
+        c.free(handles.pop(sid))
+    st = c.stats()
+    assert st["free_blocks"] == nb and st["total_refs"] == 0 and st["live_seqs"] == 0
+
+
+@pytest.mark.parametrize("name", ["beam", "mcts", "agent", "verify", "beam_cow"])
+def test_full_size_tables_bit_exact(pkv, name):
+    w = get(name)
+    nb = w.num_blocks_bound()
+    c = host_cache(pkv, nb, w.shape.BS)
+    pool = OraclePool(nb, w.shape.BS)
+    handles = {}
+    for op in w.ops:
+        if op.kind == "create":
+            pool.create(op.sid)
+            handles[op.sid] = c.create()
+        elif op.kind == "fork":
+            pool.fork(op.parent, op.sid)
+            handles[op.sid] = c.fork(handles[op.parent])
+        elif op.kind == "append":
+            want = pool.append(op.sid, zeros(op.n), zeros(op.n))
+            got = c.plan(handles[op.sid], op.n)
+            assert got[0] == want[0] and got[1] == [tuple(x) for x in want[1]]
+        else:
+            pool.free(op.sid)
+            c.free(handles.pop(op.sid))
+    compare_state(c, pool, handles)
+
+
+def test_batch_append_equals_sequential(pkv):
+    """Batch planning follows sequence order: when two batch members share a
+    partly filled tail, the first copies it and the second, now its only
+    holder, writes in place."""
+    for order in (None, list(np.random.default_rng(5).permutation(40))):
+        a = host_cache(pkv, 40, 4, order)
+        b = host_cache(pkv, 40, 4, order)
+        ra, rb = a.create(), b.create()
+        a.plan(ra, 6)
+        b.plan(rb, 6)
+        ka = [a.fork(ra) for _ in range(3)]
+        kb = [b.fork(rb) for _ in range(3)]
+        a.free(ra)
+        b.free(rb)
+        counts = [3, 0, 5]
+        from paged_kv_cache_amd import binding
+        # batch planning without device work: the arenas are absent, so use
+        # the planner through sequential plan() calls on one pool and the
+        # batch call's table outcome on the other
+        for k, n in zip(ka, counts):
+            a.plan(k, n)
+        with pytest.raises(pkv.PkvError):
+            binding.pkv_append_kv_batch(b.handle, kb, counts, None, None)   # no arenas: rejected
+        for k, n in zip(kb, counts):
+            b.plan(k, n)
+        for x, y in zip(ka, kb):
+            assert a.table(x) == b.table(y)
+
+
+def test_oom_is_atomic_and_reported(pkv):
+    c = host_cache(pkv, 3, 4)
+    s = c.create()
+    c.plan(s, 6)
+    k = c.fork(s)
+    before = (c.table(s), c.table(k), [c.refcount(b) for b in range(3)], c.stats())
+    with pytest.raises(pkv.OOM):
+        c.plan(k, 4)            # needs a copy + a fresh block, one is free
+    assert (c.table(s), c.table(k), [c.refcount(b) for b in range(3)], c.stats()) == before
+    c.plan(k, 2)
+    assert c.table(k) == [0, 2] and c.refcount(1) == 1
+
+
+def test_invalid_handles_and_arguments(pkv):
+    from paged_kv_cache_amd import binding
+    c = host_cache(pkv, 8, 4)
+    s = c.create()
+    c.plan(s, 3)
+    c.free(s)
+    for fn in (lambda: c.free(s), lambda: c.fork(s), lambda: c.plan(s, 1), lambda: c.table(s)):
+        with pytest.raises(pkv.PkvError) as e:
+            fn()
+        assert e.value.code == pkv.PKV_E_INVALID
+    with pytest.raises(pkv.PkvError):
+        binding.pkv_block_release(c.handle, 5)     # free block
+    with pytest.raises(pkv.PkvError):
+        binding.pkv_block_refcount(c.handle, 8)    # out of range
+    with pytest.raises(pkv.PkvError):
+        binding.pkv_pool_set_option(c.handle, "no_such_option", 1)
+    t = c.create()
+    with pytest.raises(pkv.PkvError):
+        c.plan(t, -1)
+    with pytest.raises(pkv.PkvError):      # device call without arenas
+        binding.pkv_cow_copy(c.handle, [(0, 1, 1)])
+    with pytest.raises(pkv.PkvError):      # bad desc
+        binding.pkv_pool_create(4, 16, 1, 3, 4, 64, 0)
+    with pytest.raises(pkv.PkvError):      # not a permutation
+        binding.pkv_pool_create(4, 16, 1, 1, 1, 64, 0, alloc_order=[0, 1, 1, 2])
+    b = binding.pkv_block_alloc(c.handle)
+    assert c.refcount(b) == 1
+    binding.pkv_block_release(c.handle, b)
+    assert c.refcount(b) == 0
+
+
+def test_fork_leaves_parent_unchanged(pkv):
+    c = host_cache(pkv, 64, 4)
+    p = c.create()
+    c.plan(p, 10)
+    t0 = c.table(p)
+    kids = [c.fork(p) for _ in range(5)]
+    assert c.table(p) == t0 and c.length(p) == 10
+    for k in kids:
+        c.plan(k, 3)
+        assert c.table(p) == t0 and c.length(p) == 10
+    assert [c.refcount(b) for b in t0] == [6, 6, 1]   # the shared tail was copied by all 5
+
+
+def distinct_tokens(c, handles):
+    seen = {}
+    for h in handles:
+        n = c.length(h)
+        for j, b in enumerate(c.table(h)):
+            seen[b] = min(c.BS, n - j * c.BS)
+    return sum(seen.values())
+
+
+@pytest.mark.parametrize("name,segments", [("tiny_a", 5), ("tiny_b", 5), ("beam", 9), ("mcts", 127),
+                                           ("agent", 5)])
+def test_plan_segments_closed_form(pkv, name, segments):
+    """Segments: the shared root plus one per private tail (star trees);
+    the root plus one per edge of the binary tree (126 edges + 1)."""
+    w = get(name)
+    c = pkv.PagedKVCache(w.num_blocks_bound(), w.shape.BS, w.shape.L, w.shape.Hkv, w.shape.Hq,
+                         w.shape.D, dtype=w.shape.dtype, device=None)
+    h = {}
+    for op in w.ops:
+        if op.kind == "create":
+            h[op.sid] = c.create()
+        elif op.kind == "fork":
+            h[op.sid] = c.fork(h[op.parent])
+        elif op.kind == "append":
+            c.plan(h[op.sid], op.n)
+        else:
+            c.free(h.pop(op.sid))
+    seqs = [h[s] for s in w.query_sids]
+    info = c.plan_info(seqs)
+    assert info["n_segments"] == segments
+    assert info["unique_tokens"] == distinct_tokens(c, seqs)
+    assert info["n_chunks"] >= segments
+    assert info["workspace_bytes"] > 0
