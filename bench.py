@@ -164,7 +164,7 @@ def run_beam(args, pkv, torch):
     for _ in range(args.warmup):
         beam_step(c, beams, step_k, step_v, q, out, scale)
     torch.cuda.synchronize()
-    for kname in ("attention", "combine", "cow_copy", "kv_write"):
+    for kname in ("attention", "combine", "append"):
         c.timing_read(kname)
     c.set_option("timing", 1)
     torch.cuda.synchronize()
@@ -174,7 +174,7 @@ def run_beam(args, pkv, torch):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     c.set_option("timing", 0)
-    ktimes = {k: c.timing_read(k) for k in ("attention", "combine", "cow_copy", "kv_write")}
+    ktimes = {k: c.timing_read(k) for k in ("attention", "combine", "append")}
     if args.calibrate_copy:
         calibrate_copy(torch)
     ms_step = dt / args.steps * 1e3
@@ -215,14 +215,19 @@ def run_beam(args, pkv, torch):
 
 
 def calibrate_copy(torch):
-    """A plain device copy of known size, for scaling the HBM counters."""
-    n = 256 << 20
+    """A plain device copy of known size (1 GiB read + 1 GiB written), for
+    scaling the HBM counters. A 1 GiB fill of another buffer in between
+    evicts the source from the 256 MB last-level cache."""
+    n = 1 << 30
     a = torch.empty(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
+    flush = torch.empty_like(a)
     a.fill_(1)
+    flush.fill_(2)
     torch.cuda.synchronize()
     b.copy_(a)
     torch.cuda.synchronize()
+    del a, b, flush
 
 
 # --------------------------------------------------------- other trees

@@ -237,15 +237,16 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  *   "chunk_tokens"      0 automatic: tokens per chunk of a shared segment
  *   "rows_per_item"     64: query rows one workgroup serves
  *   "target_workgroups" 2048: chunks are shortened until the grid has this many
- *   "timing"            0: 1 records a pair of HIP events around every kernel
- *                       launch on its stream (read with pkv_timing_read)
+ *   "timing"            0: 1 records a pair of HIP events at the start and end
+ *                       of every kernel the pool launches (pkv_timing_read)
  * Unknown keys or out-of-range values are PKV_E_INVALID. */
 int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value);
 
 /* Device time of the kernels launched since the last read (with the
- * "timing" option on): kernel is "attention", "combine", "cow_copy" or
- * "kv_write". Waits for the last recorded launch, returns the summed
- * milliseconds and the launch count, and resets both. */
+ * "timing" option on): kernel is "attention", "combine" or "append" (the
+ * launch that performs copy-on-write copies and token writes). Waits for
+ * the last recorded launch, returns the summed milliseconds and the launch
+ * count, and resets both. */
 int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_t* launches);
 
 /* Last error message of this thread ("" if none). */

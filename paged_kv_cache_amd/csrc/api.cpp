@@ -3,6 +3,7 @@
 // this file.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -45,7 +46,7 @@ struct KernelTimer {
         (void)hipEventDestroy(pr.second);
       }
   }
-  int start(hipStream_t s, hipEvent_t* stop) {
+  int take(LaunchEvents* ev) {
     std::pair<hipEvent_t, hipEvent_t> pr;
     if (!spare.empty()) {
       pr = spare.back();
@@ -56,9 +57,8 @@ struct KernelTimer {
       if ((e = hipEventCreate(&pr.second)) != hipSuccess) return hip_fail(e, "hipEventCreate");
     }
     used.push_back(pr);
-    hipError_t e = hipEventRecord(pr.first, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    *stop = pr.second;
+    ev->start = pr.first;
+    ev->stop = pr.second;
     return PKV_OK;
   }
   int read(double* ms, int64_t* n) {
@@ -79,27 +79,24 @@ struct KernelTimer {
   }
 };
 
-enum { T_ATTN = 0, T_COMBINE = 1, T_COW = 2, T_WRITE = 3, T_KINDS = 4 };
+enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_KINDS = 3 };
 
 struct pkv_pool {
   explicit pkv_pool(const pkv_pool_desc& d) : pool(d) {}
   bool timing = false;
   KernelTimer timers[T_KINDS];
 
-  // Launches `launch` (returning hipError_t), bracketed by timing events
-  // when timing is on.
+  // Calls launch(LaunchEvents) (returning hipError_t); with timing on, the
+  // events record the kernel's own start and end.
   template <typename F>
-  int timed(int kind, hipStream_t s, F&& launch, const char* what) {
-    hipEvent_t stop = nullptr;
+  int timed(int kind, F&& launch, const char* what) {
+    LaunchEvents ev;
     if (timing) {
-      int rc = timers[kind].start(s, &stop);
+      int rc = timers[kind].take(&ev);
       if (rc) return rc;
     }
-    hipError_t e = launch();
+    hipError_t e = launch(ev);
     if (e != hipSuccess) return hip_fail(e, what);
-    if (stop) {
-      if ((e = hipEventRecord(stop, s)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
     return PKV_OK;
   }
 
@@ -215,42 +212,54 @@ size_t elem_size(const pkv_pool_desc& d) { return d.kv_dtype == PKV_F32 ? 4 : 2;
 
 bool has_arenas(const pkv_pool_desc& d) { return d.k_arena && d.v_arena; }
 
-int enqueue_cow(pkv_pool* p, const std::vector<pkv_cow_op>& ops, hipStream_t stream) {
-  if (ops.empty()) return PKV_OK;
+// Copy-on-write copies and token writes of one append, in one launch. Short
+// lists travel in the kernel arguments; longer ones are staged to the
+// pool's device metadata buffer in one upload.
+int enqueue_append(pkv_pool* p, const pkv_cow_op* ops, int32_t n_ops, const int64_t* slots,
+                   int32_t n_slots, const void* k_new, const void* v_new, hipStream_t stream) {
+  if (n_ops == 0 && n_slots == 0) return PKV_OK;
   const pkv_pool_desc& d = p->pool.desc();
-  const size_t bytes = ops.size() * sizeof(pkv_cow_op);
-  int rc = p->ensure_dmeta(bytes, stream);
-  if (rc) return rc;
-  rc = p->upload(p->dmeta, bytes, stream,
-                 [&](uint8_t* h) { std::memcpy(h, ops.data(), bytes); });
-  if (rc) return rc;
+  AppendParams a{};
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_arena = d.k_arena;
+  a.v_arena = d.v_arena;
+  a.n_ops = n_ops;
+  a.n_slots = n_slots;
+  a.L = d.num_layers;
+  a.NB = d.num_blocks;
+  a.Hkv = d.num_kv_heads;
+  a.D = d.head_dim;
+  a.BS = d.block_size;
+  if (n_ops <= kInlineOps && n_slots <= kInlineSlots) {
+    for (int32_t i = 0; i < n_ops; ++i) {
+      a.inl_ops[3 * i] = ops[i].src;
+      a.inl_ops[3 * i + 1] = ops[i].dst;
+      a.inl_ops[3 * i + 2] = ops[i].n_valid;
+    }
+    for (int32_t i = 0; i < n_slots; ++i) a.inl_slots[i] = slots[i];
+  } else {
+    const size_t slot_bytes = (size_t)n_slots * sizeof(int64_t);
+    const size_t op_off = (slot_bytes + 255) & ~size_t(255);
+    const size_t bytes = op_off + (size_t)n_ops * 3 * sizeof(int32_t);
+    int rc = p->ensure_dmeta(bytes, stream);
+    if (rc) return rc;
+    rc = p->upload(p->dmeta, bytes, stream, [&](uint8_t* h) {
+      if (n_slots) std::memcpy(h, slots, slot_bytes);
+      int32_t* o = (int32_t*)(h + op_off);
+      for (int32_t i = 0; i < n_ops; ++i) {
+        o[3 * i] = ops[i].src;
+        o[3 * i + 1] = ops[i].dst;
+        o[3 * i + 2] = ops[i].n_valid;
+      }
+    });
+    if (rc) return rc;
+    a.slots = (const int64_t*)p->dmeta;
+    a.ops = (const int32_t*)((uint8_t*)p->dmeta + op_off);
+  }
   return p->timed(
-      T_COW, stream,
-      [&] {
-        return launch_cow_copy(d.kv_dtype, d.k_arena, d.v_arena, (const int32_t*)p->dmeta,
-                               (int)ops.size(), d.num_layers, d.num_blocks, d.num_kv_heads,
-                               d.head_dim, d.block_size, stream);
-      },
-      "cow_copy launch");
-}
-
-int enqueue_write(pkv_pool* p, const int64_t* slots, int32_t n, const void* k_new,
-                  const void* v_new, hipStream_t stream) {
-  if (n == 0) return PKV_OK;
-  const pkv_pool_desc& d = p->pool.desc();
-  const size_t bytes = (size_t)n * sizeof(int64_t);
-  int rc = p->ensure_dmeta(bytes, stream);
-  if (rc) return rc;
-  rc = p->upload(p->dmeta, bytes, stream, [&](uint8_t* h) { std::memcpy(h, slots, bytes); });
-  if (rc) return rc;
-  return p->timed(
-      T_WRITE, stream,
-      [&] {
-        return launch_kv_write(d.kv_dtype, k_new, v_new, d.k_arena, d.v_arena,
-                               (const int64_t*)p->dmeta, n, d.num_layers, d.num_blocks,
-                               d.num_kv_heads, d.head_dim, d.block_size, stream);
-      },
-      "kv_write launch");
+      T_APPEND, [&](const LaunchEvents& ev) { return launch_append(d.kv_dtype, a, stream, ev); },
+      "append launch");
 }
 
 bool use_mfma(const pkv_pool* p) {
@@ -336,8 +345,14 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.n_branch = S.n_branch;
   a.P = S.P;
   a.scale_log2 = scale * 1.4426950408889634f;
+  // P enters P.V as bf16 plus its bf16 rounding residual: with P alone in
+  // bf16 a row whose weight sits on a few keys is off by up to 2^-9 |v|
+  const bool lo_split = true;
   rc = p->timed(
-      T_ATTN, stream, [&] { return launch_attn(mfma, d.kv_dtype, d.head_dim, d.block_size, a, stream); },
+      T_ATTN,
+      [&](const LaunchEvents& ev) {
+        return launch_attn(mfma, lo_split, d.kv_dtype, d.head_dim, d.block_size, a, stream, ev);
+      },
       "attention launch");
   if (rc) return rc;
   CombineParams c;
@@ -352,8 +367,13 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   c.G = a.G;
   c.Hq = a.Hq;
   c.P = S.P;
-  return p->timed(T_COMBINE, stream, [&] { return launch_combine(d.head_dim, c, stream); },
-                  "combine launch");
+  int32_t max_entries = 0;
+  for (int32_t b = 0; b < S.n_branch; ++b)
+    max_entries = std::max(max_entries, S.comb_ptr[b + 1] - S.comb_ptr[b]);
+  return p->timed(
+      T_COMBINE,
+      [&](const LaunchEvents& ev) { return launch_combine(d.head_dim, max_entries, c, stream, ev); },
+      "combine launch");
 }
 
 }  // namespace
@@ -448,12 +468,14 @@ int pkv_cow_copy(pkv_pool* pool, const pkv_cow_op* ops, int32_t n, void* stream)
   const pkv_pool_desc& d = pool->pool.desc();
   if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
   if (n < 0 || (n > 0 && !ops)) return fail(PKV_E_INVALID, "cow_copy: bad op list");
-  std::vector<pkv_cow_op> v(ops, ops + n);
-  for (const pkv_cow_op& o : v)
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_cow_op& o = ops[i];
     if (o.src < 0 || o.src >= d.num_blocks || o.dst < 0 || o.dst >= d.num_blocks || o.n_valid < 0 ||
         o.n_valid > d.block_size)
       return fail(PKV_E_INVALID, "cow_copy: op out of range");
-  return enqueue_cow(pool, v, (hipStream_t)stream);
+  }
+  if ((int64_t)n * d.num_layers > INT32_MAX) return fail(PKV_E_INVALID, "cow_copy: too many ops");
+  return enqueue_append(pool, ops, n, nullptr, 0, nullptr, nullptr, (hipStream_t)stream);
   PKV_GUARD_END
 }
 
@@ -467,7 +489,7 @@ int pkv_write_kv(pkv_pool* pool, const int64_t* slots, int32_t n, const void* k_
   const int64_t max_slot = (int64_t)d.num_blocks * d.block_size;
   for (int32_t i = 0; i < n; ++i)
     if (slots[i] < 0 || slots[i] >= max_slot) return fail(PKV_E_INVALID, "write_kv: slot out of range");
-  return enqueue_write(pool, slots, n, k_new, v_new, (hipStream_t)stream);
+  return enqueue_append(pool, nullptr, 0, slots, n, k_new, v_new, (hipStream_t)stream);
   PKV_GUARD_END
 }
 
@@ -488,10 +510,8 @@ int pkv_append_kv_batch(pkv_pool* pool, const pkv_seq* seqs, const int32_t* coun
   if (rc) return rc;
   // The tables are updated; a device failure below leaves them updated
   // (the error is PKV_E_HIP, after which the device state is unknown).
-  hipStream_t s = (hipStream_t)stream;
-  rc = enqueue_cow(pool, cows, s);
-  if (rc) return rc;
-  return enqueue_write(pool, slots.data(), (int32_t)slots.size(), k_new, v_new, s);
+  return enqueue_append(pool, cows.data(), (int32_t)cows.size(), slots.data(),
+                        (int32_t)slots.size(), k_new, v_new, (hipStream_t)stream);
   PKV_GUARD_END
 }
 
@@ -651,11 +671,7 @@ int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_
   PKV_GUARD_BEGIN
   if (!pool_ok(pool) || !kernel || !total_ms || !launches) return fail(PKV_E_INVALID, "null argument");
   const std::string k(kernel);
-  int kind = k == "attention" ? T_ATTN
-             : k == "combine" ? T_COMBINE
-             : k == "cow_copy" ? T_COW
-             : k == "kv_write" ? T_WRITE
-                               : -1;
+  int kind = k == "attention" ? T_ATTN : k == "combine" ? T_COMBINE : k == "append" ? T_APPEND : -1;
   if (kind < 0) return fail(PKV_E_INVALID, "unknown kernel " + k);
   return pool->timers[kind].read(total_ms, launches);
   PKV_GUARD_END

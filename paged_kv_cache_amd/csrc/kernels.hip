@@ -1,7 +1,7 @@
 // Device kernels of the paged KV cache, written for gfx950 (MI355X, wave64).
 //
-//   kv_write_kernel    scatter appended tokens' K/V into their slots
-//   cow_copy_kernel    copy the valid slots of a shared tail block on write
+//   append_kernel      copy-on-write copies and the scatter of appended
+//                      tokens' K/V into their slots, in one launch
 //   attn_mfma_kernel   paged attention over shared tiles on the matrix cores
 //                      (bf16 K/V and q, fp32 softmax and accumulation); with a
 //                      draft-tree mask it is the verify kernel
@@ -11,6 +11,7 @@
 //
 // Layout: K tiles [BS][D] (token-major), V tiles [D][BS] (token index
 // fastest). See include/pkv.h.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -35,6 +36,41 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 row-swap permutes. v_permlane16_swap exchanges the
+// odd rows of its first register with the even rows of its second, and
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second; starting from two copies of x, each lane then holds its own and
+// its partner's value in the two registers. Written as one asm statement
+// with both registers as in/out operands, preceded by the two wait states
+// the permute needs after the VALU write of its operands.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  return a + b;
+}
+
 template <typename T>
 __device__ __forceinline__ float to_f32(T v);
 template <>
@@ -46,59 +82,59 @@ __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
   return bf16_bits_to_f32(v);
 }
 
-// ------------------------------------------------------------- kv_write
+// ------------------------------------------------------------- append
+//
+// One launch performs an append's copy-on-write copies and its token writes.
+// Workgroups [0, n_ops * L) copy: one (op, layer) each, all KV heads,
+// slots [0, n_valid) of the source tile into the destination tile. The rest
+// write: one (layer, token) each, all KV heads. A copy fills slots below
+// n_valid of a fresh block and the writes land at or above it (or in other
+// blocks), and a copy's source is shared, so no write touches it: the two
+// parts never overlap and need no ordering.
 
 template <typename T>
-__global__ __launch_bounds__(256) void kv_write_kernel(const T* __restrict__ k_new,
-                                                       const T* __restrict__ v_new, T* k_arena,
-                                                       T* v_arena, const int64_t* __restrict__ slots,
-                                                       int n, int L, int NB, int Hkv, int D,
-                                                       int BS) {
-  const int64_t total = (int64_t)L * n * Hkv * D;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    int64_t r = idx;
-    const int d = (int)(r % D);
-    r /= D;
-    const int h = (int)(r % Hkv);
-    r /= Hkv;
-    const int i = (int)(r % n);
-    const int l = (int)(r / n);
-    const int64_t slot = slots[i];
-    const int64_t blk = slot / BS;
-    const int off = (int)(slot - blk * BS);
-    const int64_t tile = ((int64_t)l * NB + blk) * Hkv + h;
-    k_arena[(tile * BS + off) * D + d] = k_new[idx];
-    v_arena[(tile * D + d) * BS + off] = v_new[idx];
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int n_copy = p.n_ops * p.L;
+  const int64_t tile = (int64_t)p.BS * p.D;
+  T* K = (T*)p.k_arena;
+  T* V = (T*)p.v_arena;
+  if ((int)blockIdx.x < n_copy) {
+    const int o = blockIdx.x / p.L;
+    const int l = blockIdx.x - o * p.L;
+    const int* op = p.ops ? p.ops + 3 * o : p.inl_ops + 3 * o;
+    const int src = op[0], dst = op[1], nv = op[2];
+    const int64_t s0 = ((int64_t)l * p.NB + src) * p.Hkv;
+    const int64_t d0 = ((int64_t)l * p.NB + dst) * p.Hkv;
+    // K: per head, the first nv token rows are one contiguous run of
+    // nv * D * sizeof(T) bytes, a whole number of 16-byte vectors
+    const int vec_per_head = (int)((int64_t)nv * p.D * sizeof(T) / 16);
+    for (int i = threadIdx.x; i < vec_per_head * p.Hkv; i += blockDim.x) {
+      const int h = i / vec_per_head, v = i - h * vec_per_head;
+      const u32x4* ks = (const u32x4*)(K + (s0 + h) * tile);
+      u32x4* kd = (u32x4*)(K + (d0 + h) * tile);
+      kd[v] = ks[v];
+    }
+    // V: nv leading entries of each of the Hkv * D rows
+    const int per_head = nv * p.D;
+    for (int i = threadIdx.x; i < per_head * p.Hkv; i += blockDim.x) {
+      const int h = i / per_head, r = i - h * per_head;
+      const int d = r / nv, t = r - d * nv;
+      V[(d0 + h) * tile + d * p.BS + t] = V[(s0 + h) * tile + d * p.BS + t];
+    }
+    return;
   }
-}
-
-// ------------------------------------------------------------- cow_copy
-
-// One workgroup per (op, layer, KV head): copies slots [0, n_valid) of the
-// source tile into the destination tile, K and V.
-template <typename T>
-__global__ __launch_bounds__(256) void cow_copy_kernel(T* k_arena, T* v_arena,
-                                                       const int32_t* __restrict__ ops, int L,
-                                                       int NB, int Hkv, int D, int BS) {
-  const int per_op = L * Hkv;
-  const int o = blockIdx.x / per_op;
-  const int rem = blockIdx.x - o * per_op;
-  const int l = rem / Hkv, h = rem - (rem / Hkv) * Hkv;
-  const int src = ops[3 * o], dst = ops[3 * o + 1], nv = ops[3 * o + 2];
-  const int64_t st = ((int64_t)l * NB + src) * Hkv + h;
-  const int64_t dt = ((int64_t)l * NB + dst) * Hkv + h;
-  const int64_t tile = (int64_t)BS * D;
-  // K: the first nv token rows are one contiguous run
-  const T* ks = k_arena + st * tile;
-  T* kd = k_arena + dt * tile;
-  for (int i = threadIdx.x; i < nv * D; i += blockDim.x) kd[i] = ks[i];
-  // V: nv leading entries of each of the D rows
-  const T* vs = v_arena + st * tile;
-  T* vd = v_arena + dt * tile;
-  for (int i = threadIdx.x; i < nv * D; i += blockDim.x) {
-    const int d = i / nv, t = i - (i / nv) * nv;
-    vd[d * BS + t] = vs[d * BS + t];
+  const int w = blockIdx.x - n_copy;  // (layer, token)
+  const int l = w / p.n_slots, i = w - l * p.n_slots;
+  const int64_t slot = p.slots ? p.slots[i] : p.inl_slots[i];
+  const int64_t b = slot / p.BS;
+  const int off = (int)(slot - b * p.BS);
+  const int64_t t0 = ((int64_t)l * p.NB + b) * p.Hkv;
+  const T* kn = (const T*)p.k_new + ((int64_t)l * p.n_slots + i) * p.Hkv * p.D;
+  const T* vn = (const T*)p.v_new + ((int64_t)l * p.n_slots + i) * p.Hkv * p.D;
+  for (int e = threadIdx.x; e < p.Hkv * p.D; e += blockDim.x) {
+    const int h = e / p.D, d = e - h * p.D;
+    K[((t0 + h) * p.BS + off) * p.D + d] = kn[e];
+    V[((t0 + h) * p.D + d) * p.BS + off] = vn[e];
   }
 }
 
@@ -124,7 +160,7 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int BS>
+template <int D, int BS, bool LO>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   constexpr int KS = D / 32;  // 32-wide k steps of Q.K
   constexpr int DB = D / 16;  // 16-wide d blocks of P.V
@@ -134,7 +170,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   __shared__ float mrg_l[3][16];
   __shared__ float mrg_acc[3][16 * ACC_STRIDE];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int per_item = p.n_layers * p.Hkv;
   const int item_idx = blockIdx.x / per_item;
@@ -176,36 +213,57 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int64_t layer_tiles = (int64_t)layer * p.num_blocks * p.Hkv;
   const int32_t* blk = p.blk + it.blk_off;
 
+  // this lane's token offsets inside a 32-token step: K tile rows and V
+  // columns; with 16-token blocks a step spans two blocks (A, B)
+  const int koff0 = 8 * (n >> 2) + (n & 3);  // tile 0; tile 1 is +4
+  const bool k_in_b = BS == 16 && koff0 >= 16;
+  const int voff = 8 * g;
+  const bool v_in_b = BS == 16 && voff >= 16;
+
   f32x4 acc[DB];
 #pragma unroll
   for (int j = 0; j < DB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
   const int n_steps = (it.n_tok + 31) >> 5;
 
-  if (active) {
+  if (active && phase < n_steps) {
+    // block ids are wave-uniform (scalar loads), fetched one step ahead
+    int bA = blk[(32 * phase) / BS];
+    int bB = blk[(32 * phase + 16) / BS];
     for (int s = phase; s < n_steps; s += phases) {
       const int tbase = s * 32;
-      // scores: two S^T tiles of 16 tokens
-      f32x4 st[2];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        const int tk = tbase + 8 * (n >> 2) + 4 * tau + (n & 3);
-        const int b = blk[tk / BS];
-        const uint16_t* kp = K + ((layer_tiles + (int64_t)b * p.Hkv + kvh) * BS + (tk % BS)) * D + 8 * g;
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) c = mfma_bf16(as_bf16x8(ld16(kp + 32 * ks)), qv[ks], c);
-        st[tau] = c;
+      const int cA = bA, cB = bB;
+      if (s + phases < n_steps) {
+        bA = blk[(32 * (s + phases)) / BS];
+        bB = blk[(32 * (s + phases) + 16) / BS];
       }
-      // V^T operands: 8 tokens (8g .. 8g+7 of the step) of d = 16 j + n
-      const int tv = tbase + 8 * g;
-      const int bv = blk[tv / BS];
-      const uint16_t* vp = V + ((layer_tiles + (int64_t)bv * p.Hkv + kvh) * D + n) * BS + (tv % BS);
+      // K rows of this lane (both S^T tiles) and V^T columns
+      const int kb = k_in_b ? cB : cA;
+      const int kslot = (tbase + koff0) % BS;
+      const uint16_t* kp = K + ((layer_tiles + (int64_t)kb * p.Hkv + kvh) * BS + kslot) * D + 8 * g;
+      const int vb = v_in_b ? cB : cA;
+      const uint16_t* vp =
+          V + ((layer_tiles + (int64_t)vb * p.Hkv + kvh) * D + n) * BS + (tbase + voff) % BS;
+      u32x4 kraw[2][KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kraw[0][ks] = ld16(kp + 32 * ks);
+        kraw[1][ks] = ld16(kp + 4 * D + 32 * ks);
+      }
       u32x4 vraw[DB];
 #pragma unroll
       for (int j = 0; j < DB; ++j) vraw[j] = ld16(vp + (int64_t)16 * j * BS);
+      f32x4 st[2];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) c = mfma_bf16(as_bf16x8(kraw[tau][ks]), qv[ks], c);
+        st[tau] = c;
+      }
 
       const bool tail = tbase + 32 > it.n_tok;
+      const int tv = tbase + voff;
       float sc[8];
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
@@ -238,8 +296,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       float mx = sc[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
@@ -251,7 +308,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         psum += pe;
         const __bf16 h = (__bf16)pe;
         phi[e] = h;
-        plo[e] = (__bf16)(pe - (float)h);
+        if (LO) plo[e] = (__bf16)(pe - (float)h);
       }
       l_run = l_run * alpha + psum;
       m_run = m_new;
@@ -259,13 +316,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       for (int j = 0; j < DB; ++j) {
         acc[j] *= alpha;
         acc[j] = mfma_bf16(as_bf16x8(vraw[j]), phi, acc[j]);
-        acc[j] = mfma_bf16(as_bf16x8(vraw[j]), plo, acc[j]);
+        if (LO) acc[j] = mfma_bf16(as_bf16x8(vraw[j]), plo, acc[j]);
       }
     }
   }
   // the four lane groups hold disjoint tokens of the same rows
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_xor32(sum_xor16(l_run));
+  float l_fin = l_tot;
 
   if (phases > 1) {
     if (phase > 0 && active) {
@@ -286,7 +343,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         const float M = fmaxf(m_run, mo);
         if (M != kNegInf) {
           const float a = fast_exp2(m_run - M), b = fast_exp2(mo - M);
-          l_tot = l_tot * a + lo * b;
+          l_fin = l_fin * a + lo * b;
 #pragma unroll
           for (int j = 0; j < DB; ++j) {
             const f32x4 o = *(const f32x4*)&mrg_acc[slot][n * ACC_STRIDE + 16 * j + 4 * g];
@@ -301,7 +358,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     const int64_t prow = (int64_t)(li * p.Hkv + kvh) * p.P + it.part_row + row;
     if (g == 0) {
       p.part_ml[2 * prow] = m_run;
-      p.part_ml[2 * prow + 1] = l_tot;
+      p.part_ml[2 * prow + 1] = l_fin;
     }
     float* pa = p.part_acc + prow * D;
 #pragma unroll
@@ -495,67 +552,91 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 
 // ------------------------------------------------------------- combine
 //
-// One workgroup per (layer, branch, KV head): for each of the G query heads
-// and each d, merge the branch's partial states in logical order:
-//   M = max m_i, L = sum l_i 2^(m_i - M), out = sum acc_i 2^(m_i - M) / L.
+// Merges each output row's partial states (one per chunk on its path) in
+// logical order: M = max m_i, L = sum l_i 2^(m_i - M),
+// out = sum acc_i 2^(m_i - M) / L. Lane j owns d = j*VW .. j*VW + VW-1.
+// WPR = 1: a wave per output row, four rows per workgroup (short lists).
+// WPR = 4: the four waves of a workgroup split one row's list (long lists:
+// split-K over a long context) and merge through LDS.
 
-template <int D>
+template <int D, int WPR>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  const int per = p.n_branch * p.Hkv;
-  const int li = blockIdx.x / per;
-  const int rem = blockIdx.x - li * per;
-  const int b = rem / p.Hkv;
-  const int kvh = rem - b * p.Hkv;
-  const int e0 = p.comb_ptr[b], e1 = p.comb_ptr[b + 1];
-  const int64_t plane = (int64_t)(li * p.Hkv + kvh) * p.P;
-  for (int idx = threadIdx.x; idx < p.G * D; idx += blockDim.x) {
-    const int gq = idx / D, d = idx - (idx / D) * D;
-    float M = kNegInf;
-    for (int e = e0; e < e1; ++e) M = fmaxf(M, p.part_ml[2 * (plane + p.comb_rows[e] + gq)]);
-    float L = 0.f, O = 0.f;
-    for (int e = e0; e < e1; ++e) {
-      const int64_t row = plane + p.comb_rows[e] + gq;
-      const float mi = p.part_ml[2 * row];
-      if (mi == kNegInf) continue;
-      const float w = fast_exp2(mi - M);
-      L += p.part_ml[2 * row + 1] * w;
-      O += p.part_acc[row * D + d] * w;
-    }
-    p.out[(((int64_t)li * p.n_branch + b) * p.Hq + kvh * p.G + gq) * D + d] = O / L;
+  constexpr int VW = D / 64;
+  typedef float vec_t __attribute__((ext_vector_type(VW)));
+  __shared__ float red_m[4];
+  __shared__ float red_l[4];
+  __shared__ vec_t red_acc[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n_out = (int64_t)p.n_layers * p.n_branch * p.Hq;
+  const int64_t orow = WPR == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
+  const bool valid = orow < n_out;
+  const int64_t per_layer = (int64_t)p.n_branch * p.Hq;
+  const int li = valid ? (int)(orow / per_layer) : 0;
+  const int rem = valid ? (int)(orow - li * per_layer) : 0;
+  const int b = rem / p.Hq, h = rem - (rem / p.Hq) * p.Hq;
+  const int kvh = h / p.G, gq = h - (h / p.G) * p.G;
+  const int e0 = valid ? p.comb_ptr[b] : 0;
+  const int e1 = valid ? p.comb_ptr[b + 1] : 0;
+  const int64_t plane = (int64_t)(li * p.Hkv + kvh) * p.P + gq;
+  const int sub = WPR == 1 ? 0 : wave;
+
+  float M = kNegInf;
+  for (int e = e0 + sub; e < e1; e += WPR) M = fmaxf(M, p.part_ml[2 * (plane + p.comb_rows[e])]);
+  if (WPR > 1) {
+    if (lane == 0) red_m[wave] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   }
+  float L = 0.f;
+  vec_t acc = {};
+#pragma unroll 4
+  for (int e = e0 + sub; e < e1; e += WPR) {
+    const int64_t row = plane + p.comb_rows[e];
+    const float mi = p.part_ml[2 * row];
+    const float w = mi == kNegInf ? 0.f : fast_exp2(mi - M);
+    L += p.part_ml[2 * row + 1] * w;
+    const vec_t a = *(const vec_t*)(p.part_acc + row * D + lane * VW);
+    acc += a * w;
+  }
+  if (WPR > 1) {
+    if (lane == 0) red_l[wave] = L;
+    red_acc[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    L = red_l[0] + red_l[1] + red_l[2] + red_l[3];
+    acc = red_acc[0][lane] + red_acc[1][lane] + red_acc[2][lane] + red_acc[3][lane];
+  }
+  if (!valid) return;
+  *(vec_t*)(p.out + orow * D + lane * VW) = acc / L;
 }
 
 // ------------------------------------------------------------- launchers
 
-hipError_t launch_kv_write(int dtype, const void* k_new, const void* v_new, void* k_arena,
-                           void* v_arena, const int64_t* d_slots, int n, int L, int NB, int Hkv,
-                           int D, int BS, hipStream_t stream) {
-  const int64_t total = (int64_t)L * n * Hkv * D;
-  if (total == 0) return hipSuccess;
-  const int64_t want = (total + 255) / 256;
-  const int grid = (int)(want < 65536 ? want : 65536);
-  if (dtype == 0)
-    kv_write_kernel<float><<<grid, 256, 0, stream>>>((const float*)k_new, (const float*)v_new,
-                                                     (float*)k_arena, (float*)v_arena, d_slots, n,
-                                                     L, NB, Hkv, D, BS);
+namespace {
+
+// Launches a kernel; with timing events, through the HIP extension that
+// records them when the kernel itself starts and ends.
+template <typename... KArgs, typename... Args>
+hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                  const LaunchEvents& ev, Args... args) {
+  if (ev.start)
+    hipExtLaunchKernelGGL(kern, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
   else
-    kv_write_kernel<uint16_t><<<grid, 256, 0, stream>>>(
-        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_arena, (uint16_t*)v_arena,
-        d_slots, n, L, NB, Hkv, D, BS);
+    kern<<<grid, block, 0, stream>>>(args...);
   return hipGetLastError();
 }
 
-hipError_t launch_cow_copy(int dtype, void* k_arena, void* v_arena, const int32_t* d_ops,
-                           int n_ops, int L, int NB, int Hkv, int D, int BS, hipStream_t stream) {
-  if (n_ops == 0) return hipSuccess;
-  const int grid = n_ops * L * Hkv;
-  if (dtype == 0)
-    cow_copy_kernel<float><<<grid, 256, 0, stream>>>((float*)k_arena, (float*)v_arena, d_ops, L,
-                                                     NB, Hkv, D, BS);
-  else
-    cow_copy_kernel<uint16_t><<<grid, 256, 0, stream>>>((uint16_t*)k_arena, (uint16_t*)v_arena,
-                                                        d_ops, L, NB, Hkv, D, BS);
-  return hipGetLastError();
+}  // namespace
+
+hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t stream,
+                         const LaunchEvents& ev) {
+  const int64_t g64 = (int64_t)p.n_ops * p.L + (int64_t)p.n_slots * p.L;
+  if (g64 == 0) return hipSuccess;
+  if (g64 > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)g64);
+  if (dtype == 0) return launch(append_kernel<float>, grid, dim3(256), stream, ev, p);
+  return launch(append_kernel<uint16_t>, grid, dim3(256), stream, ev, p);
 }
 
 bool attn_supported(bool mfma, int dtype, int D, int BS) {
@@ -565,70 +646,68 @@ bool attn_supported(bool mfma, int dtype, int D, int BS) {
   return dtype == 0 || dtype == 1;
 }
 
-#define PKV_DISPATCH_BS(KERNEL_T, ...)                                        \
-  switch (BS) {                                                               \
-    case 16: KERNEL_T(16)<<<grid, 256, 0, stream>>>(__VA_ARGS__); break;      \
-    case 32: KERNEL_T(32)<<<grid, 256, 0, stream>>>(__VA_ARGS__); break;      \
-    default: KERNEL_T(64)<<<grid, 256, 0, stream>>>(__VA_ARGS__); break;      \
-  }
+namespace {
 
-hipError_t launch_attn(bool mfma, int dtype, int D, int BS, const AttnParams& p,
-                       hipStream_t stream) {
+template <int D, bool LO>
+hipError_t launch_mfma_d(int BS, const AttnParams& p, dim3 grid, hipStream_t s, const LaunchEvents& ev) {
+  switch (BS) {
+    case 16: return launch(attn_mfma_kernel<D, 16, LO>, grid, dim3(256), s, ev, p);
+    case 32: return launch(attn_mfma_kernel<D, 32, LO>, grid, dim3(256), s, ev, p);
+    default: return launch(attn_mfma_kernel<D, 64, LO>, grid, dim3(256), s, ev, p);
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_valu_d(int BS, const AttnParams& p, dim3 grid, hipStream_t s, const LaunchEvents& ev) {
+  switch (BS) {
+    case 16: return launch(attn_valu_kernel<T, D, 16>, grid, dim3(256), s, ev, p);
+    case 32: return launch(attn_valu_kernel<T, D, 32>, grid, dim3(256), s, ev, p);
+    default: return launch(attn_valu_kernel<T, D, 64>, grid, dim3(256), s, ev, p);
+  }
+}
+
+template <typename T>
+hipError_t launch_valu(int D, int BS, const AttnParams& p, dim3 grid, hipStream_t s,
+                       const LaunchEvents& ev) {
+  if (D == 64) return launch_valu_d<T, 64>(BS, p, grid, s, ev);
+  if (D == 128) return launch_valu_d<T, 128>(BS, p, grid, s, ev);
+  return launch_valu_d<T, 256>(BS, p, grid, s, ev);
+}
+
+}  // namespace
+
+hipError_t launch_attn(bool mfma, bool lo_split, int dtype, int D, int BS, const AttnParams& p,
+                       hipStream_t stream, const LaunchEvents& ev) {
   if (!attn_supported(mfma, dtype, D, BS)) return hipErrorInvalidValue;
   const int64_t g64 = (int64_t)p.n_items * p.n_layers * p.Hkv;
   if (g64 == 0) return hipSuccess;
   if (g64 > 0x7fffffff) return hipErrorInvalidValue;
-  const int grid = (int)g64;
+  const dim3 grid((unsigned)g64);
   if (mfma) {
-#define K_MFMA_64(bs) attn_mfma_kernel<64, bs>
-#define K_MFMA_128(bs) attn_mfma_kernel<128, bs>
-#define K_MFMA_256(bs) attn_mfma_kernel<256, bs>
-    if (D == 64) {
-      PKV_DISPATCH_BS(K_MFMA_64, p)
-    } else if (D == 128) {
-      PKV_DISPATCH_BS(K_MFMA_128, p)
-    } else {
-      PKV_DISPATCH_BS(K_MFMA_256, p)
-    }
-  } else if (dtype == 0) {
-#define K_VF_64(bs) attn_valu_kernel<float, 64, bs>
-#define K_VF_128(bs) attn_valu_kernel<float, 128, bs>
-#define K_VF_256(bs) attn_valu_kernel<float, 256, bs>
-    if (D == 64) {
-      PKV_DISPATCH_BS(K_VF_64, p)
-    } else if (D == 128) {
-      PKV_DISPATCH_BS(K_VF_128, p)
-    } else {
-      PKV_DISPATCH_BS(K_VF_256, p)
-    }
-  } else {
-#define K_VB_64(bs) attn_valu_kernel<uint16_t, 64, bs>
-#define K_VB_128(bs) attn_valu_kernel<uint16_t, 128, bs>
-#define K_VB_256(bs) attn_valu_kernel<uint16_t, 256, bs>
-    if (D == 64) {
-      PKV_DISPATCH_BS(K_VB_64, p)
-    } else if (D == 128) {
-      PKV_DISPATCH_BS(K_VB_128, p)
-    } else {
-      PKV_DISPATCH_BS(K_VB_256, p)
-    }
+    if (!lo_split) return hipErrorInvalidValue;  // only the split form is built
+    if (D == 64) return launch_mfma_d<64, true>(BS, p, grid, stream, ev);
+    if (D == 128) return launch_mfma_d<128, true>(BS, p, grid, stream, ev);
+    return launch_mfma_d<256, true>(BS, p, grid, stream, ev);
   }
-  return hipGetLastError();
+  if (dtype == 0) return launch_valu<float>(D, BS, p, grid, stream, ev);
+  return launch_valu<uint16_t>(D, BS, p, grid, stream, ev);
 }
 
-hipError_t launch_combine(int D, const CombineParams& p, hipStream_t stream) {
-  const int64_t g64 = (int64_t)p.n_layers * p.n_branch * p.Hkv;
-  if (g64 == 0) return hipSuccess;
-  const int grid = (int)g64;
-  if (D == 64)
-    combine_kernel<64><<<grid, 256, 0, stream>>>(p);
-  else if (D == 128)
-    combine_kernel<128><<<grid, 256, 0, stream>>>(p);
-  else if (D == 256)
-    combine_kernel<256><<<grid, 256, 0, stream>>>(p);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+hipError_t launch_combine(int D, int max_entries, const CombineParams& p, hipStream_t stream,
+                          const LaunchEvents& ev) {
+  const int64_t n_out = (int64_t)p.n_layers * p.n_branch * p.Hq;
+  if (n_out == 0) return hipSuccess;
+  const bool wide = max_entries >= 8;
+  const int64_t g64 = wide ? n_out : (n_out + 3) / 4;
+  if (g64 > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)g64);
+  if (D == 64) return wide ? launch(combine_kernel<64, 4>, grid, dim3(256), stream, ev, p)
+                           : launch(combine_kernel<64, 1>, grid, dim3(256), stream, ev, p);
+  if (D == 128) return wide ? launch(combine_kernel<128, 4>, grid, dim3(256), stream, ev, p)
+                            : launch(combine_kernel<128, 1>, grid, dim3(256), stream, ev, p);
+  if (D == 256) return wide ? launch(combine_kernel<256, 4>, grid, dim3(256), stream, ev, p)
+                            : launch(combine_kernel<256, 1>, grid, dim3(256), stream, ev, p);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace pkv
