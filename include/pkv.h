@@ -129,6 +129,13 @@ int pkv_seq_fork(pkv_pool* pool, pkv_seq parent, pkv_seq* child);
  * become free) and invalidate the handle. */
 int pkv_seq_free(pkv_pool* pool, pkv_seq seq);
 
+/* n forks in one call: children[i] = fork of parents[i] (host arrays).
+ * All or nothing: on error no child exists. */
+int pkv_seq_fork_many(pkv_pool* pool, const pkv_seq* parents, int32_t n, pkv_seq* children);
+/* n frees in one call (host array); all handles are checked first, and a
+ * handle listed twice is PKV_E_INVALID; on error nothing is freed. */
+int pkv_seq_free_many(pkv_pool* pool, const pkv_seq* seqs, int32_t n);
+
 /* Plan an append of n >= 0 tokens to seq [D1, D2], all or nothing:
  *  1. if the last block is partly filled and shared (count > 1), take a
  *     fresh block, record the copy {last, fresh, len % block_size}, drop one
@@ -145,7 +152,9 @@ int pkv_seq_append_plan(pkv_pool* pool, pkv_seq seq, int32_t n, int64_t* slots_o
                         pkv_cow_op* cow_out, int32_t* n_cow);
 
 /* Device: perform copy-on-write copies (host array of n ops) for every
- * layer and KV head, K and V, on the stream. */
+ * layer and KV head, K and V, on the stream. Slots at and above n_valid of
+ * each destination block hold unspecified values afterwards. block_size
+ * must be 16, 32 or 64 for every device call (else PKV_E_UNSUPPORTED). */
 int pkv_cow_copy(pkv_pool* pool, const pkv_cow_op* ops, int32_t n, void* stream);
 
 /* Device: scatter n tokens of new K/V into their slots. slots: host array of

@@ -73,6 +73,8 @@ _PROTOS = {
     "pkv_seq_create": [c_void_p, POINTER(PkvSeq)],
     "pkv_seq_fork": [c_void_p, PkvSeq, POINTER(PkvSeq)],
     "pkv_seq_free": [c_void_p, PkvSeq],
+    "pkv_seq_fork_many": [c_void_p, POINTER(PkvSeq), c_int32, POINTER(PkvSeq)],
+    "pkv_seq_free_many": [c_void_p, POINTER(PkvSeq), c_int32],
     "pkv_seq_append_plan": [c_void_p, PkvSeq, c_int32, POINTER(c_int64), POINTER(PkvCowOp),
                             POINTER(c_int32)],
     "pkv_cow_copy": [c_void_p, POINTER(PkvCowOp), c_int32, c_void_p],

@@ -108,6 +108,16 @@ def pkv_seq_free(pool, seq: PkvSeq) -> None:
     check(lib.pkv_seq_free(pool, seq))
 
 
+def pkv_seq_fork_many(pool, parents: Sequence[PkvSeq]) -> List[PkvSeq]:
+    kids = (PkvSeq * max(len(parents), 1))()
+    check(lib.pkv_seq_fork_many(pool, _seq_array(parents), len(parents), kids))
+    return list(kids[:len(parents)])
+
+
+def pkv_seq_free_many(pool, seqs: Sequence[PkvSeq]) -> None:
+    check(lib.pkv_seq_free_many(pool, _seq_array(seqs), len(seqs)))
+
+
 def pkv_seq_append_plan(pool, seq: PkvSeq, n: int) -> Tuple[List[int], List[Tuple[int, int, int]]]:
     slots = (c_int64 * max(n, 1))()
     cow = PkvCowOp()
@@ -266,6 +276,12 @@ class PagedKVCache:
 
     def free(self, seq: PkvSeq) -> None:
         pkv_seq_free(self.handle, seq)
+
+    def fork_many(self, parents: Sequence[PkvSeq]) -> List[PkvSeq]:
+        return pkv_seq_fork_many(self.handle, parents)
+
+    def free_many(self, seqs: Sequence[PkvSeq]) -> None:
+        pkv_seq_free_many(self.handle, seqs)
 
     def plan(self, seq: PkvSeq, n: int):
         return pkv_seq_append_plan(self.handle, seq, n)

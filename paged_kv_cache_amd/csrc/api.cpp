@@ -212,50 +212,87 @@ size_t elem_size(const pkv_pool_desc& d) { return d.kv_dtype == PKV_F32 ? 4 : 2;
 
 bool has_arenas(const pkv_pool_desc& d) { return d.k_arena && d.v_arena; }
 
-// Copy-on-write copies and token writes of one append, in one launch. Short
-// lists travel in the kernel arguments; longer ones are staged to the
+// Copy-on-write copies and token writes of one append, in one launch. The
+// tokens that land in a copy's destination block go with the copy (the
+// copy workgroup assembles that block); the rest form the write list.
+// Short lists travel in the kernel arguments; longer ones are staged to the
 // pool's device metadata buffer in one upload.
 int enqueue_append(pkv_pool* p, const pkv_cow_op* ops, int32_t n_ops, const int64_t* slots,
-                   int32_t n_slots, const void* k_new, const void* v_new, hipStream_t stream) {
-  if (n_ops == 0 && n_slots == 0) return PKV_OK;
+                   int32_t n_tok, const void* k_new, const void* v_new, hipStream_t stream) {
+  if (n_ops == 0 && n_tok == 0) return PKV_OK;
   const pkv_pool_desc& d = p->pool.desc();
+  if (!append_supported(d.block_size))
+    return fail(PKV_E_UNSUPPORTED, "device append: block_size must be 16, 32 or 64");
+  const int64_t bs = d.block_size;
+  // per op: src, dst, n_valid, tok0, m
+  std::vector<int32_t> op5((size_t)n_ops * 5);
+  for (int32_t o = 0; o < n_ops; ++o) {
+    op5[5 * o] = ops[o].src;
+    op5[5 * o + 1] = ops[o].dst;
+    op5[5 * o + 2] = ops[o].n_valid;
+    op5[5 * o + 3] = 0;
+    op5[5 * o + 4] = 0;
+  }
+  std::vector<int64_t> wslot;
+  std::vector<int32_t> wtok;
+  wslot.reserve(n_tok);
+  wtok.reserve(n_tok);
+  for (int32_t t = 0; t < n_tok; ++t) {
+    const int64_t b = slots[t] / bs;
+    int32_t hit = -1;
+    for (int32_t o = 0; o < n_ops; ++o)
+      if (ops[o].dst == b) {
+        hit = o;
+        break;
+      }
+    if (hit >= 0) {
+      int32_t* q = &op5[5 * hit];
+      if (q[4] == 0) q[3] = t;
+      if (t != q[3] + q[4] || slots[t] != b * bs + q[2] + q[4])
+        return fail(PKV_E_INVALID, "append: tokens in a copied block must follow its valid slots");
+      ++q[4];
+    } else {
+      wslot.push_back(slots[t]);
+      wtok.push_back(t);
+    }
+  }
   AppendParams a{};
   a.k_new = k_new;
   a.v_new = v_new;
   a.k_arena = d.k_arena;
   a.v_arena = d.v_arena;
   a.n_ops = n_ops;
-  a.n_slots = n_slots;
+  a.n_write = (int32_t)wslot.size();
+  a.n_tok = n_tok;
   a.L = d.num_layers;
   a.NB = d.num_blocks;
   a.Hkv = d.num_kv_heads;
   a.D = d.head_dim;
   a.BS = d.block_size;
-  if (n_ops <= kInlineOps && n_slots <= kInlineSlots) {
-    for (int32_t i = 0; i < n_ops; ++i) {
-      a.inl_ops[3 * i] = ops[i].src;
-      a.inl_ops[3 * i + 1] = ops[i].dst;
-      a.inl_ops[3 * i + 2] = ops[i].n_valid;
+  if (n_ops <= kInlineOps && a.n_write <= kInlineSlots) {
+    std::memcpy(a.inl_ops, op5.data(), op5.size() * sizeof(int32_t));
+    for (int32_t i = 0; i < a.n_write; ++i) {
+      a.inl_slots[i] = wslot[i];
+      a.inl_tok[i] = wtok[i];
     }
-    for (int32_t i = 0; i < n_slots; ++i) a.inl_slots[i] = slots[i];
   } else {
-    const size_t slot_bytes = (size_t)n_slots * sizeof(int64_t);
-    const size_t op_off = (slot_bytes + 255) & ~size_t(255);
-    const size_t bytes = op_off + (size_t)n_ops * 3 * sizeof(int32_t);
+    const size_t b_slots = (size_t)a.n_write * sizeof(int64_t);
+    const size_t o_tok = (b_slots + 255) & ~size_t(255);
+    const size_t b_tok = (size_t)a.n_write * sizeof(int32_t);
+    const size_t o_ops = (o_tok + b_tok + 255) & ~size_t(255);
+    const size_t bytes = o_ops + op5.size() * sizeof(int32_t);
     int rc = p->ensure_dmeta(bytes, stream);
     if (rc) return rc;
     rc = p->upload(p->dmeta, bytes, stream, [&](uint8_t* h) {
-      if (n_slots) std::memcpy(h, slots, slot_bytes);
-      int32_t* o = (int32_t*)(h + op_off);
-      for (int32_t i = 0; i < n_ops; ++i) {
-        o[3 * i] = ops[i].src;
-        o[3 * i + 1] = ops[i].dst;
-        o[3 * i + 2] = ops[i].n_valid;
-      }
+      if (b_slots) std::memcpy(h, wslot.data(), b_slots);
+      if (b_tok) std::memcpy(h + o_tok, wtok.data(), b_tok);
+      if (!op5.empty()) std::memcpy(h + o_ops, op5.data(), op5.size() * sizeof(int32_t));
     });
     if (rc) return rc;
-    a.slots = (const int64_t*)p->dmeta;
-    a.ops = (const int32_t*)((uint8_t*)p->dmeta + op_off);
+    uint8_t* base = (uint8_t*)p->dmeta;
+    a.wslots = (const int64_t*)base;
+    a.wtok = (const int32_t*)(base + o_tok);
+    a.ops = (const int32_t*)(base + o_ops);
   }
   return p->timed(
       T_APPEND, [&](const LaunchEvents& ev) { return launch_append(d.kv_dtype, a, stream, ev); },
@@ -442,6 +479,37 @@ int pkv_seq_free(pkv_pool* pool, pkv_seq seq) {
   PKV_GUARD_BEGIN
   if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
   return pool->pool.seq_free(seq);
+  PKV_GUARD_END
+}
+
+int pkv_seq_fork_many(pkv_pool* pool, const pkv_seq* parents, int32_t n, pkv_seq* children) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  if (n < 0 || (n > 0 && (!parents || !children))) return fail(PKV_E_INVALID, "fork_many: bad arguments");
+  for (int32_t i = 0; i < n; ++i)
+    if (!pool->pool.get(parents[i])) return PKV_E_INVALID;
+  for (int32_t i = 0; i < n; ++i) {
+    int rc = pool->pool.seq_fork(parents[i], &children[i]);
+    if (rc) {  // cannot happen after the checks (host allocation aside): undo
+      for (int32_t j = 0; j < i; ++j) (void)pool->pool.seq_free(children[j]);
+      return rc;
+    }
+  }
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_seq_free_many(pkv_pool* pool, const pkv_seq* seqs, int32_t n) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  if (n < 0 || (n > 0 && !seqs)) return fail(PKV_E_INVALID, "free_many: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    if (!pool->pool.get(seqs[i])) return PKV_E_INVALID;
+    for (int32_t j = 0; j < i; ++j)
+      if (seqs[j].index == seqs[i].index) return fail(PKV_E_INVALID, "free_many: handle listed twice");
+  }
+  for (int32_t i = 0; i < n; ++i) (void)pool->pool.seq_free(seqs[i]);
+  return PKV_OK;
   PKV_GUARD_END
 }
 

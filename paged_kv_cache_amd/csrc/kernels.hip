@@ -85,56 +85,77 @@ __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
 // ------------------------------------------------------------- append
 //
 // One launch performs an append's copy-on-write copies and its token writes.
-// Workgroups [0, n_ops * L) copy: one (op, layer) each, all KV heads,
-// slots [0, n_valid) of the source tile into the destination tile. The rest
-// write: one (layer, token) each, all KV heads. A copy fills slots below
-// n_valid of a fresh block and the writes land at or above it (or in other
-// blocks), and a copy's source is shared, so no write touches it: the two
-// parts never overlap and need no ordering.
+// Workgroups [0, n_ops * L * Hkv) build the destination tile of one
+// (op, layer, KV head): the source's slots [0, n_valid) plus the new tokens
+// that land in the block (slots n_valid .. n_valid + m - 1); slots above
+// that are left unspecified. V rows ([BS] per (head, d)) are copied whole
+// with 16-byte vectors and patched in registers. No other workgroup writes
+// the destination block, and a copy's source is shared, so no write
+// touches it: copies and writes need no ordering. The remaining workgroups
+// write one (layer, token) of the write list each, all KV heads.
 
-template <typename T>
+template <typename T, int BS>
+__device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l, int h) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int RV = BS / EPV;  // 16-byte vectors per V row
+  const int32_t* op = p.ops ? p.ops + 5 * o : p.inl_ops + 5 * o;
+  const int src = op[0], dst = op[1], nv = op[2], tok0 = op[3], m = op[4];
+  const int64_t tile = (int64_t)BS * p.D;
+  T* __restrict__ K = (T*)p.k_arena;
+  T* __restrict__ V = (T*)p.v_arena;
+  const T* __restrict__ kn = (const T*)p.k_new;
+  const T* __restrict__ vn = (const T*)p.v_new;
+  const int64_t st = ((int64_t)l * p.NB + src) * p.Hkv + h;
+  const int64_t dt = ((int64_t)l * p.NB + dst) * p.Hkv + h;
+  // K rows: [0, nv) from the source, [nv, nv + m) from the new tokens
+  const int vrow = p.D / EPV;  // vectors per K row
+  for (int i = threadIdx.x; i < (nv + m) * vrow; i += blockDim.x) {
+    const int t = i / vrow, c = i - t * vrow;
+    const u32x4* from =
+        t < nv ? (const u32x4*)(K + st * tile + (int64_t)t * p.D) + c
+               : (const u32x4*)(kn + (((int64_t)l * p.n_tok + tok0 + t - nv) * p.Hkv + h) * p.D) + c;
+    const u32x4 x = *from;
+    ((u32x4*)(K + dt * tile + (int64_t)t * p.D))[c] = x;
+  }
+  // V rows: whole rows from the source, new tokens patched in
+  for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
+    const u32x4* vs = (const u32x4*)(V + st * tile + (int64_t)d * BS);
+    u32x4 row[RV];
+#pragma unroll
+    for (int c = 0; c < RV; ++c) row[c] = vs[c];
+    T* e = (T*)row;
+    for (int i = 0; i < m; ++i) e[nv + i] = vn[(((int64_t)l * p.n_tok + tok0 + i) * p.Hkv + h) * p.D + d];
+    u32x4* vd = (u32x4*)(V + dt * tile + (int64_t)d * BS);
+#pragma unroll
+    for (int c = 0; c < RV; ++c) vd[c] = row[c];
+  }
+}
+
+template <typename T, int BS>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-  const int n_copy = p.n_ops * p.L;
-  const int64_t tile = (int64_t)p.BS * p.D;
-  T* K = (T*)p.k_arena;
-  T* V = (T*)p.v_arena;
+  const int n_copy = p.n_ops * p.L * p.Hkv;
   if ((int)blockIdx.x < n_copy) {
-    const int o = blockIdx.x / p.L;
-    const int l = blockIdx.x - o * p.L;
-    const int* op = p.ops ? p.ops + 3 * o : p.inl_ops + 3 * o;
-    const int src = op[0], dst = op[1], nv = op[2];
-    const int64_t s0 = ((int64_t)l * p.NB + src) * p.Hkv;
-    const int64_t d0 = ((int64_t)l * p.NB + dst) * p.Hkv;
-    // K: per head, the first nv token rows are one contiguous run of
-    // nv * D * sizeof(T) bytes, a whole number of 16-byte vectors
-    const int vec_per_head = (int)((int64_t)nv * p.D * sizeof(T) / 16);
-    for (int i = threadIdx.x; i < vec_per_head * p.Hkv; i += blockDim.x) {
-      const int h = i / vec_per_head, v = i - h * vec_per_head;
-      const u32x4* ks = (const u32x4*)(K + (s0 + h) * tile);
-      u32x4* kd = (u32x4*)(K + (d0 + h) * tile);
-      kd[v] = ks[v];
-    }
-    // V: nv leading entries of each of the Hkv * D rows
-    const int per_head = nv * p.D;
-    for (int i = threadIdx.x; i < per_head * p.Hkv; i += blockDim.x) {
-      const int h = i / per_head, r = i - h * per_head;
-      const int d = r / nv, t = r - d * nv;
-      V[(d0 + h) * tile + d * p.BS + t] = V[(s0 + h) * tile + d * p.BS + t];
-    }
+    const int per_op = p.L * p.Hkv;
+    const int o = blockIdx.x / per_op;
+    const int r = blockIdx.x - o * per_op;
+    append_copy<T, BS>(p, o, r / p.Hkv, r - (r / p.Hkv) * p.Hkv);
     return;
   }
-  const int w = blockIdx.x - n_copy;  // (layer, token)
-  const int l = w / p.n_slots, i = w - l * p.n_slots;
-  const int64_t slot = p.slots ? p.slots[i] : p.inl_slots[i];
-  const int64_t b = slot / p.BS;
-  const int off = (int)(slot - b * p.BS);
+  const int w = blockIdx.x - n_copy;  // (layer, write entry)
+  const int l = w / p.n_write, i = w - l * p.n_write;
+  const int64_t slot = p.wslots ? p.wslots[i] : p.inl_slots[i];
+  const int tok = p.wtok ? p.wtok[i] : p.inl_tok[i];
+  const int64_t b = slot / BS;
+  const int off = (int)(slot - b * BS);
   const int64_t t0 = ((int64_t)l * p.NB + b) * p.Hkv;
-  const T* kn = (const T*)p.k_new + ((int64_t)l * p.n_slots + i) * p.Hkv * p.D;
-  const T* vn = (const T*)p.v_new + ((int64_t)l * p.n_slots + i) * p.Hkv * p.D;
+  T* K = (T*)p.k_arena;
+  T* V = (T*)p.v_arena;
+  const T* kn = (const T*)p.k_new + ((int64_t)l * p.n_tok + tok) * p.Hkv * p.D;
+  const T* vn = (const T*)p.v_new + ((int64_t)l * p.n_tok + tok) * p.Hkv * p.D;
   for (int e = threadIdx.x; e < p.Hkv * p.D; e += blockDim.x) {
     const int h = e / p.D, d = e - h * p.D;
-    K[((t0 + h) * p.BS + off) * p.D + d] = kn[e];
-    V[((t0 + h) * p.D + d) * p.BS + off] = vn[e];
+    K[((t0 + h) * BS + off) * p.D + d] = kn[e];
+    V[((t0 + h) * p.D + d) * BS + off] = vn[e];
   }
 }
 
@@ -631,13 +652,28 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
 
 hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t stream,
                          const LaunchEvents& ev) {
-  const int64_t g64 = (int64_t)p.n_ops * p.L + (int64_t)p.n_slots * p.L;
+  const int64_t g64 = (int64_t)p.n_ops * p.L * p.Hkv + (int64_t)p.n_write * p.L;
   if (g64 == 0) return hipSuccess;
   if (g64 > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid((unsigned)g64);
-  if (dtype == 0) return launch(append_kernel<float>, grid, dim3(256), stream, ev, p);
-  return launch(append_kernel<uint16_t>, grid, dim3(256), stream, ev, p);
+  const dim3 blk(256);
+  if (dtype == 0) {
+    switch (p.BS) {
+      case 16: return launch(append_kernel<float, 16>, grid, blk, stream, ev, p);
+      case 32: return launch(append_kernel<float, 32>, grid, blk, stream, ev, p);
+      case 64: return launch(append_kernel<float, 64>, grid, blk, stream, ev, p);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (p.BS) {
+    case 16: return launch(append_kernel<uint16_t, 16>, grid, blk, stream, ev, p);
+    case 32: return launch(append_kernel<uint16_t, 32>, grid, blk, stream, ev, p);
+    case 64: return launch(append_kernel<uint16_t, 64>, grid, blk, stream, ev, p);
+    default: return hipErrorInvalidValue;
+  }
 }
+
+bool append_supported(int BS) { return BS == 16 || BS == 32 || BS == 64; }
 
 bool attn_supported(bool mfma, int dtype, int D, int BS) {
   const bool shape_ok = (D == 64 || D == 128 || D == 256) && (BS == 16 || BS == 32 || BS == 64);

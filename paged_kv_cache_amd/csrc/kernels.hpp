@@ -19,28 +19,36 @@ struct LaunchEvents {
 constexpr int kInlineOps = 16;
 constexpr int kInlineSlots = 64;
 
-// One append: copy-on-write copies (ops: triples src, dst, n_valid) and the
-// writes of n_slots new tokens ([L][n_slots][Hkv][D] K and V). Small lists
-// travel inside the arguments (ops / slots == nullptr); larger ones are read
-// from device memory.
+// One append: copy-on-write copies and the writes of new tokens, whose K
+// and V are [L][n_tok][Hkv][D]. An op is five ints: src, dst, n_valid,
+// and the range [tok0, tok0 + m) of new tokens that land in dst right
+// after the copied slots. The write list holds every other new token: its
+// slot and its index in the new-token arrays. Small lists travel inside the
+// arguments (ops / wslots / wtok == nullptr); larger ones are read from
+// device memory.
 struct AppendParams {
   const void* k_new;
   const void* v_new;
   void* k_arena;
   void* v_arena;
   const int32_t* ops;
-  const int64_t* slots;
+  const int64_t* wslots;
+  const int32_t* wtok;
   int32_t n_ops;
-  int32_t n_slots;
+  int32_t n_write;
+  int32_t n_tok;
   int32_t L;
   int32_t NB;
   int32_t Hkv;
   int32_t D;
   int32_t BS;
-  int32_t pad;
-  int32_t inl_ops[3 * kInlineOps];
+  int32_t inl_ops[5 * kInlineOps];
   int64_t inl_slots[kInlineSlots];
+  int32_t inl_tok[kInlineSlots];
 };
+
+// Block sizes the append kernel is built for.
+bool append_supported(int BS);
 
 hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t stream,
                          const LaunchEvents& ev);

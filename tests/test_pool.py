@@ -275,3 +275,24 @@ def test_plan_segments_closed_form(pkv, name, segments):
     assert info["unique_tokens"] == distinct_tokens(c, seqs)
     assert info["n_chunks"] >= segments
     assert info["workspace_bytes"] > 0
+
+
+def test_fork_many_and_free_many(pkv):
+    c = host_cache(pkv, 32, 4)
+    p = c.create()
+    c.plan(p, 6)
+    kids = c.fork_many([p, p, p])
+    assert [c.table(k) for k in kids] == [c.table(p)] * 3
+    assert [c.refcount(b) for b in c.table(p)] == [4, 4]
+    before = c.stats()
+    stale = c.create()
+    c.free(stale)
+    with pytest.raises(pkv.PkvError):
+        c.fork_many([p, stale])          # all or nothing
+    assert c.stats() == before
+    with pytest.raises(pkv.PkvError):
+        c.free_many([kids[0], kids[0]])  # listed twice
+    assert c.stats() == before
+    c.free_many(kids)
+    assert [c.refcount(b) for b in c.table(p)] == [1, 1]
+    assert c.stats()["live_seqs"] == 1
