@@ -244,16 +244,24 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
 /* Tuning knobs of the attention planner (defaults in parentheses):
  *   "path"              0 automatic (1 = vector ALUs, 2 = matrix cores)
  *   "chunk_tokens"      0 automatic: tokens per chunk of a shared segment
- *   "rows_per_item"     64: query rows one workgroup serves
- *   "target_workgroups" 2048: chunks are shortened until the grid has this many
+ *   "rows_per_item"     32: query rows a narrow work item serves (1..64)
+ *   "wide"              1: chunks read by more rows use the wide-row kernel
+ *   "wide_rows"         128: query rows a wide work item serves (16..128)
+ *   "prefetch"          0: 1 makes each wave of the narrow kernel load its next
+ *                       32-token step while the current one computes
+ *   "wide_waves"        8: waves per wide workgroup, 4 (two 16-row blocks each)
+ *                       or 8 (one each); head_dim 256 always uses 8
+ *   "target_workgroups" 256: chunks are shortened (down to 1024 tokens) until the
+ *                       grid has this many workgroups
  *   "timing"            0: 1 records a pair of HIP events at the start and end
  *                       of every kernel the pool launches (pkv_timing_read)
  * Unknown keys or out-of-range values are PKV_E_INVALID. */
 int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value);
 
 /* Device time of the kernels launched since the last read (with the
- * "timing" option on): kernel is "attention", "combine" or "append" (the
- * launch that performs copy-on-write copies and token writes). Waits for
+ * "timing" option on): kernel is "attention" (items of few rows),
+ * "attention_wide" (items of many rows), "combine" or "append" (the launch
+ * that performs copy-on-write copies and token writes). Waits for
  * the last recorded launch, returns the summed milliseconds and the launch
  * count, and resets both. */
 int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_t* launches);

@@ -79,7 +79,7 @@ struct KernelTimer {
   }
 };
 
-enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_KINDS = 3 };
+enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_WIDE = 3, T_KINDS = 4 };
 
 struct pkv_pool {
   explicit pkv_pool(const pkv_pool_desc& d) : pool(d) {}
@@ -108,6 +108,8 @@ struct pkv_pool {
   PlannerScratch scratch;
   SchedOptions opt;
   int path = 0;  // 0 auto, 1 VALU, 2 matrix cores
+  int wide_waves = 8;  // waves per wide workgroup (4 or 8)
+  int prefetch = 0;    // narrow matrix-core kernel loads one step ahead
 
   // schedule cache
   bool cache_valid = false;
@@ -315,7 +317,10 @@ int decode_schedule(pkv_pool* p, const pkv_seq* seqs, int32_t n, int32_t layer0,
     return PKV_OK;
   p->cache_valid = false;
   SchedOptions o = p->opt;
-  if (!mfma) o.rows_per_item = std::min<int32_t>(o.rows_per_item, 16);
+  if (!mfma) {
+    o.rows_per_item = std::min<int32_t>(o.rows_per_item, 16);
+    o.wide = false;
+  }
   int rc = build_decode_schedule(p->pool, seqs, n, n_layers, layer0, o, &p->scratch, &p->sched);
   if (rc) return rc;
   p->cache_valid = true;
@@ -372,6 +377,8 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.blk = (const int32_t*)(w + S.off_blk);
   a.holders = (const int32_t*)(w + S.off_holders);
   a.anc = (const uint64_t*)(w + S.off_anc);
+  a.order = (const int32_t*)(w + S.off_order);
+  a.n_order = S.n_order_narrow;
   a.n_items = (int32_t)S.items.size();
   a.n_layers = S.n_layers;
   a.layer0 = layer0;
@@ -385,13 +392,28 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   // P enters P.V as bf16 plus its bf16 rounding residual: with P alone in
   // bf16 a row whose weight sits on a few keys is off by up to 2^-9 |v|
   const bool lo_split = true;
-  rc = p->timed(
-      T_ATTN,
-      [&](const LaunchEvents& ev) {
-        return launch_attn(mfma, lo_split, d.kv_dtype, d.head_dim, d.block_size, a, stream, ev);
-      },
-      "attention launch");
-  if (rc) return rc;
+  if (a.n_order > 0) {
+    rc = p->timed(
+        T_ATTN,
+        [&](const LaunchEvents& ev) {
+          return launch_attn(mfma, lo_split, p->prefetch != 0, d.kv_dtype, d.head_dim, d.block_size,
+                             a, stream, ev);
+        },
+        "attention launch");
+    if (rc) return rc;
+  }
+  if (S.n_order_wide > 0) {
+    AttnParams aw = a;
+    aw.order = a.order + S.n_order_narrow;
+    aw.n_order = S.n_order_wide;
+    rc = p->timed(
+        T_WIDE,
+        [&](const LaunchEvents& ev) {
+          return launch_attn_wide(d.head_dim, d.block_size, p->wide_waves, aw, stream, ev);
+        },
+        "wide attention launch");
+    if (rc) return rc;
+  }
   CombineParams c;
   c.part_ml = a.part_ml;
   c.part_acc = a.part_acc;
@@ -721,6 +743,18 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "rows_per_item") {
     if (value < 1 || value > 64) return fail(PKV_E_INVALID, "rows_per_item must be 1..64");
     pool->opt.rows_per_item = (int32_t)value;
+  } else if (k == "wide") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "wide must be 0 or 1");
+    pool->opt.wide = value != 0;
+  } else if (k == "prefetch") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "prefetch must be 0 or 1");
+    pool->prefetch = (int)value;
+  } else if (k == "wide_waves") {
+    if (value != 4 && value != 8) return fail(PKV_E_INVALID, "wide_waves must be 4 or 8");
+    pool->wide_waves = (int)value;
+  } else if (k == "wide_rows") {
+    if (value < 16 || value > 128) return fail(PKV_E_INVALID, "wide_rows must be 16..128");
+    pool->opt.wide_rows = (int32_t)value;
   } else if (k == "timing") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "timing must be 0 or 1");
     pool->timing = value != 0;
@@ -739,7 +773,11 @@ int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_
   PKV_GUARD_BEGIN
   if (!pool_ok(pool) || !kernel || !total_ms || !launches) return fail(PKV_E_INVALID, "null argument");
   const std::string k(kernel);
-  int kind = k == "attention" ? T_ATTN : k == "combine" ? T_COMBINE : k == "append" ? T_APPEND : -1;
+  int kind = k == "attention" ? T_ATTN
+             : k == "attention_wide" ? T_WIDE
+             : k == "combine" ? T_COMBINE
+             : k == "append" ? T_APPEND
+                               : -1;
   if (kind < 0) return fail(PKV_E_INVALID, "unknown kernel " + k);
   return pool->timers[kind].read(total_ms, launches);
   PKV_GUARD_END

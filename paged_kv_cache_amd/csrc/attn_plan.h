@@ -5,9 +5,11 @@
 // (its holders) reference at the same logical positions; forks share
 // prefixes, so the segments of a batch form a tree. A segment is cut into
 // *chunks* of whole blocks, and a chunk's rows (holder x query head of one
-// KV-head group) are cut into *work items* of at most 64 rows. The grid
-// replicates every work item over (layer, KV head): one workgroup reads the
-// chunk's K/V tiles once and applies them to all of its rows.
+// KV-head group) are cut into *work items*: narrow items of up to 32 rows
+// or wide items of up to 128 rows. Every work item runs once per (layer, KV
+// head); an order table maps workgroups to (item, layer, head) so that the
+// wide items of one chunk land on the same XCD, next to each other in
+// dispatch order, and share its L2.
 #pragma once
 
 #include <cstdint>
@@ -23,8 +25,11 @@ struct WorkItem {
   int32_t n_rows;     // rows handled by this item (1 .. 64)
   int32_t part_row;   // partial-state row of this item's first row, per plane
   int32_t mask_from;  // first logical position under the draft-tree mask (INT32_MAX: none)
+  int32_t reread;     // 1: another item (or another wave) reads the same chunk, so K/V
+                      // go through the caches; 0: streaming loads
+  int32_t pad[3];
 };
-static_assert(sizeof(WorkItem) == 32, "WorkItem layout");
+static_assert(sizeof(WorkItem) == 48, "WorkItem layout");
 
 // Device-side pointers to a decode / verify schedule and its partials.
 // Partial states are stored per plane (layer, KV head): P rows each.
@@ -38,6 +43,8 @@ struct AttnParams {
   const int32_t* blk;       // block ids, per chunk padded to a whole 32-token step
   const int32_t* holders;   // branch index of each holder
   const uint64_t* anc;      // [n_branch] ancestor-or-self bits (verify only)
+  const int32_t* order;     // per workgroup: item * (n_layers * Hkv) + layer * Hkv + head, or -1
+  int32_t n_order;          // workgroups in the launch
   int32_t n_items;
   int32_t n_layers;
   int32_t layer0;

@@ -28,6 +28,15 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ u32x4 ld16(const void* ptr) { return *(const u32x4*)ptr; }
 
+// K/V tiles that only one wave reads are fetched with streaming
+// (non-temporal) loads: on gfx950 they sustain ~7 TB/s on long reads where
+// ordinary loads stop near 5.4 TB/s. Tiles that two waves of a workgroup,
+// or sibling workgroups, read use ordinary loads, so that the second read
+// hits in the caches instead of going back to HBM.
+__device__ __forceinline__ u32x4 ld16_stream(const void* ptr) {
+  return __builtin_nontemporal_load((const u32x4*)ptr);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
@@ -181,7 +190,27 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int BS, bool LO>
+// Online softmax with a lazy reference: a row's probabilities are taken as
+// 2^(s - m) against a reference m that is moved (and the running sum and
+// accumulators rescaled) only when the row's maximum exceeds it by more
+// than 8, so weights stay below 2^8 and the accumulators, which live in
+// AGPRs, are rarely touched outside the matrix products. The vote keeps the
+// branch wave-uniform. The partial state (m, l, acc) then means
+// out = acc / l with acc and l both scaled by 2^-m, as before.
+template <int DB>
+__device__ __forceinline__ void rebase(float mx, float& m_ref, float& l_run, f32x4 (&acc)[DB]) {
+  const bool need = mx > m_ref + 8.f;
+  if (__any(need)) {
+    const float m_new = need ? mx : m_ref;
+    const float alpha = need ? fast_exp2(m_ref - m_new) : 1.f;  // 0 on the first finite max
+    l_run *= alpha;
+#pragma unroll
+    for (int j = 0; j < DB; ++j) acc[j] *= alpha;
+    m_ref = m_new;
+  }
+}
+
+template <int D, int BS, bool LO, bool PF>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   constexpr int KS = D / 32;  // 32-wide k steps of Q.K
   constexpr int DB = D / 16;  // 16-wide d blocks of P.V
@@ -194,9 +223,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
+  const int code = p.order[blockIdx.x];
+  if (code < 0) return;
   const int per_item = p.n_layers * p.Hkv;
-  const int item_idx = blockIdx.x / per_item;
-  const int rem = blockIdx.x - item_idx * per_item;
+  const int item_idx = code / per_item;
+  const int rem = code - item_idx * per_item;
   const int li = rem / p.Hkv;
   const int kvh = rem - li * p.Hkv;
   const int layer = p.layer0 + li;
@@ -247,97 +278,128 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   float m_run = kNegInf, l_run = 0.f;
   const int n_steps = (it.n_tok + 31) >> 5;
 
+  // K rows of this lane (both S^T tiles) and V^T columns of step s
+  const bool stream_kv = it.reread == 0;
+  auto ldkv = [&](const uint16_t* ptr) { return stream_kv ? ld16_stream(ptr) : ld16(ptr); };
+  auto load_kv = [&](int s, int bA, int bB, u32x4 (&kr)[2][KS], u32x4 (&vr)[DB]) {
+    const int tbase = s * 32;
+    const int kb = k_in_b ? bB : bA;
+    const uint16_t* kp =
+        K + ((layer_tiles + (int64_t)kb * p.Hkv + kvh) * BS + (tbase + koff0) % BS) * D + 8 * g;
+    const int vb = v_in_b ? bB : bA;
+    const uint16_t* vp =
+        V + ((layer_tiles + (int64_t)vb * p.Hkv + kvh) * D + n) * BS + (tbase + voff) % BS;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kr[0][ks] = ldkv(kp + 32 * ks);
+      kr[1][ks] = ldkv(kp + 4 * D + 32 * ks);
+    }
+#pragma unroll
+    for (int j = 0; j < DB; ++j) vr[j] = ldkv(vp + (int64_t)16 * j * BS);
+  };
+  auto compute = [&](int s, const u32x4 (&kraw)[2][KS], u32x4 (&vraw)[DB]) {
+    const int tbase = s * 32;
+    f32x4 st[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) c = mfma_bf16(as_bf16x8(kraw[tau][ks]), qv[ks], c);
+      st[tau] = c;
+    }
+    const bool tail = tbase + 32 > it.n_tok;
+    const int tv = tbase + voff;
+    float sc[8];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tau + i;
+        const int t = tv + e;
+        float v = st[tau][i] * p.scale_log2;
+        if (tail && t >= it.n_tok) v = kNegInf;
+        if (tree) {
+          const int pos = it.t0 + t;
+          if (pos >= it.mask_from && !((anc >> (pos - it.mask_from)) & 1ull)) v = kNegInf;
+        }
+        sc[e] = v;
+      }
+    if (tail) {
+      // slots past the chunk may hold anything (even NaN): zero them so
+      // that 0 * V stays 0 in the P.V product
+      u32x4 keep;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = (tv + 2 * w < it.n_tok) ? 0x0000ffffu : 0u;
+        const uint32_t hi = (tv + 2 * w + 1 < it.n_tok) ? 0xffff0000u : 0u;
+        keep[w] = lo | hi;
+      }
+#pragma unroll
+      for (int j = 0; j < DB; ++j) vraw[j] &= keep;
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+    mx = max_xor32(max_xor16(mx));
+    rebase(mx, m_run, l_run, acc);
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    float psum = 0.f;
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pe = fast_exp2(sc[e] - m_use);
+      psum += pe;
+      const __bf16 h = (__bf16)pe;
+      phi[e] = h;
+      if (LO) plo[e] = (__bf16)(pe - (float)h);
+    }
+    l_run += psum;
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      acc[j] = mfma_bf16(as_bf16x8(vraw[j]), phi, acc[j]);
+      if (LO) acc[j] = mfma_bf16(as_bf16x8(vraw[j]), plo, acc[j]);
+    }
+  };
+
   if (active && phase < n_steps) {
-    // block ids are wave-uniform (scalar loads), fetched one step ahead
-    int bA = blk[(32 * phase) / BS];
-    int bB = blk[(32 * phase + 16) / BS];
-    for (int s = phase; s < n_steps; s += phases) {
-      const int tbase = s * 32;
-      const int cA = bA, cB = bB;
-      if (s + phases < n_steps) {
-        bA = blk[(32 * (s + phases)) / BS];
-        bB = blk[(32 * (s + phases) + 16) / BS];
+    // block ids are wave-uniform (scalar loads)
+    auto ids = [&](int s, int& a, int& b) {
+      a = blk[(32 * s) / BS];
+      b = blk[(32 * s + 16) / BS];
+    };
+    if (!PF) {
+      int bA, bB;
+      ids(phase, bA, bB);
+      for (int s = phase; s < n_steps; s += phases) {
+        const int cA = bA, cB = bB;
+        if (s + phases < n_steps) ids(s + phases, bA, bB);
+        u32x4 kr[2][KS], vr[DB];
+        load_kv(s, cA, cB, kr, vr);
+        compute(s, kr, vr);
       }
-      // K rows of this lane (both S^T tiles) and V^T columns
-      const int kb = k_in_b ? cB : cA;
-      const int kslot = (tbase + koff0) % BS;
-      const uint16_t* kp = K + ((layer_tiles + (int64_t)kb * p.Hkv + kvh) * BS + kslot) * D + 8 * g;
-      const int vb = v_in_b ? cB : cA;
-      const uint16_t* vp =
-          V + ((layer_tiles + (int64_t)vb * p.Hkv + kvh) * D + n) * BS + (tbase + voff) % BS;
-      u32x4 kraw[2][KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kraw[0][ks] = ld16(kp + 32 * ks);
-        kraw[1][ks] = ld16(kp + 4 * D + 32 * ks);
-      }
-      u32x4 vraw[DB];
-#pragma unroll
-      for (int j = 0; j < DB; ++j) vraw[j] = ld16(vp + (int64_t)16 * j * BS);
-      f32x4 st[2];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) c = mfma_bf16(as_bf16x8(kraw[tau][ks]), qv[ks], c);
-        st[tau] = c;
-      }
-
-      const bool tail = tbase + 32 > it.n_tok;
-      const int tv = tbase + voff;
-      float sc[8];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = 4 * tau + i;
-          const int t = tv + e;
-          float v = st[tau][i] * p.scale_log2;
-          if (tail && t >= it.n_tok) v = kNegInf;
-          if (tree) {
-            const int pos = it.t0 + t;
-            if (pos >= it.mask_from && !((anc >> (pos - it.mask_from)) & 1ull)) v = kNegInf;
-          }
-          sc[e] = v;
+    } else {
+      // loads of the wave's next step are in flight while this one computes
+      // (two register sets, loop unrolled by two)
+      u32x4 ka[2][KS], va[DB], kb[2][KS], vb[DB];
+      int bA, bB;
+      ids(phase, bA, bB);
+      load_kv(phase, bA, bB, ka, va);
+      for (int s = phase; s < n_steps; s += 2 * phases) {
+        const int s1 = s + phases;
+        if (s1 < n_steps) {
+          ids(s1, bA, bB);
+          load_kv(s1, bA, bB, kb, vb);
         }
-      if (tail) {
-        // slots past the chunk may hold anything (even NaN): zero them so
-        // that 0 * V stays 0 in the P.V product
-        u32x4 keep;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = (tv + 2 * w < it.n_tok) ? 0x0000ffffu : 0u;
-          const uint32_t hi = (tv + 2 * w + 1 < it.n_tok) ? 0xffff0000u : 0u;
-          keep[w] = lo | hi;
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s, ka, va);
+        if (s1 >= n_steps) break;
+        const int s2 = s1 + phases;
+        if (s2 < n_steps) {
+          ids(s2, bA, bB);
+          load_kv(s2, bA, bB, ka, va);
         }
-#pragma unroll
-        for (int j = 0; j < DB; ++j) vraw[j] &= keep;
-      }
-
-      float mx = sc[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-      mx = max_xor32(max_xor16(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
-      bf16x8 phi, plo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pe = fast_exp2(sc[e] - m_use);
-        psum += pe;
-        const __bf16 h = (__bf16)pe;
-        phi[e] = h;
-        if (LO) plo[e] = (__bf16)(pe - (float)h);
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int j = 0; j < DB; ++j) {
-        acc[j] *= alpha;
-        acc[j] = mfma_bf16(as_bf16x8(vraw[j]), phi, acc[j]);
-        if (LO) acc[j] = mfma_bf16(as_bf16x8(vraw[j]), plo, acc[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(s1, kb, vb);
       }
     }
   }
@@ -387,6 +449,243 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   }
 }
 
+// ------------------------------------------------- wide MFMA attention
+//
+// For chunks read by many query rows (draft-tree verify: nodes x GQA group;
+// the shared root of a wide tree). One workgroup serves up to 128
+// rows: NW waves, wave w owns row blocks w + NW * r for r < RBW (4 waves x
+// 2 blocks up to D = 128; 8 waves x 1 block at D = 256, where two blocks'
+// accumulators and queries would not fit one wave's registers). Each
+// 32-token step of K/V is loaded once by the whole workgroup into LDS,
+// already in operand order:
+// 1 KiB section per (K tile, k step) and per V d block, lane l's 16 bytes at
+// l * 16, so every operand read is a conflict-free ds_read_b128 and each
+// wave applies it to all of its row blocks. Loads run two steps ahead of
+// the math (two register sets, two LDS buffers). Math per row block is the
+// narrow kernel's.
+
+template <int D, int BS, int NW, int RBW>
+__global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
+  constexpr int KS = D / 32;
+  constexpr int DB = D / 16;
+  constexpr int NSEC = 2 * KS + DB;  // 1 KiB sections per step
+  constexpr int CPT = NSEC / NW;     // sections (16 B per lane) each wave stages
+  constexpr int KCPT = (2 * KS) / NW;  // of which K sections
+  static_assert(NSEC % NW == 0 && (2 * KS) % NW == 0, "sections per wave");
+  static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
+  static_assert(RBW == 1 || RBW == 2, "row blocks per wave");
+  __shared__ u32x4 stage[2][NSEC * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int code = p.order[blockIdx.x];
+  if (code < 0) return;
+  const int per_item = p.n_layers * p.Hkv;
+  const int item_idx = code / per_item;
+  const int rem = code - item_idx * per_item;
+  const int li = rem / p.Hkv;
+  const int kvh = rem - li * p.Hkv;
+  const int layer = p.layer0 + li;
+  const WorkItem it = p.items[item_idx];
+  const int RB = (it.n_rows + 15) >> 4;
+  int nrb = 0;
+#pragma unroll
+  for (int r = 0; r < RBW; ++r) nrb += (wave + NW * r < RB) ? 1 : 0;
+  const bool tree = it.mask_from != 0x7fffffff && it.t0 + it.n_tok > it.mask_from;
+
+  bf16x8 qv[RBW][KS];
+  bool row_ok[RBW];
+  uint64_t anc[RBW];
+#pragma unroll
+  for (int r = 0; r < RBW; ++r) {
+    const int row = (wave + NW * r) * 16 + n;
+    row_ok[r] = r < nrb && row < it.n_rows;
+    const int crow = it.r0 + row;
+    const int hold = crow / p.G;
+    const int gq = crow - hold * p.G;
+    const int branch = row_ok[r] ? p.holders[it.hold_off + hold] : 0;
+    const uint16_t* qp = (const uint16_t*)p.q +
+                         (((int64_t)li * p.n_branch + branch) * p.Hq + kvh * p.G + gq) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 raw = {0u, 0u, 0u, 0u};
+      if (row_ok[r]) raw = ld16(qp + 32 * ks);
+      qv[r][ks] = as_bf16x8(raw);
+    }
+    anc[r] = (tree && row_ok[r]) ? p.anc[branch] : ~0ull;
+  }
+
+  const uint16_t* K = (const uint16_t*)p.k_arena;
+  const uint16_t* V = (const uint16_t*)p.v_arena;
+  const int64_t layer_tiles = (int64_t)layer * p.num_blocks * p.Hkv;
+  const int32_t* blk = p.blk + it.blk_off;
+  const int n_steps = (it.n_tok + 31) >> 5;
+  const int koff0 = 8 * (n >> 2) + (n & 3);
+  const int voff = 8 * g;
+
+  // global -> registers: this wave's sections of step s (section
+  // NW * i + wave; the first 2KS sections are K, the rest V)
+  const bool stream_kv = it.reread == 0;
+  auto ldkv = [&](const uint16_t* ptr) { return stream_kv ? ld16_stream(ptr) : ld16(ptr); };
+  auto load_step = [&](int s, u32x4 (&r)[CPT]) {
+    const int tbase = 32 * s;
+    const int bA = blk[tbase / BS];
+    const int bB = blk[(tbase + 16) / BS];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int sect = wave + NW * i;
+      if (i < KCPT) {
+        const int tau = sect / KS, ks = sect - (sect / KS) * KS;
+        const int off = koff0 + 4 * tau;
+        const int b = (BS == 16 && off >= 16) ? bB : bA;
+        r[i] = ldkv(K + ((layer_tiles + (int64_t)b * p.Hkv + kvh) * BS + (tbase + off) % BS) * D +
+                    32 * ks + 8 * g);
+      } else {
+        const int j = sect - 2 * KS;
+        const int b = (BS == 16 && voff >= 16) ? bB : bA;
+        u32x4 v = ldkv(V + ((layer_tiles + (int64_t)b * p.Hkv + kvh) * D + 16 * j + n) * BS +
+                       (tbase + voff) % BS);
+        if (tbase + 32 > it.n_tok) {
+          // slots past the chunk may hold anything: zero them (0 * V = 0)
+          const int tv = tbase + voff;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t lo = (tv + 2 * w < it.n_tok) ? 0x0000ffffu : 0u;
+            const uint32_t hi = (tv + 2 * w + 1 < it.n_tok) ? 0xffff0000u : 0u;
+            v[w] &= lo | hi;
+          }
+        }
+        r[i] = v;
+      }
+    }
+  };
+  auto store_step = [&](int buf, const u32x4 (&r)[CPT]) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) stage[buf][(wave + NW * i) * 64 + lane] = r[i];
+  };
+
+  f32x4 acc[RBW][DB];
+#pragma unroll
+  for (int r = 0; r < RBW; ++r)
+#pragma unroll
+    for (int j = 0; j < DB; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[RBW], l_run[RBW];
+#pragma unroll
+  for (int r = 0; r < RBW; ++r) {
+    m_run[r] = kNegInf;
+    l_run[r] = 0.f;
+  }
+
+  // Pipeline: the loads of step s + 2 are issued (into the free register
+  // set) before step s computes; step s + 1's registers, loaded a step
+  // earlier, go to the other LDS buffer after it. The loop is unrolled by
+  // two so that both register sets keep static indices.
+  auto compute = [&](int step, int buf) {
+    const u32x4* st_sec = stage[buf];
+    const int s = step;
+    if (nrb > 0) {
+      f32x4 sc4[RBW][2];
+#pragma unroll
+      for (int r = 0; r < RBW; ++r)
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) sc4[r][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = as_bf16x8(st_sec[(tau * KS + ks) * 64 + lane]);
+#pragma unroll
+          for (int r = 0; r < RBW; ++r)
+            if (r < nrb) sc4[r][tau] = mfma_bf16(a, qv[r][ks], sc4[r][tau]);
+        }
+      const int tbase = 32 * s;
+      const bool tail = tbase + 32 > it.n_tok;
+      const int tv = tbase + voff;
+      bf16x8 phi[RBW], plo[RBW];
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) {
+        if (r >= nrb) continue;
+        float sc[8];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * tau + i;
+            const int t = tv + e;
+            float v = sc4[r][tau][i] * p.scale_log2;
+            if (tail && t >= it.n_tok) v = kNegInf;
+            if (tree) {
+              const int pos = it.t0 + t;
+              if (pos >= it.mask_from && !((anc[r] >> (pos - it.mask_from)) & 1ull)) v = kNegInf;
+            }
+            sc[e] = v;
+          }
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        mx = max_xor32(max_xor16(mx));
+        rebase(mx, m_run[r], l_run[r], acc[r]);
+        const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pe = fast_exp2(sc[e] - m_use);
+          psum += pe;
+          const __bf16 h = (__bf16)pe;
+          phi[r][e] = h;
+          plo[r][e] = (__bf16)(pe - (float)h);
+        }
+        l_run[r] += psum;
+      }
+#pragma unroll
+      for (int j = 0; j < DB; ++j) {
+        const bf16x8 a = as_bf16x8(st_sec[(2 * KS + j) * 64 + lane]);
+#pragma unroll
+        for (int r = 0; r < RBW; ++r) {
+          if (r < nrb) {
+            acc[r][j] = mfma_bf16(a, phi[r], acc[r][j]);
+            acc[r][j] = mfma_bf16(a, plo[r], acc[r][j]);
+          }
+        }
+      }
+    }
+  };
+  u32x4 ra[CPT], rb[CPT];
+  load_step(0, ra);
+  store_step(0, ra);
+  if (n_steps > 1) load_step(1, rb);
+  __syncthreads();
+  for (int s = 0; s < n_steps; s += 2) {
+    if (s + 2 < n_steps) load_step(s + 2, ra);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, 0);
+    if (s + 1 < n_steps) store_step(1, rb);
+    __syncthreads();
+    if (s + 1 >= n_steps) break;
+    if (s + 3 < n_steps) load_step(s + 3, rb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s + 1, 1);
+    if (s + 2 < n_steps) store_step(0, ra);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < RBW; ++r) {
+    if (r >= nrb) continue;
+    const float l_tot = sum_xor32(sum_xor16(l_run[r]));
+    if (!row_ok[r]) continue;
+    const int row = (wave + NW * r) * 16 + n;
+    const int64_t prow = (int64_t)(li * p.Hkv + kvh) * p.P + it.part_row + row;
+    if (g == 0) {
+      p.part_ml[2 * prow] = m_run[r];
+      p.part_ml[2 * prow + 1] = l_tot;
+    }
+    float* pa = p.part_acc + prow * D;
+#pragma unroll
+    for (int j = 0; j < DB; ++j) *(f32x4*)(pa + 16 * j + 4 * g) = acc[r][j];
+  }
+}
+
 // ----------------------------------------------------- VALU attention
 //
 // One workgroup (4 waves) per (work item, layer, KV head), at most 16 rows.
@@ -411,9 +710,11 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   __shared__ float mrg_acc[3][MAXR][D];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int code = p.order[blockIdx.x];
+  if (code < 0) return;
   const int per_item = p.n_layers * p.Hkv;
-  const int item_idx = blockIdx.x / per_item;
-  const int rem = blockIdx.x - item_idx * per_item;
+  const int item_idx = code / per_item;
+  const int rem = code - item_idx * per_item;
   const int li = rem / p.Hkv;
   const int kvh = rem - li * p.Hkv;
   const int layer = p.layer0 + li;
@@ -617,7 +918,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const float mi = p.part_ml[2 * row];
     const float w = mi == kNegInf ? 0.f : fast_exp2(mi - M);
     L += p.part_ml[2 * row + 1] * w;
-    const vec_t a = *(const vec_t*)(p.part_acc + row * D + lane * VW);
+    const vec_t a = __builtin_nontemporal_load((const vec_t*)(p.part_acc + row * D + lane * VW));
     acc += a * w;
   }
   if (WPR > 1) {
@@ -684,12 +985,12 @@ bool attn_supported(bool mfma, int dtype, int D, int BS) {
 
 namespace {
 
-template <int D, bool LO>
+template <int D, bool LO, bool PF>
 hipError_t launch_mfma_d(int BS, const AttnParams& p, dim3 grid, hipStream_t s, const LaunchEvents& ev) {
   switch (BS) {
-    case 16: return launch(attn_mfma_kernel<D, 16, LO>, grid, dim3(256), s, ev, p);
-    case 32: return launch(attn_mfma_kernel<D, 32, LO>, grid, dim3(256), s, ev, p);
-    default: return launch(attn_mfma_kernel<D, 64, LO>, grid, dim3(256), s, ev, p);
+    case 16: return launch(attn_mfma_kernel<D, 16, LO, PF>, grid, dim3(256), s, ev, p);
+    case 32: return launch(attn_mfma_kernel<D, 32, LO, PF>, grid, dim3(256), s, ev, p);
+    default: return launch(attn_mfma_kernel<D, 64, LO, PF>, grid, dim3(256), s, ev, p);
   }
 }
 
@@ -712,18 +1013,40 @@ hipError_t launch_valu(int D, int BS, const AttnParams& p, dim3 grid, hipStream_
 
 }  // namespace
 
-hipError_t launch_attn(bool mfma, bool lo_split, int dtype, int D, int BS, const AttnParams& p,
-                       hipStream_t stream, const LaunchEvents& ev) {
+hipError_t launch_attn_wide(int D, int BS, int waves, const AttnParams& p, hipStream_t stream,
+                            const LaunchEvents& ev) {
+  if (!attn_supported(true, 1, D, BS)) return hipErrorInvalidValue;
+  if (p.n_order == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.n_order);
+#define PKV_WIDE(d, nw, rbw)                                                                    \
+  switch (BS) {                                                                                 \
+    case 16: return launch(attn_wide_kernel<d, 16, nw, rbw>, grid, dim3(nw * 64), stream, ev, p); \
+    case 32: return launch(attn_wide_kernel<d, 32, nw, rbw>, grid, dim3(nw * 64), stream, ev, p); \
+    default: return launch(attn_wide_kernel<d, 64, nw, rbw>, grid, dim3(nw * 64), stream, ev, p); \
+  }
+  // 128 rows per item either way: 4 waves x 2 row blocks or 8 waves x 1
+  if (D == 64) PKV_WIDE(64, 4, 2)  // 8 waves would leave K sections unevenly split
+  if (D == 128) {
+    if (waves == 8) PKV_WIDE(128, 8, 1)
+    PKV_WIDE(128, 4, 2)
+  }
+  PKV_WIDE(256, 8, 1)
+#undef PKV_WIDE
+}
+
+hipError_t launch_attn(bool mfma, bool lo_split, bool prefetch, int dtype, int D, int BS,
+                       const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
   if (!attn_supported(mfma, dtype, D, BS)) return hipErrorInvalidValue;
-  const int64_t g64 = (int64_t)p.n_items * p.n_layers * p.Hkv;
-  if (g64 == 0) return hipSuccess;
-  if (g64 > 0x7fffffff) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)g64);
+  if (p.n_order == 0) return hipSuccess;
+  const dim3 grid((unsigned)p.n_order);
   if (mfma) {
     if (!lo_split) return hipErrorInvalidValue;  // only the split form is built
-    if (D == 64) return launch_mfma_d<64, true>(BS, p, grid, stream, ev);
-    if (D == 128) return launch_mfma_d<128, true>(BS, p, grid, stream, ev);
-    return launch_mfma_d<256, true>(BS, p, grid, stream, ev);
+    if (D == 64) return prefetch ? launch_mfma_d<64, true, true>(BS, p, grid, stream, ev)
+                                 : launch_mfma_d<64, true, false>(BS, p, grid, stream, ev);
+    if (D == 128) return prefetch ? launch_mfma_d<128, true, true>(BS, p, grid, stream, ev)
+                                  : launch_mfma_d<128, true, false>(BS, p, grid, stream, ev);
+    return prefetch ? launch_mfma_d<256, true, true>(BS, p, grid, stream, ev)
+                    : launch_mfma_d<256, true, false>(BS, p, grid, stream, ev);
   }
   if (dtype == 0) return launch_valu<float>(D, BS, p, grid, stream, ev);
   return launch_valu<uint16_t>(D, BS, p, grid, stream, ev);

@@ -56,10 +56,18 @@ hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t stream,
 // True if the (dtype, D, BS) combination has a compiled attention kernel.
 bool attn_supported(bool mfma, int dtype, int D, int BS);
 
-// One workgroup per (work item, layer, KV head): grid = n_items * n_layers * Hkv.
-// lo_split: P.V adds the bf16 rounding residual of P in a second product.
-hipError_t launch_attn(bool mfma, bool lo_split, int dtype, int D, int BS, const AttnParams& p,
-                       hipStream_t stream, const LaunchEvents& ev);
+// One workgroup per entry of p.order (grid = p.n_order), each one (work
+// item, layer, KV head). lo_split: P.V adds the bf16 rounding residual of P
+// in a second product (the only form built).
+// prefetch: each wave loads its next step while the current one computes.
+hipError_t launch_attn(bool mfma, bool lo_split, bool prefetch, int dtype, int D, int BS,
+                       const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
+
+// The wide-row matrix-core kernel (bf16), same grid convention. waves: 4
+// (two 16-row blocks per wave) or 8 (one); head_dim 256 always uses 8,
+// head_dim 64 always 4.
+hipError_t launch_attn_wide(int D, int BS, int waves, const AttnParams& p, hipStream_t stream,
+                            const LaunchEvents& ev);
 
 // max_entries: the longest per-branch list of partial states.
 hipError_t launch_combine(int D, int max_entries, const CombineParams& p, hipStream_t stream,

@@ -58,7 +58,9 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
       int32_t len = std::max(round_up(opt.min_chunk_tokens, step), round_up(base_len(s) / div, step));
       if (opt.chunk_tokens > 0) len = base_len(s);
       int64_t chunks = (s.n_tok + len - 1) / len;
-      int64_t items = (s.n_hold * G + rpi - 1) / rpi;
+      const int64_t rows = (int64_t)s.n_hold * G;
+      int64_t items = (opt.wide && rows > rpi) ? (rows + opt.wide_rows - 1) / opt.wide_rows
+                                               : (rows + rpi - 1) / rpi;
       w += chunks * items;
     }
     return w * n_layers * Hkv;
@@ -96,29 +98,95 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
     s.chunk_end = (int32_t)chunks.size();
   }
   S->n_chunks = (int32_t)chunks.size();
+  // narrow items: up to rpi rows; wide items (more rows than that): the
+  // rows split evenly in whole 16-row blocks, at most wide_rows each
+  std::vector<WorkItem> narrow;
+  std::vector<std::vector<WorkItem>> wide_groups;
   for (const Chunk& c : chunks) {
     const Segment& s = segs[c.seg];
     const int32_t rows = s.n_hold * G;
-    for (int32_t r0 = 0; r0 < rows; r0 += rpi) {
-      WorkItem w;
-      w.blk_off = c.blk_off;
-      w.n_tok = c.n_tok;
-      w.t0 = c.t0;
-      w.hold_off = s.hold_off;
-      w.r0 = r0;
-      w.n_rows = std::min(rpi, rows - r0);
-      w.part_row = c.part_base + r0;
-      w.mask_from = s.mask_from;
-      S->items.push_back(w);
+    WorkItem w{};
+    w.blk_off = c.blk_off;
+    w.n_tok = c.n_tok;
+    w.t0 = c.t0;
+    w.hold_off = s.hold_off;
+    w.mask_from = s.mask_from;
+    if (opt.wide && rows > rpi) {
+      // wide items of one chunk (siblings) read it through the shared L2
+      const int32_t k = (rows + opt.wide_rows - 1) / opt.wide_rows;
+      const int32_t per = round_up((rows + k - 1) / k, 16);
+      std::vector<WorkItem> grp;
+      w.reread = per < rows ? 1 : 0;
+      for (int32_t r0 = 0; r0 < rows; r0 += per) {
+        w.r0 = r0;
+        w.n_rows = std::min(per, rows - r0);
+        w.part_row = c.part_base + r0;
+        grp.push_back(w);
+      }
+      wide_groups.push_back(std::move(grp));
+    } else {
+      // a narrow item of more than 16 rows has two waves per step loading
+      // the same K/V; several items of one chunk read it again
+      for (int32_t r0 = 0; r0 < rows; r0 += rpi) {
+        w.r0 = r0;
+        w.n_rows = std::min(rpi, rows - r0);
+        w.part_row = c.part_base + r0;
+        w.reread = (rpi < rows || w.n_rows > 16) ? 1 : 0;
+        narrow.push_back(w);
+      }
     }
   }
-  // longest chunks first, so the tail of the grid holds the short ones
-  std::stable_sort(S->items.begin(), S->items.end(),
+  // longest chunks first, so the tail of each grid holds the short ones;
+  // wide groups also by sibling count, so equal counts sit together
+  std::stable_sort(narrow.begin(), narrow.end(),
                    [](const WorkItem& a, const WorkItem& b) { return a.n_tok > b.n_tok; });
+  std::stable_sort(wide_groups.begin(), wide_groups.end(),
+                   [](const std::vector<WorkItem>& a, const std::vector<WorkItem>& b) {
+                     if (a.size() != b.size()) return a.size() > b.size();
+                     return a[0].n_tok > b[0].n_tok;
+                   });
+  S->items = std::move(narrow);
+  S->n_narrow = (int32_t)S->items.size();
+  for (const auto& grp : wide_groups) S->items.insert(S->items.end(), grp.begin(), grp.end());
+  S->build_order(n_layers, Hkv);
   return chunks;
 }
 
 }  // namespace
+
+void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
+  const int32_t LH = n_layers * Hkv;
+  order.clear();
+  // narrow launch: item-major, all (layer, head) planes of an item together
+  for (int32_t i = 0; i < n_narrow; ++i)
+    for (int32_t lh = 0; lh < LH; ++lh) order.push_back(i * LH + lh);
+  n_order_narrow = (int32_t)order.size();
+  // wide launch: a unit is (sibling group, plane); the R siblings of a unit
+  // are placed 8 workgroups apart, so that with workgroups dealt round-robin
+  // to the 8 XCDs they share one XCD (and its L2) and start together
+  struct Unit {
+    int32_t first, R, lh;
+  };
+  std::vector<Unit> units;
+  for (int32_t i = n_narrow; i < (int32_t)items.size();) {
+    int32_t R = 1;
+    while (i + R < (int32_t)items.size() && items[i + R].blk_off == items[i].blk_off &&
+           items[i + R].r0 > items[i].r0)
+      ++R;
+    for (int32_t lh = 0; lh < LH; ++lh) units.push_back({i, R, lh});
+    i += R;
+  }
+  for (size_t u = 0; u < units.size();) {
+    const int32_t R = units[u].R;
+    size_t k = 0;
+    while (k < 8 && u + k < units.size() && units[u + k].R == R) ++k;
+    for (int32_t r = 0; r < R; ++r)
+      for (size_t j = 0; j < 8; ++j)
+        order.push_back(j < k ? (units[u + j].first + r) * LH + units[u + j].lh : -1);
+    u += k;
+  }
+  n_order_wide = (int32_t)order.size() - n_order_narrow;
+}
 
 void Schedule::layout(int Hkv, int D) {
   size_t o = 0;
@@ -134,6 +202,8 @@ void Schedule::layout(int Hkv, int D) {
   o = align256(o + comb_rows.size() * sizeof(int32_t));
   off_anc = o;
   o = align256(o + anc.size() * sizeof(uint64_t));
+  off_order = o;
+  o = align256(o + order.size() * sizeof(int32_t));
   meta_bytes = o;
   const size_t planes = (size_t)n_layers * Hkv;
   off_ml = o;
@@ -151,6 +221,7 @@ void Schedule::pack_meta(uint8_t* dst) const {
   std::memcpy(dst + off_comb_ptr, comb_ptr.data(), comb_ptr.size() * sizeof(int32_t));
   std::memcpy(dst + off_comb_rows, comb_rows.data(), comb_rows.size() * sizeof(int32_t));
   if (!anc.empty()) std::memcpy(dst + off_anc, anc.data(), anc.size() * sizeof(uint64_t));
+  if (!order.empty()) std::memcpy(dst + off_order, order.data(), order.size() * sizeof(int32_t));
 }
 
 void PlannerScratch::ensure(int nb) {

@@ -15,15 +15,21 @@ namespace pkv {
 
 struct SchedOptions {
   int32_t chunk_tokens = 0;        // 0 = automatic
-  int32_t rows_per_item = 64;      // matrix-core path; 16 for the VALU path
-  int32_t target_workgroups = 2048;
-  int32_t min_chunk_tokens = 256;
-  int32_t max_chunk_tokens = 4096;
+  int32_t rows_per_item = 32;      // narrow items (16 on the VALU path)
+  bool wide = true;                // chunks with more rows go to wide items
+  int32_t wide_rows = 128;         // rows per wide item at most
+  int32_t target_workgroups = 256;  // shorten chunks only to fill every CU once
+  int32_t min_chunk_tokens = 1024;
+  int32_t max_chunk_tokens = 8192;
   int32_t tokens_per_row = 40;     // chunk length per query row (keeps partial traffic ~5%)
 };
 
 struct Schedule {
-  std::vector<WorkItem> items;
+  std::vector<WorkItem> items;     // narrow items, then wide items
+  int32_t n_narrow = 0;
+  std::vector<int32_t> order;      // workgroup order: narrow launch, then wide launch
+  int32_t n_order_narrow = 0;
+  int32_t n_order_wide = 0;
   std::vector<int32_t> blk;
   std::vector<int32_t> holders;
   std::vector<int32_t> comb_ptr;
@@ -38,9 +44,11 @@ struct Schedule {
 
   // byte offsets inside the workspace
   size_t off_items = 0, off_blk = 0, off_holders = 0, off_comb_ptr = 0, off_comb_rows = 0,
-         off_anc = 0, meta_bytes = 0, off_ml = 0, off_acc = 0, total_bytes = 0;
+         off_anc = 0, off_order = 0, meta_bytes = 0, off_ml = 0, off_acc = 0, total_bytes = 0;
 
   void layout(int Hkv, int D);
+  // Fills `order` for n_layers x Hkv planes (items must be final).
+  void build_order(int32_t n_layers, int32_t Hkv);
   void pack_meta(uint8_t* dst) const;  // writes meta_bytes bytes
 };
 

@@ -60,14 +60,21 @@ SMALL_DECODE = [
            n_branches=3, branch_len=70),
     scaled("agent", "gqa1_d128_bs32", shape=replace_shape(AG, Hq=2, Hkv=2, D=128), root_len=33,
            n_branches=2, branch_len=1),
+    # more than 32 query rows share the root and the first edges: wide items
+    scaled("mcts", "mcts_wide", shape=replace_shape(B16, L=2, Hq=16, Hkv=2), root_len=77, depth=4,
+           edge_len=19),
+    scaled("beam", "beam_wide_d256", shape=replace_shape(AG, L=1, Hq=24, Hkv=2), root_len=150,
+           n_branches=9, branch_len=40),
 ]
 
 
-def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None):
+def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("path", path)
+    c.set_option("prefetch", prefetch)
     c.set_option("chunk_tokens", chunk_tokens)
+    c.set_option("wide", wide)
     if rows_per_item:
         c.set_option("rows_per_item", rows_per_item)
     seqs = [h[s] for s in w.query_sids]
@@ -85,11 +92,11 @@ def _lib(pkv):
 
 
 @pytest.mark.parametrize("w", SMALL_DECODE, ids=lambda w: w.name)
-@pytest.mark.parametrize("path,chunk", [(0, 0), (0, 64), (1, 0), (1, 64)],
-                         ids=["auto", "auto_split64", "valu", "valu_split64"])
-def test_decode_matches_oracle(w, path, chunk):
-    note(f"decode {w.name} path={path} chunk={chunk}")
-    inp, got = run_decode(w, path=path, chunk_tokens=chunk)
+@pytest.mark.parametrize("path,chunk,pf", [(0, 0, 0), (0, 64, 0), (0, 96, 1), (1, 0, 0), (1, 64, 0)],
+                         ids=["auto", "auto_split64", "prefetch_split96", "valu", "valu_split64"])
+def test_decode_matches_oracle(w, path, chunk, pf):
+    note(f"decode {w.name} path={path} chunk={chunk} prefetch={pf}")
+    inp, got = run_decode(w, path=path, chunk_tokens=chunk, prefetch=pf)
     pool = build_oracle(w, inp)
     want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
     check_close(got, want, f"{w.name} path={path} chunk={chunk}")
@@ -114,6 +121,19 @@ def test_split_and_row_grouping_agree(w):
         _, other = run_decode(w, chunk_tokens=chunk, rows_per_item=rpi)
         ma, _ = errors(other, base)
         assert ma <= 1e-4, (chunk, rpi, ma)
+
+
+@pytest.mark.parametrize("w", [SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
+def test_wide_and_narrow_items_agree(w):
+    """Rows of a chunk served by wide items (LDS-staged, two row blocks per
+    wave) or by narrow ones give the same result to fp32 rounding."""
+    note(f"wide/narrow {w.name}")
+    inp, wide = run_decode(w, wide=1)
+    _, narrow = run_decode(w, wide=0, rows_per_item=64)
+    ma, _ = errors(wide, narrow)
+    assert ma <= 1e-4, ma
+    _, chunked = run_decode(w, wide=1, chunk_tokens=32)
+    assert errors(chunked, wide)[0] <= 1e-4
 
 
 @pytest.mark.parametrize("name,keep_root", [("tiny_a", True), ("tiny_b", True), ("tiny_b", False)])
