@@ -248,7 +248,12 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  *   "wide"              1: chunks read by more rows use the wide-row kernel
  *   "wide_rows"         128: query rows a wide work item serves (16..128)
  *   "prefetch"          0: 1 makes each wave of the narrow kernel load its next
- *                       32-token step while the current one computes
+ *                       32-token step while the current one computes (with one
+ *                       16-row block per wave)
+ *   "row_blocks_per_wave" 1: 16-row blocks one wave of the narrow kernel may
+ *                       own, 1 or 2; with 2 (head_dim <= 128 only) an item of
+ *                       up to 32 rows loads each K/V step once, at the cost of
+ *                       occupancy
  *   "wide_waves"        8: waves per wide workgroup, 4 (two 16-row blocks each)
  *                       or 8 (one each); head_dim 256 always uses 8
  *   "target_workgroups" 256: chunks are shortened (down to 1024 tokens) until the

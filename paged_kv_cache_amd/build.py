@@ -7,7 +7,10 @@
 compiles csrc/*.hip and csrc/*.cpp with hipcc into objects under
 ``_build/`` and links them into ``paged_kv_cache_amd/libpkv.so``. All device
 code is built with ``-target-feature -packed-fp32-ops`` (no packed fp32
-arithmetic is generated).
+arithmetic is generated) and with the matrix-core instructions in their
+VGPR form (``-amdgpu-mfma-vgpr-form``): the attention kernels' accumulators
+then live in ordinary VGPRs instead of being copied between AGPRs and VGPRs
+around every online-softmax rescale, which frees registers for occupancy.
 """
 
 from __future__ import annotations
@@ -41,6 +44,7 @@ def compile_cmd(src: str, obj: str):
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
            "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form=1",
            "-Wall", "-Wno-unused-function", "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]

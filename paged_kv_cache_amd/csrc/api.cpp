@@ -307,6 +307,21 @@ bool use_mfma(const pkv_pool* p) {
   return attn_supported(true, d.kv_dtype, d.head_dim, d.block_size);
 }
 
+// The planner options for the kernel path in use.
+SchedOptions planner_options(const pkv_pool* p, bool mfma) {
+  SchedOptions o = p->opt;
+  if (!mfma) {
+    o.rows_per_item = std::min<int32_t>(o.rows_per_item, 16);
+    o.wide = false;
+    o.max_row_blocks_per_wave = 1;
+  } else {
+    o.max_row_blocks_per_wave = std::min(
+        o.max_row_blocks_per_wave, attn_max_row_blocks_per_wave(p->pool.desc().head_dim));
+    if (p->prefetch) o.max_row_blocks_per_wave = 1;
+  }
+  return o;
+}
+
 // Builds (or reuses) the decode schedule for these arguments.
 int decode_schedule(pkv_pool* p, const pkv_seq* seqs, int32_t n, int32_t layer0, int32_t n_layers) {
   const bool mfma = use_mfma(p);
@@ -316,11 +331,7 @@ int decode_schedule(pkv_pool* p, const pkv_seq* seqs, int32_t n, int32_t layer0,
       std::memcmp(p->cache_seqs.data(), seqs, sizeof(pkv_seq) * n) == 0)
     return PKV_OK;
   p->cache_valid = false;
-  SchedOptions o = p->opt;
-  if (!mfma) {
-    o.rows_per_item = std::min<int32_t>(o.rows_per_item, 16);
-    o.wide = false;
-  }
+  const SchedOptions o = planner_options(p, mfma);
   int rc = build_decode_schedule(p->pool, seqs, n, n_layers, layer0, o, &p->scratch, &p->sched);
   if (rc) return rc;
   p->cache_valid = true;
@@ -343,7 +354,8 @@ int verify_schedule(pkv_pool* p, const pkv_seq* reqs, int32_t n_req, const int32
       std::memcmp(p->cache_parents.data(), parents, np * sizeof(int32_t)) == 0)
     return PKV_OK;
   p->cache_valid = false;
-  int rc = build_verify_schedule(p->pool, reqs, n_req, parents, n_nodes, p->opt, &p->sched);
+  int rc = build_verify_schedule(p->pool, reqs, n_req, parents, n_nodes, planner_options(p, true),
+                                 &p->sched);
   if (rc) return rc;
   p->cache_valid = true;
   p->cache_kind = 1;
@@ -396,8 +408,8 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
     rc = p->timed(
         T_ATTN,
         [&](const LaunchEvents& ev) {
-          return launch_attn(mfma, lo_split, p->prefetch != 0, d.kv_dtype, d.head_dim, d.block_size,
-                             a, stream, ev);
+          return launch_attn(mfma, lo_split, p->prefetch != 0, S.narrow_rw, d.kv_dtype,
+                             d.head_dim, d.block_size, a, stream, ev);
         },
         "attention launch");
     if (rc) return rc;
@@ -749,6 +761,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "prefetch") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "prefetch must be 0 or 1");
     pool->prefetch = (int)value;
+  } else if (k == "row_blocks_per_wave") {
+    if (value < 1 || value > 2) return fail(PKV_E_INVALID, "row_blocks_per_wave must be 1 or 2");
+    pool->opt.max_row_blocks_per_wave = (int32_t)value;
   } else if (k == "wide_waves") {
     if (value != 4 && value != 8) return fail(PKV_E_INVALID, "wide_waves must be 4 or 8");
     pool->wide_waves = (int)value;

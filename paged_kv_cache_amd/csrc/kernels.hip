@@ -210,15 +210,17 @@ __device__ __forceinline__ void rebase(float mx, float& m_ref, float& l_run, f32
   }
 }
 
-template <int D, int BS, bool LO, bool PF>
+template <int D, int BS, bool LO, bool PF, int RW>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   constexpr int KS = D / 32;  // 32-wide k steps of Q.K
   constexpr int DB = D / 16;  // 16-wide d blocks of P.V
   constexpr int ACC_STRIDE = D + 4;
+  constexpr int SLOTS = 3 * RW;
   static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
-  __shared__ float mrg_m[3][16];
-  __shared__ float mrg_l[3][16];
-  __shared__ float mrg_acc[3][16 * ACC_STRIDE];
+  static_assert(RW == 1 || (RW == 2 && !PF), "row blocks per wave");
+  __shared__ float mrg_m[SLOTS][16];
+  __shared__ float mrg_l[SLOTS][16];
+  __shared__ float mrg_acc[SLOTS][16 * ACC_STRIDE];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -233,32 +235,38 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int layer = p.layer0 + li;
   const WorkItem it = p.items[item_idx];
 
+  // row blocks of 16 rows; a wave owns RW consecutive blocks (a row group)
   const int RB = (it.n_rows + 15) >> 4;
-  const int RBp = RB == 1 ? 1 : (RB == 2 ? 2 : 4);
-  const int phases = 4 / RBp;
-  const int rb = wave % RBp, phase = wave / RBp;
-  const bool active = rb < RB;
-  const int row = rb * 16 + n;
-  const bool row_ok = active && row < it.n_rows;
-  const int crow = it.r0 + row;
-  const int hold = crow / p.G;
-  const int gq = crow - hold * p.G;
-  const int branch = row_ok ? p.holders[it.hold_off + hold] : 0;
-  const int qh = kvh * p.G + gq;
+  const int RG = (RB + RW - 1) / RW;
+  const int RGp = RG == 1 ? 1 : (RG == 2 ? 2 : 4);
+  const int phases = 4 / RGp;
+  const int rg = wave % RGp, phase = wave / RGp;
+  const bool active = rg < RG;
+  const int nblk = active ? min(RW, RB - rg * RW) : 0;  // wave-uniform
 
-  bf16x8 qv[KS];
-  {
+  bf16x8 qv[RW][KS];
+  bool row_ok[RW];
+  uint64_t anc[RW];
+  const bool tree = it.mask_from != 0x7fffffff && it.t0 + it.n_tok > it.mask_from;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = (rg * RW + r) * 16 + n;
+    row_ok[r] = r < nblk && row < it.n_rows;
+    const int crow = it.r0 + row;
+    const int hold = crow / p.G;
+    const int gq = crow - hold * p.G;
+    const int branch = row_ok[r] ? p.holders[it.hold_off + hold] : 0;
+    const int qh = kvh * p.G + gq;
     const uint16_t* qp =
         (const uint16_t*)p.q + (((int64_t)li * p.n_branch + branch) * p.Hq + qh) * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (row_ok) raw = ld16(qp + 32 * ks);
-      qv[ks] = as_bf16x8(raw);
+      if (row_ok[r]) raw = ld16(qp + 32 * ks);
+      qv[r][ks] = as_bf16x8(raw);
     }
+    anc[r] = (tree && row_ok[r]) ? p.anc[branch] : ~0ull;
   }
-  const bool tree = it.mask_from != 0x7fffffff && it.t0 + it.n_tok > it.mask_from;
-  const uint64_t anc = (tree && row_ok) ? p.anc[branch] : ~0ull;
 
   const uint16_t* K = (const uint16_t*)p.k_arena;
   const uint16_t* V = (const uint16_t*)p.v_arena;
@@ -272,10 +280,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int voff = 8 * g;
   const bool v_in_b = BS == 16 && voff >= 16;
 
-  f32x4 acc[DB];
+  f32x4 acc[RW][DB];
+  float m_run[RW], l_run[RW];
 #pragma unroll
-  for (int j = 0; j < DB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
+  for (int r = 0; r < RW; ++r) {
+#pragma unroll
+    for (int j = 0; j < DB; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[r] = kNegInf;
+    l_run[r] = 0.f;
+  }
   const int n_steps = (it.n_tok + 31) >> 5;
 
   // K rows of this lane (both S^T tiles) and V^T columns of step s
@@ -299,31 +312,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   };
   auto compute = [&](int s, const u32x4 (&kraw)[2][KS], u32x4 (&vraw)[DB]) {
     const int tbase = s * 32;
-    f32x4 st[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) c = mfma_bf16(as_bf16x8(kraw[tau][ks]), qv[ks], c);
-      st[tau] = c;
-    }
     const bool tail = tbase + 32 > it.n_tok;
     const int tv = tbase + voff;
-    float sc[8];
-#pragma unroll
-    for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * tau + i;
-        const int t = tv + e;
-        float v = st[tau][i] * p.scale_log2;
-        if (tail && t >= it.n_tok) v = kNegInf;
-        if (tree) {
-          const int pos = it.t0 + t;
-          if (pos >= it.mask_from && !((anc >> (pos - it.mask_from)) & 1ull)) v = kNegInf;
-        }
-        sc[e] = v;
-      }
     if (tail) {
       // slots past the chunk may hold anything (even NaN): zero them so
       // that 0 * V stays 0 in the P.V product
@@ -337,27 +327,57 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
       for (int j = 0; j < DB; ++j) vraw[j] &= keep;
     }
-    float mx = sc[0];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-    mx = max_xor32(max_xor16(mx));
-    rebase(mx, m_run, l_run, acc);
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    float psum = 0.f;
-    bf16x8 phi, plo;
+    for (int r = 0; r < RW; ++r) {
+      if (r > 0 && r >= nblk) continue;
+      f32x4 st[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float pe = fast_exp2(sc[e] - m_use);
-      psum += pe;
-      const __bf16 h = (__bf16)pe;
-      phi[e] = h;
-      if (LO) plo[e] = (__bf16)(pe - (float)h);
-    }
-    l_run += psum;
+      for (int tau = 0; tau < 2; ++tau) {
+        f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      acc[j] = mfma_bf16(as_bf16x8(vraw[j]), phi, acc[j]);
-      if (LO) acc[j] = mfma_bf16(as_bf16x8(vraw[j]), plo, acc[j]);
+        for (int ks = 0; ks < KS; ++ks) c = mfma_bf16(as_bf16x8(kraw[tau][ks]), qv[r][ks], c);
+        st[tau] = c;
+      }
+      float sc[8];
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * tau + i;
+          const int t = tv + e;
+          float v = st[tau][i] * p.scale_log2;
+          if (tail && t >= it.n_tok) v = kNegInf;
+          if (tree) {
+            const int pos = it.t0 + t;
+            if (pos >= it.mask_from && !((anc[r] >> (pos - it.mask_from)) & 1ull)) v = kNegInf;
+          }
+          sc[e] = v;
+        }
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+      mx = max_xor32(max_xor16(mx));
+      rebase(mx, m_run[r], l_run[r], acc[r]);
+      const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
+      float psum = 0.f;
+      bf16x8 phi, plo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pe = fast_exp2(sc[e] - m_use);
+        psum += pe;
+        const __bf16 h = (__bf16)pe;
+        phi[e] = h;
+        if (LO) plo[e] = (__bf16)(pe - (float)h);
+      }
+      l_run[r] += psum;
+#pragma unroll
+      for (int j = 0; j < DB; ++j) {
+        acc[r][j] = mfma_bf16(as_bf16x8(vraw[j]), phi, acc[r][j]);
+        if (LO) acc[r][j] = mfma_bf16(as_bf16x8(vraw[j]), plo, acc[r][j]);
+      }
+      // one row block at a time: interleaving the two would keep both
+      // blocks' scores and probabilities live
+      if (RW > 1) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -404,48 +424,62 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     }
   }
   // the four lane groups hold disjoint tokens of the same rows
-  const float l_tot = sum_xor32(sum_xor16(l_run));
-  float l_fin = l_tot;
+  float l_fin[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) l_fin[r] = sum_xor32(sum_xor16(l_run[r]));
 
   if (phases > 1) {
-    if (phase > 0 && active) {
-      const int slot = (phase - 1) * RBp + rb;
-      if (g == 0) {
-        mrg_m[slot][n] = m_run;
-        mrg_l[slot][n] = l_tot;
-      }
+    if (phase > 0) {
 #pragma unroll
-      for (int j = 0; j < DB; ++j)
-        *(f32x4*)&mrg_acc[slot][n * ACC_STRIDE + 16 * j + 4 * g] = acc[j];
+      for (int r = 0; r < RW; ++r) {
+        if (r > 0 && r >= nblk) continue;
+        const int slot = ((phase - 1) * RGp + rg) * RW + r;
+        if (g == 0) {
+          mrg_m[slot][n] = m_run[r];
+          mrg_l[slot][n] = l_fin[r];
+        }
+#pragma unroll
+        for (int j = 0; j < DB; ++j)
+          *(f32x4*)&mrg_acc[slot][n * ACC_STRIDE + 16 * j + 4 * g] = acc[r][j];
+      }
     }
     __syncthreads();
-    if (phase == 0 && active) {
-      for (int ph = 1; ph < phases; ++ph) {
-        const int slot = (ph - 1) * RBp + rb;
-        const float mo = mrg_m[slot][n], lo = mrg_l[slot][n];
-        const float M = fmaxf(m_run, mo);
-        if (M != kNegInf) {
-          const float a = fast_exp2(m_run - M), b = fast_exp2(mo - M);
-          l_fin = l_fin * a + lo * b;
+    if (phase == 0) {
 #pragma unroll
-          for (int j = 0; j < DB; ++j) {
-            const f32x4 o = *(const f32x4*)&mrg_acc[slot][n * ACC_STRIDE + 16 * j + 4 * g];
-            acc[j] = acc[j] * a + o * b;
+      for (int r = 0; r < RW; ++r) {
+        if (r > 0 && r >= nblk) continue;
+        for (int ph = 1; ph < phases; ++ph) {
+          const int slot = ((ph - 1) * RGp + rg) * RW + r;
+          const float mo = mrg_m[slot][n], lo = mrg_l[slot][n];
+          const float M = fmaxf(m_run[r], mo);
+          if (M != kNegInf) {
+            const float a = fast_exp2(m_run[r] - M), b = fast_exp2(mo - M);
+            l_fin[r] = l_fin[r] * a + lo * b;
+#pragma unroll
+            for (int j = 0; j < DB; ++j) {
+              const f32x4 o = *(const f32x4*)&mrg_acc[slot][n * ACC_STRIDE + 16 * j + 4 * g];
+              acc[r][j] = acc[r][j] * a + o * b;
+            }
+            m_run[r] = M;
           }
-          m_run = M;
         }
       }
     }
   }
-  if (phase == 0 && row_ok) {
-    const int64_t prow = (int64_t)(li * p.Hkv + kvh) * p.P + it.part_row + row;
-    if (g == 0) {
-      p.part_ml[2 * prow] = m_run;
-      p.part_ml[2 * prow + 1] = l_fin;
-    }
-    float* pa = p.part_acc + prow * D;
+  if (phase == 0) {
 #pragma unroll
-    for (int j = 0; j < DB; ++j) *(f32x4*)(pa + 16 * j + 4 * g) = acc[j];
+    for (int r = 0; r < RW; ++r) {
+      if (!row_ok[r]) continue;
+      const int row = (rg * RW + r) * 16 + n;
+      const int64_t prow = (int64_t)(li * p.Hkv + kvh) * p.P + it.part_row + row;
+      if (g == 0) {
+        p.part_ml[2 * prow] = m_run[r];
+        p.part_ml[2 * prow + 1] = l_fin[r];
+      }
+      float* pa = p.part_acc + prow * D;
+#pragma unroll
+      for (int j = 0; j < DB; ++j) *(f32x4*)(pa + 16 * j + 4 * g) = acc[r][j];
+    }
   }
 }
 
@@ -985,12 +1019,12 @@ bool attn_supported(bool mfma, int dtype, int D, int BS) {
 
 namespace {
 
-template <int D, bool LO, bool PF>
+template <int D, bool LO, bool PF, int RW>
 hipError_t launch_mfma_d(int BS, const AttnParams& p, dim3 grid, hipStream_t s, const LaunchEvents& ev) {
   switch (BS) {
-    case 16: return launch(attn_mfma_kernel<D, 16, LO, PF>, grid, dim3(256), s, ev, p);
-    case 32: return launch(attn_mfma_kernel<D, 32, LO, PF>, grid, dim3(256), s, ev, p);
-    default: return launch(attn_mfma_kernel<D, 64, LO, PF>, grid, dim3(256), s, ev, p);
+    case 16: return launch(attn_mfma_kernel<D, 16, LO, PF, RW>, grid, dim3(256), s, ev, p);
+    case 32: return launch(attn_mfma_kernel<D, 32, LO, PF, RW>, grid, dim3(256), s, ev, p);
+    default: return launch(attn_mfma_kernel<D, 64, LO, PF, RW>, grid, dim3(256), s, ev, p);
   }
 }
 
@@ -1034,19 +1068,28 @@ hipError_t launch_attn_wide(int D, int BS, int waves, const AttnParams& p, hipSt
 #undef PKV_WIDE
 }
 
-hipError_t launch_attn(bool mfma, bool lo_split, bool prefetch, int dtype, int D, int BS,
-                       const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
+int attn_max_row_blocks_per_wave(int D) { return D <= 128 ? 2 : 1; }
+
+hipError_t launch_attn(bool mfma, bool lo_split, bool prefetch, int row_blocks_per_wave, int dtype,
+                       int D, int BS, const AttnParams& p, hipStream_t stream,
+                       const LaunchEvents& ev) {
   if (!attn_supported(mfma, dtype, D, BS)) return hipErrorInvalidValue;
   if (p.n_order == 0) return hipSuccess;
   const dim3 grid((unsigned)p.n_order);
   if (mfma) {
     if (!lo_split) return hipErrorInvalidValue;  // only the split form is built
-    if (D == 64) return prefetch ? launch_mfma_d<64, true, true>(BS, p, grid, stream, ev)
-                                 : launch_mfma_d<64, true, false>(BS, p, grid, stream, ev);
-    if (D == 128) return prefetch ? launch_mfma_d<128, true, true>(BS, p, grid, stream, ev)
-                                  : launch_mfma_d<128, true, false>(BS, p, grid, stream, ev);
-    return prefetch ? launch_mfma_d<256, true, true>(BS, p, grid, stream, ev)
-                    : launch_mfma_d<256, true, false>(BS, p, grid, stream, ev);
+    if (row_blocks_per_wave == 2) {
+      if (D == 64) return launch_mfma_d<64, true, false, 2>(BS, p, grid, stream, ev);
+      if (D == 128) return launch_mfma_d<128, true, false, 2>(BS, p, grid, stream, ev);
+      return hipErrorInvalidValue;
+    }
+    if (row_blocks_per_wave != 1) return hipErrorInvalidValue;
+    if (D == 64) return prefetch ? launch_mfma_d<64, true, true, 1>(BS, p, grid, stream, ev)
+                                 : launch_mfma_d<64, true, false, 1>(BS, p, grid, stream, ev);
+    if (D == 128) return prefetch ? launch_mfma_d<128, true, true, 1>(BS, p, grid, stream, ev)
+                                  : launch_mfma_d<128, true, false, 1>(BS, p, grid, stream, ev);
+    return prefetch ? launch_mfma_d<256, true, true, 1>(BS, p, grid, stream, ev)
+                    : launch_mfma_d<256, true, false, 1>(BS, p, grid, stream, ev);
   }
   if (dtype == 0) return launch_valu<float>(D, BS, p, grid, stream, ev);
   return launch_valu<uint16_t>(D, BS, p, grid, stream, ev);

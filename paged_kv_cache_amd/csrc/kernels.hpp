@@ -59,9 +59,16 @@ bool attn_supported(bool mfma, int dtype, int D, int BS);
 // One workgroup per entry of p.order (grid = p.n_order), each one (work
 // item, layer, KV head). lo_split: P.V adds the bf16 rounding residual of P
 // in a second product (the only form built).
-// prefetch: each wave loads its next step while the current one computes.
-hipError_t launch_attn(bool mfma, bool lo_split, bool prefetch, int dtype, int D, int BS,
-                       const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
+// prefetch: each wave loads its next step while the current one computes
+// (one row block per wave only). row_blocks_per_wave: 16-row blocks each
+// wave of the matrix-core kernel owns, 1 or 2 (2 for D <= 128 only).
+hipError_t launch_attn(bool mfma, bool lo_split, bool prefetch, int row_blocks_per_wave, int dtype,
+                       int D, int BS, const AttnParams& p, hipStream_t stream,
+                       const LaunchEvents& ev);
+
+// The most 16-row blocks one wave of the matrix-core kernel can own at
+// this head size.
+int attn_max_row_blocks_per_wave(int D);
 
 // The wide-row matrix-core kernel (bf16), same grid convention. waves: 4
 // (two 16-row blocks per wave) or 8 (one); head_dim 256 always uses 8,

@@ -125,17 +125,25 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
       }
       wide_groups.push_back(std::move(grp));
     } else {
-      // a narrow item of more than 16 rows has two waves per step loading
-      // the same K/V; several items of one chunk read it again
+      // several items of one chunk each read it (the rows of one item
+      // more than one wave owns are marked below)
       for (int32_t r0 = 0; r0 < rows; r0 += rpi) {
         w.r0 = r0;
         w.n_rows = std::min(rpi, rows - r0);
         w.part_row = c.part_base + r0;
-        w.reread = (rpi < rows || w.n_rows > 16) ? 1 : 0;
+        w.reread = rpi < rows ? 1 : 0;
         narrow.push_back(w);
       }
     }
   }
+  // a narrow wave owns two 16-row blocks when some item has more than 16
+  // rows (and the head size leaves the registers for it); an item with
+  // more rows than one wave owns has several waves loading each step
+  int32_t max_rows = 0;
+  for (const WorkItem& w : narrow) max_rows = std::max(max_rows, w.n_rows);
+  S->narrow_rw = (max_rows > 16 && opt.max_row_blocks_per_wave >= 2) ? 2 : 1;
+  for (WorkItem& w : narrow)
+    if (w.n_rows > 16 * S->narrow_rw) w.reread = 1;
   // longest chunks first, so the tail of each grid holds the short ones;
   // wide groups also by sibling count, so equal counts sit together
   std::stable_sort(narrow.begin(), narrow.end(),

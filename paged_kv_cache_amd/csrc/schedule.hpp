@@ -22,11 +22,13 @@ struct SchedOptions {
   int32_t min_chunk_tokens = 1024;
   int32_t max_chunk_tokens = 8192;
   int32_t tokens_per_row = 40;     // chunk length per query row (keeps partial traffic ~5%)
+  int32_t max_row_blocks_per_wave = 1;  // 16-row blocks one narrow wave may own (1 or 2)
 };
 
 struct Schedule {
   std::vector<WorkItem> items;     // narrow items, then wide items
   int32_t n_narrow = 0;
+  int32_t narrow_rw = 1;           // 16-row blocks per wave in the narrow launch
   std::vector<int32_t> order;      // workgroup order: narrow launch, then wide launch
   int32_t n_order_narrow = 0;
   int32_t n_order_wide = 0;

@@ -68,11 +68,13 @@ SMALL_DECODE = [
 ]
 
 
-def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0):
+def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
+               row_blocks=1):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("path", path)
     c.set_option("prefetch", prefetch)
+    c.set_option("row_blocks_per_wave", row_blocks)
     c.set_option("chunk_tokens", chunk_tokens)
     c.set_option("wide", wide)
     if rows_per_item:
@@ -92,11 +94,13 @@ def _lib(pkv):
 
 
 @pytest.mark.parametrize("w", SMALL_DECODE, ids=lambda w: w.name)
-@pytest.mark.parametrize("path,chunk,pf", [(0, 0, 0), (0, 64, 0), (0, 96, 1), (1, 0, 0), (1, 64, 0)],
-                         ids=["auto", "auto_split64", "prefetch_split96", "valu", "valu_split64"])
-def test_decode_matches_oracle(w, path, chunk, pf):
-    note(f"decode {w.name} path={path} chunk={chunk} prefetch={pf}")
-    inp, got = run_decode(w, path=path, chunk_tokens=chunk, prefetch=pf)
+@pytest.mark.parametrize("path,chunk,pf,rbw", [(0, 0, 0, 1), (0, 64, 0, 1), (0, 0, 0, 2), (0, 96, 1, 1),
+                                              (1, 0, 0, 1), (1, 64, 0, 1)],
+                         ids=["auto", "auto_split64", "two_blocks_per_wave", "prefetch_split96", "valu",
+                              "valu_split64"])
+def test_decode_matches_oracle(w, path, chunk, pf, rbw):
+    note(f"decode {w.name} path={path} chunk={chunk} prefetch={pf} row_blocks={rbw}")
+    inp, got = run_decode(w, path=path, chunk_tokens=chunk, prefetch=pf, row_blocks=rbw)
     pool = build_oracle(w, inp)
     want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
     check_close(got, want, f"{w.name} path={path} chunk={chunk}")
@@ -117,10 +121,10 @@ def test_page_layout_does_not_change_output(w):
 def test_split_and_row_grouping_agree(w):
     note(f"splits {w.name}")
     inp, base = run_decode(w)
-    for chunk, rpi in [(32, None), (96, 16), (0, 8), (0, 48)]:
-        _, other = run_decode(w, chunk_tokens=chunk, rows_per_item=rpi)
+    for chunk, rpi, rbw in [(32, None, 1), (96, 16, 1), (0, 8, 1), (0, 48, 1), (0, 48, 2), (0, 64, 2)]:
+        _, other = run_decode(w, chunk_tokens=chunk, rows_per_item=rpi, row_blocks=rbw)
         ma, _ = errors(other, base)
-        assert ma <= 1e-4, (chunk, rpi, ma)
+        assert ma <= 1e-4, (chunk, rpi, rbw, ma)
 
 
 @pytest.mark.parametrize("w", [SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
