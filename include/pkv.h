@@ -246,7 +246,8 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  *   "chunk_tokens"      0 automatic: tokens per chunk of a shared segment
  *   "rows_per_item"     32: query rows a narrow work item serves (1..64)
  *   "wide"              1: chunks read by more rows use the wide-row kernel
- *   "wide_rows"         128: query rows a wide work item serves (16..128)
+ *   "wide_rows"         256: query rows a wide work item serves at most (16..256;
+ *                       never more than one wide workgroup serves)
  *   "prefetch"          0: 1 makes each wave of the narrow kernel load its next
  *                       32-token step while the current one computes (with one
  *                       16-row block per wave)
@@ -254,10 +255,14 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  *                       own, 1 or 2; with 2 (head_dim <= 128 only) an item of
  *                       up to 32 rows loads each K/V step once, at the cost of
  *                       occupancy
- *   "wide_waves"        8: waves per wide workgroup, 4 (two 16-row blocks each)
- *                       or 8 (one each); head_dim 256 always uses 8
- *   "target_workgroups" 256: chunks are shortened (down to 1024 tokens) until the
- *                       grid has this many workgroups
+ *   "wide_waves"        0: compute waves per wide workgroup, 4, 6 or 8; 0 picks 8
+ *                       (the workgroup adds one or two loader waves)
+ *   "wide_row_blocks"   0: 16-row blocks each wide compute wave owns, 1 or 2; 0
+ *                       picks 2 up to head_dim 128 and 1 at 256 (6 waves, and 8
+ *                       at head_dim 256, always own one); a wide item holds at
+ *                       most 16 * waves * row blocks rows
+ *   "target_workgroups" 256: chunks are shortened (down to 1024 tokens) while the
+ *                       grid has fewer than 3/4 of this many workgroups
  *   "timing"            0: 1 records a pair of HIP events at the start and end
  *                       of every kernel the pool launches (pkv_timing_read)
  * Unknown keys or out-of-range values are PKV_E_INVALID. */

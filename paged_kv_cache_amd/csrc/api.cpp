@@ -108,7 +108,8 @@ struct pkv_pool {
   PlannerScratch scratch;
   SchedOptions opt;
   int path = 0;  // 0 auto, 1 VALU, 2 matrix cores
-  int wide_waves = 8;  // waves per wide workgroup (4 or 8)
+  int wide_waves = 0;  // compute waves per wide workgroup (4, 6, 8; 0 automatic)
+  int wide_row_blocks = 0;  // 16-row blocks per wave of the wide kernel (1, 2; 0 automatic)
   int prefetch = 0;    // narrow matrix-core kernel loads one step ahead
 
   // schedule cache
@@ -318,6 +319,10 @@ SchedOptions planner_options(const pkv_pool* p, bool mfma) {
     o.max_row_blocks_per_wave = std::min(
         o.max_row_blocks_per_wave, attn_max_row_blocks_per_wave(p->pool.desc().head_dim));
     if (p->prefetch) o.max_row_blocks_per_wave = 1;
+    // a wide item holds at most what one workgroup of the wide kernel serves
+    int w = p->wide_waves, r = p->wide_row_blocks;
+    attn_wide_shape(p->pool.desc().head_dim, &w, &r);
+    o.wide_rows = std::min<int32_t>(o.wide_rows, 16 * w * r);
   }
   return o;
 }
@@ -421,7 +426,9 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
     rc = p->timed(
         T_WIDE,
         [&](const LaunchEvents& ev) {
-          return launch_attn_wide(d.head_dim, d.block_size, p->wide_waves, aw, stream, ev);
+          int w = p->wide_waves, r = p->wide_row_blocks;
+          attn_wide_shape(d.head_dim, &w, &r);
+          return launch_attn_wide(d.head_dim, d.block_size, w, r, aw, stream, ev);
         },
         "wide attention launch");
     if (rc) return rc;
@@ -718,7 +725,8 @@ int pkv_verify_workspace_size(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req
   std::vector<int32_t> chain(np);
   for (size_t i = 0; i < np; ++i) chain[i] = (int32_t)(i % n_nodes) - 1;
   Schedule s;
-  int rc = build_verify_schedule(pool->pool, reqs, n_req, chain.data(), n_nodes, pool->opt, &s);
+  int rc = build_verify_schedule(pool->pool, reqs, n_req, chain.data(), n_nodes,
+                                 planner_options(pool, true), &s);
   if (rc) return rc;
   *bytes = s.total_bytes;
   return PKV_OK;
@@ -765,10 +773,15 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
     if (value < 1 || value > 2) return fail(PKV_E_INVALID, "row_blocks_per_wave must be 1 or 2");
     pool->opt.max_row_blocks_per_wave = (int32_t)value;
   } else if (k == "wide_waves") {
-    if (value != 4 && value != 8) return fail(PKV_E_INVALID, "wide_waves must be 4 or 8");
+    if (value != 0 && value != 4 && value != 6 && value != 8)
+      return fail(PKV_E_INVALID, "wide_waves must be 0 (automatic), 4, 6 or 8");
     pool->wide_waves = (int)value;
+  } else if (k == "wide_row_blocks") {
+    if (value < 0 || value > 2)
+      return fail(PKV_E_INVALID, "wide_row_blocks must be 0 (automatic), 1 or 2");
+    pool->wide_row_blocks = (int)value;
   } else if (k == "wide_rows") {
-    if (value < 16 || value > 128) return fail(PKV_E_INVALID, "wide_rows must be 16..128");
+    if (value < 16 || value > 256) return fail(PKV_E_INVALID, "wide_rows must be 16..256");
     pool->opt.wide_rows = (int32_t)value;
   } else if (k == "timing") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "timing must be 0 or 1");

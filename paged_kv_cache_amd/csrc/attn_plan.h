@@ -16,6 +16,10 @@
 
 namespace pkv {
 
+// Most blocks one chunk may span: the matrix-core kernels copy a chunk's
+// block ids to LDS.
+constexpr int32_t kMaxChunkBlocks = 512;
+
 struct WorkItem {
   int32_t blk_off;    // index in blk[] of the chunk's first block
   int32_t n_tok;      // valid tokens in the chunk (> 0)

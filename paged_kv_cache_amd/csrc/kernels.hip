@@ -210,6 +210,20 @@ __device__ __forceinline__ void rebase(float mx, float& m_ref, float& l_run, f32
   }
 }
 
+// A chunk's block ids are copied to LDS when the workgroup starts (at most
+// kMaxChunkBlocks of them; the planner cuts chunks to fit) and read from
+// there at wave-uniform indexes. Read from global memory as each step
+// needs them, they would be vector loads (the compiler cannot prove the
+// table unwritten, so it does not use the scalar cache) with a wait in
+// front of every step, and that wait would also drain the K/V loads
+// already in flight.
+template <int BS>
+__device__ __forceinline__ int stage_block_ids(int32_t* dst, const int32_t* blk, int n_steps) {
+  const int nbk = (32 * n_steps + BS - 1) / BS;
+  for (int i = threadIdx.x; i < nbk; i += blockDim.x) dst[i] = blk[i];
+  return nbk;
+}
+
 template <int D, int BS, bool LO, bool PF, int RW>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   constexpr int KS = D / 32;  // 32-wide k steps of Q.K
@@ -290,6 +304,15 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     l_run[r] = 0.f;
   }
   const int n_steps = (it.n_tok + 31) >> 5;
+  // With prefetch the block ids come from LDS (see stage_block_ids); a
+  // wave that loads one step at a time reads them from global memory one
+  // step ahead, which costs no extra wait and spares short items the
+  // staging round trip.
+  __shared__ int32_t blk_s[PF ? kMaxChunkBlocks : 1];
+  if (PF) {
+    stage_block_ids<BS>(blk_s, blk, n_steps);
+    __syncthreads();
+  }
 
   // K rows of this lane (both S^T tiles) and V^T columns of step s
   const bool stream_kv = it.reread == 0;
@@ -382,10 +405,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   };
 
   if (active && phase < n_steps) {
-    // block ids are wave-uniform (scalar loads)
     auto ids = [&](int s, int& a, int& b) {
-      a = blk[(32 * s) / BS];
-      b = blk[(32 * s + 16) / BS];
+      const int32_t* src = PF ? blk_s : blk;
+      a = src[(32 * s) / BS];
+      b = src[(32 * s + 16) / BS];
     };
     if (!PF) {
       int bA, bB;
@@ -400,24 +423,24 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     } else {
       // loads of the wave's next step are in flight while this one computes
       // (two register sets, loop unrolled by two)
+      // (the prefetch is unconditional, re-reading the last step past the
+      // end, so that the compiler's wait before each step's math counts
+      // only that step's loads)
+      const int last = n_steps - 1;
       u32x4 ka[2][KS], va[DB], kb[2][KS], vb[DB];
       int bA, bB;
       ids(phase, bA, bB);
       load_kv(phase, bA, bB, ka, va);
       for (int s = phase; s < n_steps; s += 2 * phases) {
         const int s1 = s + phases;
-        if (s1 < n_steps) {
-          ids(s1, bA, bB);
-          load_kv(s1, bA, bB, kb, vb);
-        }
+        ids(min(s1, last), bA, bB);
+        load_kv(min(s1, last), bA, bB, kb, vb);
         __builtin_amdgcn_sched_barrier(0);
         compute(s, ka, va);
         if (s1 >= n_steps) break;
-        const int s2 = s1 + phases;
-        if (s2 < n_steps) {
-          ids(s2, bA, bB);
-          load_kv(s2, bA, bB, ka, va);
-        }
+        const int s2 = min(s1 + phases, last);
+        ids(s2, bA, bB);
+        load_kv(s2, bA, bB, ka, va);
         __builtin_amdgcn_sched_barrier(0);
         compute(s1, kb, vb);
       }
@@ -486,32 +509,39 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
 // ------------------------------------------------- wide MFMA attention
 //
 // For chunks read by many query rows (draft-tree verify: nodes x GQA group;
-// the shared root of a wide tree). One workgroup serves up to 128
-// rows: NW waves, wave w owns row blocks w + NW * r for r < RBW (4 waves x
-// 2 blocks up to D = 128; 8 waves x 1 block at D = 256, where two blocks'
-// accumulators and queries would not fit one wave's registers). Each
-// 32-token step of K/V is loaded once by the whole workgroup into LDS,
-// already in operand order:
-// 1 KiB section per (K tile, k step) and per V d block, lane l's 16 bytes at
-// l * 16, so every operand read is a conflict-free ds_read_b128 and each
-// wave applies it to all of its row blocks. Loads run two steps ahead of
-// the math (two register sets, two LDS buffers). Math per row block is the
-// narrow kernel's.
+// the shared root of a wide tree). One workgroup serves up to 16 * NC * RBW
+// rows with NC compute waves (wave w owns row blocks w + NC * r, r < RBW)
+// and NP loader waves. Each 32-token step of K/V is loaded once for the
+// whole workgroup straight from global memory into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at l * 16 of a 1 KiB
+// section), already in operand order: one section per (K tile, k step) and
+// per V d block, so every operand read is a conflict-free ds_read_b128 and
+// each compute wave applies it to all of its row blocks. The loader waves
+// keep two steps in flight in a ring of three LDS stages; they never read
+// LDS and the compute waves never load from global memory, so neither
+// waits on the other's traffic beyond the one barrier per step. Math per
+// row block is the narrow kernel's.
 
-template <int D, int BS, int NW, int RBW>
-__global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
+template <int D>
+constexpr int wide_loaders() { return D == 256 ? 2 : 1; }
+
+template <int D, int BS, int NC, int RBW>
+__global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kernel(AttnParams p) {
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
+  constexpr int NP = wide_loaders<D>();
   constexpr int NSEC = 2 * KS + DB;  // 1 KiB sections per step
-  constexpr int CPT = NSEC / NW;     // sections (16 B per lane) each wave stages
-  constexpr int KCPT = (2 * KS) / NW;  // of which K sections
-  static_assert(NSEC % NW == 0 && (2 * KS) % NW == 0, "sections per wave");
+  constexpr int SPL = NSEC / NP;     // sections per loader wave per step
+  static_assert(NSEC % NP == 0 && 2 * SPL < 64, "loads in flight per loader wave");
   static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
   static_assert(RBW == 1 || RBW == 2, "row blocks per wave");
-  __shared__ u32x4 stage[2][NSEC * 64];
+  // the ring's stages as separate arrays
+  __shared__ u32x4 st0[NSEC * 64], st1[NSEC * 64], st2[NSEC * 64];
+  __shared__ int32_t blk_s[kMaxChunkBlocks];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool loader = wave >= NC;
   const int n = lane & 15, g = lane >> 4;
   const int code = p.order[blockIdx.x];
   if (code < 0) return;
@@ -522,10 +552,95 @@ __global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
   const int kvh = rem - li * p.Hkv;
   const int layer = p.layer0 + li;
   const WorkItem it = p.items[item_idx];
+  const int n_steps = (it.n_tok + 31) >> 5;
+  const int last = n_steps - 1;
+  stage_block_ids<BS>(blk_s, p.blk + it.blk_off, n_steps);
+  __syncthreads();
+  const int voff = 8 * g;
+
+  // One barrier per step; the s_waitcnt immediate below has vmcnt in bits
+  // 3:0 and 15:14, expcnt 7 and lgkmcnt 15 meaning "no wait" on those. The
+  // barrier is the bare s_barrier: a workgroup fence would make every wave
+  // wait for all of its loads in flight.
+  if (loader) {
+    const int lw = wave - NC;
+    const uint16_t* K = (const uint16_t*)p.k_arena;
+    const uint16_t* V = (const uint16_t*)p.v_arena;
+    const int64_t layer_tiles = (int64_t)layer * p.num_blocks * p.Hkv;
+    const int koff0 = 8 * (n >> 2) + (n & 3);
+    // sections lw + NP * i of step s (the first 2KS are K, the rest V)
+    auto issue = [&](int s, u32x4* buf) __attribute__((always_inline)) {
+      const int tbase = 32 * s;
+      const int bA = blk_s[tbase / BS];
+      const int bB = blk_s[(tbase + 16) / BS];
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int sect = lw + NP * i;
+        const uint16_t* src;
+        if (sect < 2 * KS) {
+          const int tau = sect / KS, ks = sect - (sect / KS) * KS;
+          const int off = koff0 + 4 * tau;
+          const int b = (BS == 16 && off >= 16) ? bB : bA;
+          src = K + ((layer_tiles + (int64_t)b * p.Hkv + kvh) * BS + (tbase + off) % BS) * D +
+                32 * ks + 8 * g;
+        } else {
+          const int j = sect - 2 * KS;
+          const int b = (BS == 16 && voff >= 16) ? bB : bA;
+          src = V + ((layer_tiles + (int64_t)b * p.Hkv + kvh) * D + 16 * j + n) * BS +
+                (tbase + voff) % BS;
+        }
+        __builtin_amdgcn_global_load_lds(
+            src, (__attribute__((address_space(3))) void*)&buf[sect * 64], 16, 0, 0);
+      }
+    };
+    // At step s: wait for this wave's loads of step s (step s + 1's may
+    // stay in flight), barrier (step s has landed everywhere and every
+    // compute wave is done with step s - 1's stage), then load step s + 2
+    // into that stage. Past the end the last step is loaded again (in
+    // bounds, never read), so the count of younger loads is always SPL.
+    // In the chunk's last step the V slots past its end may hold anything
+    // (even NaN); each loader zeroes them in the V sections it loaded,
+    // after they land and before the barrier, so that 0 * V stays 0.
+    const bool ragged = (it.n_tok & 31) != 0;
+    auto zero_tail = [&](u32x4* cur) __attribute__((always_inline)) {
+      const int tv = 32 * last + voff;
+      u32x4 keep;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = (tv + 2 * w < it.n_tok) ? 0x0000ffffu : 0u;
+        const uint32_t hi = (tv + 2 * w + 1 < it.n_tok) ? 0xffff0000u : 0u;
+        keep[w] = lo | hi;
+      }
+#pragma unroll
+      for (int i = 0; i < SPL; ++i) {
+        const int sect = lw + NP * i;
+        if (sect >= 2 * KS) cur[sect * 64 + lane] &= keep;
+      }
+    };
+    constexpr int kWaitVm = 0x0F70 | (SPL & 0xF) | ((SPL >> 4) << 14);
+    auto step = [&](int s, u32x4* cur, u32x4* next) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm);
+      if (ragged && s == last) zero_tail(cur);
+      __builtin_amdgcn_s_barrier();
+      issue(min(s + 2, last), next);
+    };
+    issue(0, st0);
+    issue(min(1, last), st1);
+    for (int s = 0; s < n_steps; s += 3) {
+      step(s, st0, st2);
+      if (s + 1 >= n_steps) break;
+      step(s + 1, st1, st0);
+      if (s + 2 >= n_steps) break;
+      step(s + 2, st2, st1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    return;
+  }
+
   const int RB = (it.n_rows + 15) >> 4;
   int nrb = 0;
 #pragma unroll
-  for (int r = 0; r < RBW; ++r) nrb += (wave + NW * r < RB) ? 1 : 0;
+  for (int r = 0; r < RBW; ++r) nrb += (wave + NC * r < RB) ? 1 : 0;
   const bool tree = it.mask_from != 0x7fffffff && it.t0 + it.n_tok > it.mask_from;
 
   bf16x8 qv[RBW][KS];
@@ -533,7 +648,7 @@ __global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
   uint64_t anc[RBW];
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
-    const int row = (wave + NW * r) * 16 + n;
+    const int row = (wave + NC * r) * 16 + n;
     row_ok[r] = r < nrb && row < it.n_rows;
     const int crow = it.r0 + row;
     const int hold = crow / p.G;
@@ -550,55 +665,6 @@ __global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
     anc[r] = (tree && row_ok[r]) ? p.anc[branch] : ~0ull;
   }
 
-  const uint16_t* K = (const uint16_t*)p.k_arena;
-  const uint16_t* V = (const uint16_t*)p.v_arena;
-  const int64_t layer_tiles = (int64_t)layer * p.num_blocks * p.Hkv;
-  const int32_t* blk = p.blk + it.blk_off;
-  const int n_steps = (it.n_tok + 31) >> 5;
-  const int koff0 = 8 * (n >> 2) + (n & 3);
-  const int voff = 8 * g;
-
-  // global -> registers: this wave's sections of step s (section
-  // NW * i + wave; the first 2KS sections are K, the rest V)
-  const bool stream_kv = it.reread == 0;
-  auto ldkv = [&](const uint16_t* ptr) { return stream_kv ? ld16_stream(ptr) : ld16(ptr); };
-  auto load_step = [&](int s, u32x4 (&r)[CPT]) {
-    const int tbase = 32 * s;
-    const int bA = blk[tbase / BS];
-    const int bB = blk[(tbase + 16) / BS];
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int sect = wave + NW * i;
-      if (i < KCPT) {
-        const int tau = sect / KS, ks = sect - (sect / KS) * KS;
-        const int off = koff0 + 4 * tau;
-        const int b = (BS == 16 && off >= 16) ? bB : bA;
-        r[i] = ldkv(K + ((layer_tiles + (int64_t)b * p.Hkv + kvh) * BS + (tbase + off) % BS) * D +
-                    32 * ks + 8 * g);
-      } else {
-        const int j = sect - 2 * KS;
-        const int b = (BS == 16 && voff >= 16) ? bB : bA;
-        u32x4 v = ldkv(V + ((layer_tiles + (int64_t)b * p.Hkv + kvh) * D + 16 * j + n) * BS +
-                       (tbase + voff) % BS);
-        if (tbase + 32 > it.n_tok) {
-          // slots past the chunk may hold anything: zero them (0 * V = 0)
-          const int tv = tbase + voff;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t lo = (tv + 2 * w < it.n_tok) ? 0x0000ffffu : 0u;
-            const uint32_t hi = (tv + 2 * w + 1 < it.n_tok) ? 0xffff0000u : 0u;
-            v[w] &= lo | hi;
-          }
-        }
-        r[i] = v;
-      }
-    }
-  };
-  auto store_step = [&](int buf, const u32x4 (&r)[CPT]) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) stage[buf][(wave + NW * i) * 64 + lane] = r[i];
-  };
-
   f32x4 acc[RBW][DB];
 #pragma unroll
   for (int r = 0; r < RBW; ++r)
@@ -611,12 +677,7 @@ __global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
     l_run[r] = 0.f;
   }
 
-  // Pipeline: the loads of step s + 2 are issued (into the free register
-  // set) before step s computes; step s + 1's registers, loaded a step
-  // earlier, go to the other LDS buffer after it. The loop is unrolled by
-  // two so that both register sets keep static indices.
-  auto compute = [&](int step, int buf) {
-    const u32x4* st_sec = stage[buf];
+  auto compute = [&](int step, const u32x4* st_sec) __attribute__((always_inline)) {
     const int s = step;
     if (nrb > 0) {
       f32x4 sc4[RBW][2];
@@ -639,22 +700,22 @@ __global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
       bf16x8 phi[RBW], plo[RBW];
 #pragma unroll
       for (int r = 0; r < RBW; ++r) {
-        if (r >= nrb) continue;
+        if (r > 0 && r >= nrb) continue;
         float sc[8];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * tau + i;
+          for (int i = 0; i < 4; ++i) sc[4 * tau + i] = sc4[r][tau][i] * p.scale_log2;
+        if (tail || tree) {  // wave-uniform: only the chunk's last step and masked steps
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
             const int t = tv + e;
-            float v = sc4[r][tau][i] * p.scale_log2;
-            if (tail && t >= it.n_tok) v = kNegInf;
-            if (tree) {
-              const int pos = it.t0 + t;
-              if (pos >= it.mask_from && !((anc[r] >> (pos - it.mask_from)) & 1ull)) v = kNegInf;
-            }
-            sc[e] = v;
+            if (t >= it.n_tok) sc[e] = kNegInf;
+            const int pos = it.t0 + t;
+            if (tree && pos >= it.mask_from && !((anc[r] >> (pos - it.mask_from)) & 1ull))
+              sc[e] = kNegInf;
           }
+        }
         float mx = sc[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
@@ -677,7 +738,7 @@ __global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
         const bf16x8 a = as_bf16x8(st_sec[(2 * KS + j) * 64 + lane]);
 #pragma unroll
         for (int r = 0; r < RBW; ++r) {
-          if (r < nrb) {
+          if (r == 0 || r < nrb) {
             acc[r][j] = mfma_bf16(a, phi[r], acc[r][j]);
             acc[r][j] = mfma_bf16(a, plo[r], acc[r][j]);
           }
@@ -685,30 +746,23 @@ __global__ __launch_bounds__(NW * 64) void attn_wide_kernel(AttnParams p) {
       }
     }
   };
-  u32x4 ra[CPT], rb[CPT];
-  load_step(0, ra);
-  store_step(0, ra);
-  if (n_steps > 1) load_step(1, rb);
-  __syncthreads();
-  for (int s = 0; s < n_steps; s += 2) {
-    if (s + 2 < n_steps) load_step(s + 2, ra);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s, 0);
-    if (s + 1 < n_steps) store_step(1, rb);
-    __syncthreads();
+  for (int s = 0; s < n_steps; s += 3) {
+    __builtin_amdgcn_s_barrier();
+    compute(s, st0);
     if (s + 1 >= n_steps) break;
-    if (s + 3 < n_steps) load_step(s + 3, rb);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s + 1, 1);
-    if (s + 2 < n_steps) store_step(0, ra);
-    __syncthreads();
+    __builtin_amdgcn_s_barrier();
+    compute(s + 1, st1);
+    if (s + 2 >= n_steps) break;
+    __builtin_amdgcn_s_barrier();
+    compute(s + 2, st2);
   }
+
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
     if (r >= nrb) continue;
     const float l_tot = sum_xor32(sum_xor16(l_run[r]));
     if (!row_ok[r]) continue;
-    const int row = (wave + NW * r) * 16 + n;
+    const int row = (wave + NC * r) * 16 + n;
     const int64_t prow = (int64_t)(li * p.Hkv + kvh) * p.P + it.part_row + row;
     if (g == 0) {
       p.part_ml[2 * prow] = m_run[r];
@@ -1047,24 +1101,54 @@ hipError_t launch_valu(int D, int BS, const AttnParams& p, dim3 grid, hipStream_
 
 }  // namespace
 
-hipError_t launch_attn_wide(int D, int BS, int waves, const AttnParams& p, hipStream_t stream,
-                            const LaunchEvents& ev) {
+void attn_wide_shape(int D, int* waves, int* row_blocks) {
+  // automatic (waves 0 or row_blocks 0): 8 compute waves, two row blocks
+  // each up to head_dim 128 and one at 256 (where two blocks' accumulators
+  // would not fit next to three waves per SIMD)
+  const bool auto_w = !(*waves == 4 || *waves == 6 || *waves == 8);
+  int w = auto_w ? 8 : *waves;
+  int r = *row_blocks == 1 || *row_blocks == 2 ? *row_blocks : (D <= 128 ? 2 : 1);
+  if (w == 6 || (D == 256 && w == 8)) r = 1;
+  *waves = w;
+  *row_blocks = r;
+}
+
+hipError_t launch_attn_wide(int D, int BS, int waves, int row_blocks, const AttnParams& p,
+                            hipStream_t stream, const LaunchEvents& ev) {
   if (!attn_supported(true, 1, D, BS)) return hipErrorInvalidValue;
+  int w = waves, r = row_blocks;
+  attn_wide_shape(D, &w, &r);
+  if (w != waves || r != row_blocks) return hipErrorInvalidValue;
   if (p.n_order == 0) return hipSuccess;
   const dim3 grid((unsigned)p.n_order);
 #define PKV_WIDE(d, nw, rbw)                                                                    \
   switch (BS) {                                                                                 \
-    case 16: return launch(attn_wide_kernel<d, 16, nw, rbw>, grid, dim3(nw * 64), stream, ev, p); \
-    case 32: return launch(attn_wide_kernel<d, 32, nw, rbw>, grid, dim3(nw * 64), stream, ev, p); \
-    default: return launch(attn_wide_kernel<d, 64, nw, rbw>, grid, dim3(nw * 64), stream, ev, p); \
+    case 16: return launch(attn_wide_kernel<d, 16, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, p); \
+    case 32: return launch(attn_wide_kernel<d, 32, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, p); \
+    default: return launch(attn_wide_kernel<d, 64, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, p); \
   }
-  // 128 rows per item either way: 4 waves x 2 row blocks or 8 waves x 1
-  if (D == 64) PKV_WIDE(64, 4, 2)  // 8 waves would leave K sections unevenly split
+  if (D == 64) {
+    if (w == 8) {
+      if (r == 2) PKV_WIDE(64, 8, 2)
+      PKV_WIDE(64, 8, 1)
+    }
+    if (w == 6) PKV_WIDE(64, 6, 1)
+    if (r == 2) PKV_WIDE(64, 4, 2)
+    PKV_WIDE(64, 4, 1)
+  }
   if (D == 128) {
-    if (waves == 8) PKV_WIDE(128, 8, 1)
-    PKV_WIDE(128, 4, 2)
+    if (w == 8) {
+      if (r == 2) PKV_WIDE(128, 8, 2)
+      PKV_WIDE(128, 8, 1)
+    }
+    if (w == 6) PKV_WIDE(128, 6, 1)
+    if (r == 2) PKV_WIDE(128, 4, 2)
+    PKV_WIDE(128, 4, 1)
   }
-  PKV_WIDE(256, 8, 1)
+  if (w == 8) PKV_WIDE(256, 8, 1)
+  if (w == 6) PKV_WIDE(256, 6, 1)
+  if (r == 2) PKV_WIDE(256, 4, 2)
+  PKV_WIDE(256, 4, 1)
 #undef PKV_WIDE
 }
 

@@ -70,11 +70,18 @@ hipError_t launch_attn(bool mfma, bool lo_split, bool prefetch, int row_blocks_p
 // this head size.
 int attn_max_row_blocks_per_wave(int D);
 
-// The wide-row matrix-core kernel (bf16), same grid convention. waves: 4
-// (two 16-row blocks per wave) or 8 (one); head_dim 256 always uses 8,
-// head_dim 64 always 4.
-hipError_t launch_attn_wide(int D, int BS, int waves, const AttnParams& p, hipStream_t stream,
-                            const LaunchEvents& ev);
+// The wide-row matrix-core kernel (bf16), same grid convention: waves per
+// workgroup and 16-row blocks per wave, one of the compiled shapes
+// (attn_wide_shape); a workgroup serves up to 16 * waves * row_blocks rows.
+hipError_t launch_attn_wide(int D, int BS, int waves, int row_blocks, const AttnParams& p,
+                            hipStream_t stream, const LaunchEvents& ev);
+
+// The compiled wide shape for the requested one (in/out). waves counts the
+// compute waves (4, 6 or 8; anything else: automatic, 8); row_blocks the
+// 16-row blocks each owns (1 or 2; anything else: automatic, 2 up to
+// head_dim 128 and 1 at 256). 6 waves, and 8 at head_dim 256, own one
+// block each. The kernel adds its loader waves.
+void attn_wide_shape(int D, int* waves, int* row_blocks);
 
 // max_entries: the longest per-branch list of partial states.
 hipError_t launch_combine(int D, int max_entries, const CombineParams& p, hipStream_t stream,

@@ -9,6 +9,7 @@
 #include "schedule.hpp"
 
 #include <algorithm>
+#include <stdexcept>
 #include <cstring>
 
 namespace pkv {
@@ -46,16 +47,19 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   // chunk length per segment: long enough that the partial states a chunk
   // writes stay small next to the K/V it reads (rows * (D + 2) floats vs
   // tokens * 2 * D elements), short enough to fill the machine
+  // no chunk spans more than kMaxChunkBlocks blocks
+  const int32_t cap = (kMaxChunkBlocks / step_blocks) * step;
   auto base_len = [&](const Segment& s) {
-    if (opt.chunk_tokens > 0) return round_up(opt.chunk_tokens, step);
+    if (opt.chunk_tokens > 0) return std::min(round_up(opt.chunk_tokens, step), cap);
     int32_t rows = s.n_hold * G;
     int32_t t = round_up(std::max(opt.min_chunk_tokens, opt.tokens_per_row * rows), step);
-    return std::min(t, round_up(opt.max_chunk_tokens, step));
+    return std::min({t, round_up(opt.max_chunk_tokens, step), cap});
   };
   auto count_wgs = [&](int32_t div) {
     int64_t w = 0;
     for (const Segment& s : segs) {
-      int32_t len = std::max(round_up(opt.min_chunk_tokens, step), round_up(base_len(s) / div, step));
+      int32_t len =
+          std::min(cap, std::max(round_up(opt.min_chunk_tokens, step), round_up(base_len(s) / div, step)));
       if (opt.chunk_tokens > 0) len = base_len(s);
       int64_t chunks = (s.n_tok + len - 1) / len;
       const int64_t rows = (int64_t)s.n_hold * G;
@@ -67,7 +71,9 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   };
   int32_t div = 1;
   if (opt.chunk_tokens <= 0) {
-    while (div < 64 && count_wgs(div) < opt.target_workgroups &&
+    // (three quarters: one workgroup per CU on 3/4 of the chip beats two
+    // half-length rounds on all of it plus twice the partial states)
+    while (div < 64 && 4 * count_wgs(div) < 3 * (int64_t)opt.target_workgroups &&
            count_wgs(div * 2) > count_wgs(div))
       div *= 2;
   }
@@ -76,11 +82,13 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
     Segment& s = segs[si];
     int32_t len = opt.chunk_tokens > 0
                       ? base_len(s)
-                      : std::max(round_up(opt.min_chunk_tokens, step), round_up(base_len(s) / div, step));
+                      : std::min(cap, std::max(round_up(opt.min_chunk_tokens, step),
+                                               round_up(base_len(s) / div, step)));
     const int32_t nb = (int32_t)s.blocks.size();
     int32_t k = (s.n_tok + len - 1) / len;
     // equal chunks of whole steps
     int32_t per = round_up((nb + k - 1) / k, step_blocks);
+    if (per > kMaxChunkBlocks) throw std::logic_error("planner: chunk longer than kMaxChunkBlocks");
     s.chunk_begin = (int32_t)chunks.size();
     for (int32_t b0 = 0; b0 < nb; b0 += per) {
       int32_t b1 = std::min(nb, b0 + per);

@@ -17,8 +17,8 @@ struct SchedOptions {
   int32_t chunk_tokens = 0;        // 0 = automatic
   int32_t rows_per_item = 32;      // narrow items (16 on the VALU path)
   bool wide = true;                // chunks with more rows go to wide items
-  int32_t wide_rows = 128;         // rows per wide item at most
-  int32_t target_workgroups = 256;  // shorten chunks only to fill every CU once
+  int32_t wide_rows = 256;         // rows per wide item at most (also capped by the kernel shape)
+  int32_t target_workgroups = 256;  // shorten chunks while the grid has fewer than 3/4 of this
   int32_t min_chunk_tokens = 1024;
   int32_t max_chunk_tokens = 8192;
   int32_t tokens_per_row = 40;     // chunk length per query row (keeps partial traffic ~5%)

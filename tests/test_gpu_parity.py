@@ -69,9 +69,12 @@ SMALL_DECODE = [
 
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
-               row_blocks=1):
+               row_blocks=1, wide_shape=None):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    if wide_shape:
+        c.set_option("wide_waves", wide_shape[0])
+        c.set_option("wide_row_blocks", wide_shape[1])
     c.set_option("path", path)
     c.set_option("prefetch", prefetch)
     c.set_option("row_blocks_per_wave", row_blocks)
@@ -138,6 +141,21 @@ def test_wide_and_narrow_items_agree(w):
     assert ma <= 1e-4, ma
     _, chunked = run_decode(w, wide=1, chunk_tokens=32)
     assert errors(chunked, wide)[0] <= 1e-4
+
+
+WIDE_SHAPES = [(8, 1), (6, 1), (4, 1), (4, 2), (8, 2)]
+
+
+@pytest.mark.parametrize("w", [SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: f"{s[0]}w{s[1]}b")
+def test_wide_shapes_match_oracle(w, shape):
+    """Every compiled wide-kernel shape (waves per workgroup x row blocks
+    per wave; the library falls back to the nearest one a head size has)."""
+    note(f"wide shape {w.name} {shape}")
+    inp, got = run_decode(w, wide_shape=shape)
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"{w.name} wide {shape}")
 
 
 @pytest.mark.parametrize("name,keep_root", [("tiny_a", True), ("tiny_b", True), ("tiny_b", False)])
@@ -219,11 +237,14 @@ def test_random_traces_device_bit_exact(pkv, seed, dtype, bs):
 
 # ------------------------------------------------------------------ verify
 
-def run_verify(w, order=None, chunk_tokens=0, parents=None):
+def run_verify(w, order=None, chunk_tokens=0, parents=None, wide_shape=None):
     inp = generate(w)
     if parents is not None:
         inp.parents = parents
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    if wide_shape:
+        c.set_option("wide_waves", wide_shape[0])
+        c.set_option("wide_row_blocks", wide_shape[1])
     c.set_option("chunk_tokens", chunk_tokens)
     reqs = [h[s] for s in w.query_sids]
     out = c.verify(reqs, inp.parents, to_device(inp.q), scale=w.softmax_scale)
@@ -255,6 +276,16 @@ def test_verify_matches_oracle(w, chunk):
     pool = build_oracle(w, inp)
     want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), w.softmax_scale)
     check_close(got, want, f"verify {w.name} chunk={chunk}")
+
+
+@pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: f"{s[0]}w{s[1]}b")
+def test_verify_wide_shapes(shape):
+    for w in (SMALL_VERIFY[0], SMALL_VERIFY[1], SMALL_VERIFY[2]):
+        note(f"verify {w.name} wide {shape}")
+        inp, got = run_verify(w, wide_shape=shape)
+        pool = build_oracle(w, inp)
+        want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), w.softmax_scale)
+        check_close(got, want, f"verify {w.name} wide {shape}")
 
 
 def test_verify_chain_and_star_trees():

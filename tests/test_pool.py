@@ -277,6 +277,33 @@ def test_plan_segments_closed_form(pkv, name, segments):
     assert info["workspace_bytes"] > 0
 
 
+def build_host_tree(pkv, w):
+    c = pkv.PagedKVCache(w.num_blocks_bound(), w.shape.BS, w.shape.L, w.shape.Hkv, w.shape.Hq,
+                         w.shape.D, dtype=w.shape.dtype, device=None)
+    h = {}
+    for op in w.ops:
+        if op.kind == "create":
+            h[op.sid] = c.create()
+        elif op.kind == "fork":
+            h[op.sid] = c.fork(h[op.parent])
+        elif op.kind == "append":
+            c.plan(h[op.sid], op.n)
+        else:
+            c.free(h.pop(op.sid))
+    return c, [h[s] for s in w.query_sids]
+
+
+@pytest.mark.parametrize("name,chunks", [("agent", 1 + 4 * 2), ("beam", 9)])
+def test_plan_caps_chunks_at_512_blocks(pkv, name, chunks):
+    """However long the requested chunks, none spans more than 512 blocks
+    (the matrix-core kernels stage a chunk's block ids in LDS): agent's
+    416-block prefix stays whole and each 1024-block tail splits in two."""
+    w = get(name)
+    c, seqs = build_host_tree(pkv, w)
+    c.set_option("chunk_tokens", 1 << 20)
+    assert c.plan_info(seqs)["n_chunks"] == chunks
+
+
 def test_fork_many_and_free_many(pkv):
     c = host_cache(pkv, 32, 4)
     p = c.create()
