@@ -255,6 +255,8 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  *                       own, 1 or 2; with 2 (head_dim <= 128 only) an item of
  *                       up to 32 rows loads each K/V step once, at the cost of
  *                       occupancy
+ *   "wide_fill"         1: fill every wide item of a chunk but the last to the row
+ *                       limit (0: split the rows evenly)
  *   "wide_waves"        0: compute waves per wide workgroup, 4, 6 or 8; 0 picks 8
  *                       (the workgroup adds one or two loader waves)
  *   "wide_row_blocks"   0: 16-row blocks each wide compute wave owns, 1 or 2; 0

@@ -780,6 +780,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
     if (value < 0 || value > 2)
       return fail(PKV_E_INVALID, "wide_row_blocks must be 0 (automatic), 1 or 2");
     pool->wide_row_blocks = (int)value;
+  } else if (k == "wide_fill") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "wide_fill must be 0 or 1");
+    pool->opt.wide_fill = value != 0;
   } else if (k == "wide_rows") {
     if (value < 16 || value > 256) return fail(PKV_E_INVALID, "wide_rows must be 16..256");
     pool->opt.wide_rows = (int32_t)value;

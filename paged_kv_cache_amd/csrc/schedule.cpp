@@ -121,8 +121,11 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
     w.mask_from = s.mask_from;
     if (opt.wide && rows > rpi) {
       // wide items of one chunk (siblings) read it through the shared L2
+      // (rows split evenly in whole blocks, or with wide_fill every item
+      // but the last full)
       const int32_t k = (rows + opt.wide_rows - 1) / opt.wide_rows;
-      const int32_t per = round_up((rows + k - 1) / k, 16);
+      const int32_t per = opt.wide_fill ? std::max<int32_t>(16, opt.wide_rows / 16 * 16)
+                                        : round_up((rows + k - 1) / k, 16);
       std::vector<WorkItem> grp;
       w.reread = per < rows ? 1 : 0;
       for (int32_t r0 = 0; r0 < rows; r0 += per) {

@@ -18,6 +18,7 @@ struct SchedOptions {
   int32_t rows_per_item = 32;      // narrow items (16 on the VALU path)
   bool wide = true;                // chunks with more rows go to wide items
   int32_t wide_rows = 256;         // rows per wide item at most (also capped by the kernel shape)
+  bool wide_fill = true;           // wide items full but the last (else an even split)
   int32_t target_workgroups = 256;  // shorten chunks while the grid has fewer than 3/4 of this
   int32_t min_chunk_tokens = 1024;
   int32_t max_chunk_tokens = 8192;
