@@ -255,6 +255,9 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  *                       own, 1 or 2; with 2 (head_dim <= 128 only) an item of
  *                       up to 32 rows loads each K/V step once, at the cost of
  *                       occupancy
+ *   "concurrent"        0: 1 runs the wide-item launch on a second stream of the
+ *                       library's, forked from and joined back into the caller's
+ *                       stream, beside the narrow-item launch
  *   "wide_fill"         1: fill every wide item of a chunk but the last to the row
  *                       limit (0: split the rows evenly)
  *   "wide_waves"        0: compute waves per wide workgroup, 4, 6 or 8; 0 picks 8
@@ -272,10 +275,12 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value);
 
 /* Device time of the kernels launched since the last read (with the
  * "timing" option on): kernel is "attention" (items of few rows),
- * "attention_wide" (items of many rows), "combine" or "append" (the launch
- * that performs copy-on-write copies and token writes). Waits for
+ * "attention_wide" (items of many rows; the two may overlap in time),
+ * "attention_span" (from before the first to after the last attention
+ * launch of a call, on the caller's stream), "combine" or "append" (the
+ * launch that performs copy-on-write copies and token writes). Waits for
  * the last recorded launch, returns the summed milliseconds and the launch
- * count, and resets both. */
+ * (or call) count, and resets both. */
 int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_t* launches);
 
 /* Last error message of this thread ("" if none). */

@@ -79,7 +79,7 @@ struct KernelTimer {
   }
 };
 
-enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_WIDE = 3, T_KINDS = 4 };
+enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_WIDE = 3, T_SPAN = 4, T_KINDS = 5 };
 
 struct pkv_pool {
   explicit pkv_pool(const pkv_pool_desc& d) : pool(d) {}
@@ -111,6 +111,25 @@ struct pkv_pool {
   int wide_waves = 0;  // compute waves per wide workgroup (4, 6, 8; 0 automatic)
   int wide_row_blocks = 0;  // 16-row blocks per wave of the wide kernel (1, 2; 0 automatic)
   int prefetch = 0;    // narrow matrix-core kernel loads one step ahead
+  int concurrent = 0;  // narrow and wide launches on two streams
+
+  // A second stream (default priority) for the wide launch, so that it runs
+  // beside the narrow one; created on first use, on the device current then.
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  int side_stream(hipStream_t* out) {
+    if (!side) {
+      hipError_t e;
+      if ((e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking)) != hipSuccess)
+        return hip_fail(e, "hipStreamCreateWithFlags");
+      if ((e = hipEventCreateWithFlags(&ev_fork, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "hipEventCreateWithFlags");
+      if ((e = hipEventCreateWithFlags(&ev_join, hipEventDisableTiming)) != hipSuccess)
+        return hip_fail(e, "hipEventCreateWithFlags");
+    }
+    *out = side;
+    return PKV_OK;
+  }
 
   // schedule cache
   bool cache_valid = false;
@@ -123,6 +142,12 @@ struct pkv_pool {
   Schedule sched;
 
   ~pkv_pool() {
+    if (side) {
+      (void)hipStreamSynchronize(side);
+      (void)hipStreamDestroy(side);
+    }
+    if (ev_fork) (void)hipEventDestroy(ev_fork);
+    if (ev_join) (void)hipEventDestroy(ev_join);
     for (Staging& s : ring) {
       if (s.ev) {
         if (s.pending) (void)hipEventSynchronize(s.ev);
@@ -409,15 +434,24 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   // P enters P.V as bf16 plus its bf16 rounding residual: with P alone in
   // bf16 a row whose weight sits on a few keys is off by up to 2^-9 |v|
   const bool lo_split = true;
-  if (a.n_order > 0) {
-    rc = p->timed(
-        T_ATTN,
-        [&](const LaunchEvents& ev) {
-          return launch_attn(mfma, lo_split, p->prefetch != 0, S.narrow_rw, d.kv_dtype,
-                             d.head_dim, d.block_size, a, stream, ev);
-        },
-        "attention launch");
-    if (rc) return rc;
+  // With both launches present the wide one runs on the side stream, forked
+  // from and joined back into the caller's stream: the two read disjoint
+  // chunks and write disjoint partial rows, and together they keep more
+  // loads in flight than either alone.
+  const bool fork = a.n_order > 0 && S.n_order_wide > 0 && p->concurrent;
+  hipStream_t wstream = stream;
+  LaunchEvents span;  // both attention launches, start to end, on the caller's stream
+  if (p->timing) {
+    if ((rc = p->timers[T_SPAN].take(&span))) return rc;
+    hipError_t e = hipEventRecord(span.start, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  if (fork) {
+    if ((rc = p->side_stream(&wstream))) return rc;
+    hipError_t e;
+    if ((e = hipEventRecord(p->ev_fork, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(wstream, p->ev_fork, 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
   }
   if (S.n_order_wide > 0) {
     AttnParams aw = a;
@@ -428,10 +462,30 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
         [&](const LaunchEvents& ev) {
           int w = p->wide_waves, r = p->wide_row_blocks;
           attn_wide_shape(d.head_dim, &w, &r);
-          return launch_attn_wide(d.head_dim, d.block_size, w, r, aw, stream, ev);
+          return launch_attn_wide(d.head_dim, d.block_size, w, r, aw, wstream, ev);
         },
         "wide attention launch");
     if (rc) return rc;
+  }
+  if (a.n_order > 0) {
+    rc = p->timed(
+        T_ATTN,
+        [&](const LaunchEvents& ev) {
+          return launch_attn(mfma, lo_split, p->prefetch != 0, S.narrow_rw, d.kv_dtype,
+                             d.head_dim, d.block_size, a, stream, ev);
+        },
+        "attention launch");
+    if (rc) return rc;
+  }
+  if (fork) {
+    hipError_t e;
+    if ((e = hipEventRecord(p->ev_join, wstream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(stream, p->ev_join, 0)) != hipSuccess)
+      return hip_fail(e, "hipStreamWaitEvent");
+  }
+  if (p->timing) {
+    hipError_t e = hipEventRecord(span.stop, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   CombineParams c;
   c.part_ml = a.part_ml;
@@ -769,6 +823,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "prefetch") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "prefetch must be 0 or 1");
     pool->prefetch = (int)value;
+  } else if (k == "concurrent") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "concurrent must be 0 or 1");
+    pool->concurrent = (int)value;
   } else if (k == "row_blocks_per_wave") {
     if (value < 1 || value > 2) return fail(PKV_E_INVALID, "row_blocks_per_wave must be 1 or 2");
     pool->opt.max_row_blocks_per_wave = (int32_t)value;
@@ -806,6 +863,7 @@ int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_
   const std::string k(kernel);
   int kind = k == "attention" ? T_ATTN
              : k == "attention_wide" ? T_WIDE
+             : k == "attention_span" ? T_SPAN
              : k == "combine" ? T_COMBINE
              : k == "append" ? T_APPEND
                                : -1;

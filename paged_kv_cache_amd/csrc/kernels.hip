@@ -964,7 +964,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 //
 // Merges each output row's partial states (one per chunk on its path) in
 // logical order: M = max m_i, L = sum l_i 2^(m_i - M),
-// out = sum acc_i 2^(m_i - M) / L. Lane j owns d = j*VW .. j*VW + VW-1.
+// out = sum acc_i 2^(m_i - M) / L, computed in one online pass. Lane j owns
+// d = j*VW .. j*VW + VW-1.
 // WPR = 1: a wave per output row, four rows per workgroup (short lists).
 // WPR = 4: the four waves of a workgroup split one row's list (long lists:
 // split-K over a long context) and merge through LDS.
@@ -972,6 +973,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 template <int D, int WPR>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   constexpr int VW = D / 64;
+  constexpr int NB = 8;  // partials whose loads are in flight together
   typedef float vec_t __attribute__((ext_vector_type(VW)));
   __shared__ float red_m[4];
   __shared__ float red_l[4];
@@ -991,27 +993,53 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int64_t plane = (int64_t)(li * p.Hkv + kvh) * p.P + gq;
   const int sub = WPR == 1 ? 0 : wave;
 
-  float M = kNegInf;
-  for (int e = e0 + sub; e < e1; e += WPR) M = fmaxf(M, p.part_ml[2 * (plane + p.comb_rows[e])]);
+  // One pass, online: a running maximum M with the sum L and the vector
+  // acc scaled by 2^-M, rescaled when M grows. The (m, l, acc) loads of up
+  // to NB partials are issued before any of them is used, so a row costs
+  // about one memory round trip per NB partials.
+  float M = kNegInf, L = 0.f;
+  vec_t acc = {};
+  for (int e = e0 + sub; e < e1; e += NB * WPR) {
+    float mi[NB], li_[NB];
+    vec_t ai[NB];
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int ek = e + k * WPR;
+      mi[k] = kNegInf;
+      li_[k] = 0.f;
+      ai[k] = vec_t{};
+      if (ek < e1) {
+        const int64_t row = plane + p.comb_rows[ek];
+        mi[k] = p.part_ml[2 * row];
+        li_[k] = p.part_ml[2 * row + 1];
+        ai[k] = __builtin_nontemporal_load((const vec_t*)(p.part_acc + row * D + lane * VW));
+      }
+    }
+    float bm = mi[0];
+#pragma unroll
+    for (int k = 1; k < NB; ++k) bm = fmaxf(bm, mi[k]);
+    const float Mn = fmaxf(M, bm);
+    if (Mn != kNegInf) {
+      const float a = M == kNegInf ? 0.f : fast_exp2(M - Mn);
+      L *= a;
+      acc *= a;
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const float w = mi[k] == kNegInf ? 0.f : fast_exp2(mi[k] - Mn);
+        L += li_[k] * w;
+        acc += ai[k] * w;
+      }
+      M = Mn;
+    }
+  }
   if (WPR > 1) {
+    // merge the four waves' states
     if (lane == 0) red_m[wave] = M;
     __syncthreads();
-    M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-  }
-  float L = 0.f;
-  vec_t acc = {};
-#pragma unroll 4
-  for (int e = e0 + sub; e < e1; e += WPR) {
-    const int64_t row = plane + p.comb_rows[e];
-    const float mi = p.part_ml[2 * row];
-    const float w = mi == kNegInf ? 0.f : fast_exp2(mi - M);
-    L += p.part_ml[2 * row + 1] * w;
-    const vec_t a = __builtin_nontemporal_load((const vec_t*)(p.part_acc + row * D + lane * VW));
-    acc += a * w;
-  }
-  if (WPR > 1) {
-    if (lane == 0) red_l[wave] = L;
-    red_acc[wave][lane] = acc;
+    const float Mt = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    const float a = (M == kNegInf) ? 0.f : fast_exp2(M - Mt);
+    if (lane == 0) red_l[wave] = L * a;
+    red_acc[wave][lane] = acc * a;
     __syncthreads();
     if (wave != 0) return;
     L = red_l[0] + red_l[1] + red_l[2] + red_l[3];

@@ -69,9 +69,10 @@ SMALL_DECODE = [
 
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
-               row_blocks=1, wide_shape=None):
+               row_blocks=1, wide_shape=None, concurrent=1):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    c.set_option("concurrent", concurrent)
     if wide_shape:
         c.set_option("wide_waves", wide_shape[0])
         c.set_option("wide_row_blocks", wide_shape[1])
@@ -141,6 +142,16 @@ def test_wide_and_narrow_items_agree(w):
     assert ma <= 1e-4, ma
     _, chunked = run_decode(w, wide=1, chunk_tokens=32)
     assert errors(chunked, wide)[0] <= 1e-4
+
+
+@pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[8]], ids=lambda w: w.name)
+def test_concurrent_launches_bit_identical(w):
+    """The wide launch on the library's second stream (forked from and joined
+    into the caller's) computes exactly what it computes in order."""
+    note(f"concurrent {w.name}")
+    _, a = run_decode(w, rows_per_item=16, concurrent=1)
+    _, b = run_decode(w, rows_per_item=16, concurrent=0)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
 WIDE_SHAPES = [(8, 1), (6, 1), (4, 1), (4, 2), (8, 2)]
