@@ -59,6 +59,19 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
+def warm_up(args, step, torch, min_seconds: float = 0.3):
+    """W untimed steps, continued until min_seconds have passed: a fresh GPU
+    needs a fraction of a second of load before its clocks settle."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < args.warmup or time.perf_counter() - t0 < min_seconds:
+        step()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def to_dev(t):
     import torch
     if t.dtype == "f32":
@@ -159,9 +172,7 @@ def run_beam(args, pkv, torch):
     assert info["unique_tokens"] == uniq_tok, (info, uniq_tok)
     c.free_many(kids)
     uniq_bytes = uniq_tok * sh.token_kv_bytes * sh.L
-    for _ in range(args.warmup):
-        beam_step(c, beams, step_k, step_v, q, out, scale)
-    torch.cuda.synchronize()
+    warm_up(args, lambda: beam_step(c, beams, step_k, step_v, q, out, scale), torch)
     # timed region: K steps, no timing events (they add commands to the stream)
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -264,9 +275,7 @@ def run_tree(args, pkv, torch):
         out = torch.empty((sh.L, len(seqs), sh.Hq, sh.D), dtype=torch.float32, device="cuda")
         fn = lambda: c.decode(seqs, q, scale=w.softmax_scale, out=out)  # noqa: E731
         n_queries = len(seqs) * sh.L
-    for _ in range(args.warmup):
-        fn()
-    torch.cuda.synchronize()
+    warm_up(args, fn, torch)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         fn()

@@ -126,15 +126,20 @@ __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l,
     const u32x4 x = *from;
     ((u32x4*)(K + dt * tile + (int64_t)t * p.D))[c] = x;
   }
-  // V rows: whole rows from the source, new tokens patched in
+  // V rows: whole rows from the source, new tokens patched in (slot k of
+  // the row is visited with a compile-time index, so the row stays in
+  // registers)
+  typedef T vecT __attribute__((ext_vector_type(EPV)));
   for (int d = threadIdx.x; d < p.D; d += blockDim.x) {
-    const u32x4* vs = (const u32x4*)(V + st * tile + (int64_t)d * BS);
-    u32x4 row[RV];
+    const vecT* vs = (const vecT*)(V + st * tile + (int64_t)d * BS);
+    vecT row[RV];
 #pragma unroll
     for (int c = 0; c < RV; ++c) row[c] = vs[c];
-    T* e = (T*)row;
-    for (int i = 0; i < m; ++i) e[nv + i] = vn[(((int64_t)l * p.n_tok + tok0 + i) * p.Hkv + h) * p.D + d];
-    u32x4* vd = (u32x4*)(V + dt * tile + (int64_t)d * BS);
+    const T* vnew = vn + (((int64_t)l * p.n_tok + tok0) * p.Hkv + h) * p.D + d;
+#pragma unroll
+    for (int k = 0; k < BS; ++k)
+      if (k >= nv && k < nv + m) row[k / EPV][k % EPV] = vnew[(int64_t)(k - nv) * p.Hkv * p.D];
+    vecT* vd = (vecT*)(V + dt * tile + (int64_t)d * BS);
 #pragma unroll
     for (int c = 0; c < RV; ++c) vd[c] = row[c];
   }
