@@ -340,6 +340,7 @@ SchedOptions planner_options(const pkv_pool* p, bool mfma) {
     o.rows_per_item = std::min<int32_t>(o.rows_per_item, 16);
     o.wide = false;
     o.max_row_blocks_per_wave = 1;
+    o.short_items = false;
   } else {
     o.max_row_blocks_per_wave = std::min(
         o.max_row_blocks_per_wave, attn_max_row_blocks_per_wave(p->pool.desc().head_dim));
@@ -421,6 +422,8 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.anc = (const uint64_t*)(w + S.off_anc);
   a.order = (const int32_t*)(w + S.off_order);
   a.n_order = S.n_order_narrow;
+  a.n_long = (S.n_narrow - S.n_short) * S.n_layers * d.num_kv_heads;
+  a.n_codes = S.n_narrow * S.n_layers * d.num_kv_heads;
   a.n_items = (int32_t)S.items.size();
   a.n_layers = S.n_layers;
   a.layer0 = layer0;
@@ -455,7 +458,7 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   }
   if (S.n_order_wide > 0) {
     AttnParams aw = a;
-    aw.order = a.order + S.n_order_narrow;
+    aw.order = a.order;
     aw.n_order = S.n_order_wide;
     rc = p->timed(
         T_WIDE,
@@ -823,6 +826,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "prefetch") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "prefetch must be 0 or 1");
     pool->prefetch = (int)value;
+  } else if (k == "short_items") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "short_items must be 0 or 1");
+    pool->opt.short_items = value != 0;
   } else if (k == "concurrent") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "concurrent must be 0 or 1");
     pool->concurrent = (int)value;

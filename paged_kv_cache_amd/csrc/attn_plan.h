@@ -20,6 +20,11 @@ namespace pkv {
 // block ids to LDS.
 constexpr int32_t kMaxChunkBlocks = 512;
 
+// A narrow item of at most 16 rows and this many tokens is short: one wave
+// does all of it (four items' planes per workgroup) instead of four waves
+// splitting its steps and merging.
+constexpr int32_t kShortTokens = 64;
+
 struct WorkItem {
   int32_t blk_off;    // index in blk[] of the chunk's first block
   int32_t n_tok;      // valid tokens in the chunk (> 0)
@@ -47,8 +52,13 @@ struct AttnParams {
   const int32_t* blk;       // block ids, per chunk padded to a whole 32-token step
   const int32_t* holders;   // branch index of each holder
   const uint64_t* anc;      // [n_branch] ancestor-or-self bits (verify only)
-  const int32_t* order;     // per workgroup: item * (n_layers * Hkv) + layer * Hkv + head, or -1
+  const int32_t* order;     // wide launch: per workgroup item * (n_layers * Hkv) + layer * Hkv + head, or -1
   int32_t n_order;          // workgroups in the launch
+  // Narrow launch (no order table): code = item * (n_layers * Hkv) + layer *
+  // Hkv + head. Workgroups [0, n_long) take code = blockIdx; after them each
+  // workgroup takes four codes of short items, one per wave.
+  int32_t n_long;
+  int32_t n_codes;
   int32_t n_items;
   int32_t n_layers;
   int32_t layer0;

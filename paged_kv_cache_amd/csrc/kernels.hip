@@ -244,8 +244,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int code = p.order[blockIdx.x];
-  if (code < 0) return;
+  // long items: the workgroup serves one code; short items: each wave one
+  // (the workgroup's mode is uniform: short items come last)
+  const bool solo = (int)blockIdx.x >= p.n_long;
+  const int code = solo ? p.n_long + ((int)blockIdx.x - p.n_long) * 4 + wave : (int)blockIdx.x;
+  if (code >= p.n_codes) return;  // only whole waves of a solo workgroup
   const int per_item = p.n_layers * p.Hkv;
   const int item_idx = code / per_item;
   const int rem = code - item_idx * per_item;
@@ -258,8 +261,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int RB = (it.n_rows + 15) >> 4;
   const int RG = (RB + RW - 1) / RW;
   const int RGp = RG == 1 ? 1 : (RG == 2 ? 2 : 4);
-  const int phases = 4 / RGp;
-  const int rg = wave % RGp, phase = wave / RGp;
+  const int phases = solo ? 1 : 4 / RGp;
+  const int rg = solo ? 0 : wave % RGp, phase = solo ? 0 : wave / RGp;
   const bool active = rg < RG;
   const int nblk = active ? min(RW, RB - rg * RW) : 0;  // wave-uniform
 
@@ -314,7 +317,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   // step ahead, which costs no extra wait and spares short items the
   // staging round trip.
   __shared__ int32_t blk_s[PF ? kMaxChunkBlocks : 1];
-  if (PF) {
+  const bool staged = PF && !solo;  // (a solo wave reads its own ids)
+  if (staged) {
     stage_block_ids<BS>(blk_s, blk, n_steps);
     __syncthreads();
   }
@@ -411,7 +415,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
 
   if (active && phase < n_steps) {
     auto ids = [&](int s, int& a, int& b) {
-      const int32_t* src = PF ? blk_s : blk;
+      const int32_t* src = staged ? blk_s : blk;
       a = src[(32 * s) / BS];
       b = src[(32 * s + 16) / BS];
     };
@@ -803,8 +807,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   __shared__ float mrg_acc[3][MAXR][D];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int code = p.order[blockIdx.x];
-  if (code < 0) return;
+  const int code = blockIdx.x;  // (the vector-ALU plans have no short items)
   const int per_item = p.n_layers * p.Hkv;
   const int item_idx = code / per_item;
   const int rem = code - item_idx * per_item;

@@ -155,10 +155,19 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   S->narrow_rw = (max_rows > 16 && opt.max_row_blocks_per_wave >= 2) ? 2 : 1;
   for (WorkItem& w : narrow)
     if (w.n_rows > 16 * S->narrow_rw) w.reread = 1;
-  // longest chunks first, so the tail of each grid holds the short ones;
-  // wide groups also by sibling count, so equal counts sit together
-  std::stable_sort(narrow.begin(), narrow.end(),
-                   [](const WorkItem& a, const WorkItem& b) { return a.n_tok > b.n_tok; });
+  // longest chunks first, so the tail of each grid holds the short ones
+  // (short items, one wave each, last); wide groups also by sibling count,
+  // so equal counts sit together
+  auto is_short = [&](const WorkItem& w) {
+    return opt.short_items && w.n_rows <= 16 && w.n_tok <= kShortTokens;
+  };
+  std::stable_sort(narrow.begin(), narrow.end(), [&](const WorkItem& a, const WorkItem& b) {
+    const bool sa = is_short(a), sb = is_short(b);
+    if (sa != sb) return sb;  // long before short
+    return a.n_tok > b.n_tok;
+  });
+  S->n_short = 0;
+  for (const WorkItem& w : narrow) S->n_short += is_short(w) ? 1 : 0;
   std::stable_sort(wide_groups.begin(), wide_groups.end(),
                    [](const std::vector<WorkItem>& a, const std::vector<WorkItem>& b) {
                      if (a.size() != b.size()) return a.size() > b.size();
@@ -176,10 +185,11 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
 void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
   const int32_t LH = n_layers * Hkv;
   order.clear();
-  // narrow launch: item-major, all (layer, head) planes of an item together
-  for (int32_t i = 0; i < n_narrow; ++i)
-    for (int32_t lh = 0; lh < LH; ++lh) order.push_back(i * LH + lh);
-  n_order_narrow = (int32_t)order.size();
+  // narrow launch: no table (code = blockIdx for long items, four codes per
+  // workgroup for the short ones)
+  const int64_t long_codes = (int64_t)(n_narrow - n_short) * LH;
+  const int64_t short_codes = (int64_t)n_short * LH;
+  n_order_narrow = (int32_t)(long_codes + (short_codes + 3) / 4);
   // wide launch: a unit is (sibling group, plane); the R siblings of a unit
   // are placed 8 workgroups apart, so that with workgroups dealt round-robin
   // to the 8 XCDs they share one XCD (and its L2) and start together
@@ -204,7 +214,7 @@ void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
         order.push_back(j < k ? (units[u + j].first + r) * LH + units[u + j].lh : -1);
     u += k;
   }
-  n_order_wide = (int32_t)order.size() - n_order_narrow;
+  n_order_wide = (int32_t)order.size();
 }
 
 void Schedule::layout(int Hkv, int D) {

@@ -24,14 +24,16 @@ struct SchedOptions {
   int32_t max_chunk_tokens = 8192;
   int32_t tokens_per_row = 40;     // chunk length per query row (keeps partial traffic ~5%)
   int32_t max_row_blocks_per_wave = 1;  // 16-row blocks one narrow wave may own (1 or 2)
+  bool short_items = true;         // one wave per plane for short narrow items
 };
 
 struct Schedule {
-  std::vector<WorkItem> items;     // narrow items, then wide items
+  std::vector<WorkItem> items;     // narrow items (long, then short), then wide items
   int32_t n_narrow = 0;
+  int32_t n_short = 0;             // short narrow items (the last n_short of the narrow ones)
   int32_t narrow_rw = 1;           // 16-row blocks per wave in the narrow launch
-  std::vector<int32_t> order;      // workgroup order: narrow launch, then wide launch
-  int32_t n_order_narrow = 0;
+  std::vector<int32_t> order;      // workgroup order of the wide launch
+  int32_t n_order_narrow = 0;      // workgroups of the narrow launch (no table)
   int32_t n_order_wide = 0;
   std::vector<int32_t> blk;
   std::vector<int32_t> holders;

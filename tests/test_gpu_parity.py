@@ -69,10 +69,11 @@ SMALL_DECODE = [
 
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
-               row_blocks=1, wide_shape=None, concurrent=1):
+               row_blocks=1, wide_shape=None, concurrent=0, short_items=1):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("concurrent", concurrent)
+    c.set_option("short_items", short_items)
     if wide_shape:
         c.set_option("wide_waves", wide_shape[0])
         c.set_option("wide_row_blocks", wide_shape[1])
@@ -142,6 +143,21 @@ def test_wide_and_narrow_items_agree(w):
     assert ma <= 1e-4, ma
     _, chunked = run_decode(w, wide=1, chunk_tokens=32)
     assert errors(chunked, wide)[0] <= 1e-4
+
+
+@pytest.mark.parametrize("w", [SMALL_DECODE[3], SMALL_DECODE[8]], ids=lambda w: w.name)
+@pytest.mark.parametrize("chunk,pf", [(0, 0), (32, 0), (32, 1)])
+def test_short_items_one_wave_each(w, chunk, pf):
+    """Short narrow items (<= 16 rows, <= 64 tokens) run one (layer, head)
+    plane per wave; the results match the four-wave form to fp32 rounding
+    and the oracle to tolerance."""
+    note(f"short items {w.name} chunk={chunk} prefetch={pf}")
+    inp, a = run_decode(w, chunk_tokens=chunk, prefetch=pf, short_items=1)
+    _, b = run_decode(w, chunk_tokens=chunk, prefetch=pf, short_items=0)
+    assert errors(a, b)[0] <= 1e-4
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(a, want, f"{w.name} short items chunk={chunk}")
 
 
 @pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[8]], ids=lambda w: w.name)
