@@ -22,6 +22,17 @@ print no algorithm):
 * An append is all or nothing: if the pool runs dry part-way, every change
   it made is undone and ``OOMError`` is raised.
 * Appending zero tokens writes nothing and so copies nothing.
+* Truncating a sequence to its first n tokens releases the references of
+  the blocks that then hold none of its tokens; a kept, partly filled last
+  block keeps its count (a later append copies it if it is shared).
+* Committing a verified draft tree (Ferrite page, section 04: best-first
+  trees verified in one pass; section 06: speculation never changes the
+  text) keeps the accepted path: the request's last n_nodes tokens are the
+  tree (node j at position len - n_nodes + j); the accepted nodes must form
+  a chain from a root (each one's parent is the one before it, the first
+  one's parent is -1). The sequence becomes the context followed by the
+  accepted nodes' K/V in path order, exactly as if those tokens had been
+  appended one after another: truncate to the context, then append them.
 """
 
 from __future__ import annotations
@@ -145,6 +156,58 @@ class OraclePool:
         self.mat[sid] = self.mat[sid] + [(kc, vc)]
         self.cow_log.extend(cows)
         return slots, cows
+
+    def truncate(self, sid: int, n: int) -> None:
+        """Keep the first ``n`` tokens of ``sid`` (0 <= n <= length)."""
+        self._check(sid)
+        if n < 0 or n > self.lens[sid]:
+            raise InvalidError("truncate length outside [0, length]")
+        bs = self.block_size
+        keep = (n + bs - 1) // bs
+        table = self.tables[sid]
+        for b in table[keep:]:
+            self.ref[b] -= 1
+            if self.ref[b] == 0:
+                self.free_blocks.add(b)
+        del table[keep:]
+        self.lens[sid] = n
+        if n == 0:
+            self.mat[sid] = []
+        else:
+            k, v = self.kv(sid)
+            k = np.array(k[:, :n], copy=True)
+            v = np.array(v[:, :n], copy=True)
+            k.flags.writeable = False
+            v.flags.writeable = False
+            self.mat[sid] = [(k, v)]
+
+    @staticmethod
+    def check_path(parents: Sequence[int], accepted: Sequence[int]) -> None:
+        """Raise InvalidError unless ``accepted`` is a chain from a root of
+        the tree given by ``parents`` (parent index or -1 per node)."""
+        n = len(parents)
+        prev = -1
+        for a in accepted:
+            if not 0 <= a < n or parents[a] != prev:
+                raise InvalidError("accepted nodes are not a chain from a root")
+            prev = a
+
+    def commit(self, sid: int, n_nodes: int, parents: Sequence[int], accepted: Sequence[int]):
+        """Keep the accepted path of the draft tree that ends ``sid``.
+        Returns the (slots, cow_ops) of the re-append."""
+        self._check(sid)
+        if n_nodes < 1 or n_nodes > self.lens[sid] or len(parents) != n_nodes:
+            raise InvalidError("tree size does not fit the sequence")
+        self.check_path(parents, accepted)
+        c = self.lens[sid] - n_nodes
+        k, v = self.kv(sid)
+        pos = [c + a for a in accepted]
+        kk = np.array(k[:, pos], copy=True)
+        vv = np.array(v[:, pos], copy=True)
+        self.truncate(sid, c)
+        if not accepted:
+            return [], []
+        return self.append(sid, kk, vv)
 
     def free(self, sid: int) -> None:
         self._check(sid)

@@ -487,3 +487,112 @@ def test_planted_verify_mask_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oatt, "ancestors", no_self)
     with pytest.raises(AssertionError):
         test_verify_chain_equals_causal_attention()
+
+
+# --------------------------------------------------------- commit (f2)
+
+def _tree_request(seed, ctx, n_nodes, bs=4, L=2, Hkv=2, D=4, max_depth=8, nb=64):
+    """A pool holding one request: ctx context tokens then an n_nodes draft
+    tree (parents drawn as for the verify workload)."""
+    from workloads.gen import verify_parents
+    rng = np.random.default_rng(seed)
+    pool = OraclePool(nb, bs)
+    s = pool.create()
+    kv = rng.standard_normal((2, L, ctx + n_nodes, Hkv, D)).astype(np.float32)
+    if ctx:
+        pool.append(s, kv[0][:, :ctx], kv[1][:, :ctx])
+    pool.append(s, kv[0][:, ctx:], kv[1][:, ctx:])
+    parents = verify_parents(seed, 0, n_nodes, max_depth)
+    return pool, s, kv, [int(x) for x in parents]
+
+
+def _root_path(parents, leaf):
+    path = []
+    while leaf != -1:
+        path.append(leaf)
+        leaf = parents[leaf]
+    return path[::-1]
+
+
+def test_commit_of_a_whole_chain_changes_nothing():
+    """A chain tree accepted in full is already in path order."""
+    pool, s, kv, _ = _tree_request(1, 9, 7)
+    chain = [-1] + list(range(6))
+    t0, refs0 = pool.table(s), list(pool.ref)
+    k0, v0 = pool.kv(s)
+    slots, cows = pool.commit(s, 7, chain, list(range(7)))
+    k1, v1 = pool.kv(s)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    assert pool.table(s) == t0 and pool.ref == refs0 and cows == []
+    check_invariants(pool)
+
+
+def test_commit_of_no_node_keeps_the_context():
+    pool, s, kv, parents = _tree_request(2, 10, 9)
+    free0 = len(pool.free_blocks)
+    pool.commit(s, 9, parents, [])
+    assert pool.length(s) == 10
+    k, v = pool.kv(s)
+    assert np.array_equal(k, kv[0][:, :10]) and np.array_equal(v, kv[1][:, :10])
+    # 19 tokens in 5 blocks of 4 -> 10 tokens in 3 blocks
+    assert len(pool.table(s)) == 3 and len(pool.free_blocks) == free0 + 2
+    check_invariants(pool)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_commit_equals_appending_the_path(seed):
+    """Committing a root path gives, by value, the sequence built by
+    appending the context and then the path's tokens ("speculation never
+    changes the text")."""
+    ctx, N = 5 + seed, 12
+    pool, s, kv, parents = _tree_request(10 + seed, ctx, N)
+    leaf = int(np.random.default_rng(seed).integers(N))
+    path = _root_path(parents, leaf)
+    pool.commit(s, N, parents, path)
+    ref = OraclePool(64, 4)
+    r = ref.create()
+    ref.append(r, kv[0][:, :ctx], kv[1][:, :ctx])
+    for a in path:
+        ref.append(r, kv[0][:, ctx + a:ctx + a + 1], kv[1][:, ctx + a:ctx + a + 1])
+    assert pool.length(s) == ref.length(r) == ctx + len(path)
+    k1, v1 = pool.kv(s)
+    k2, v2 = ref.kv(r)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    check_invariants(pool)
+
+
+def test_commit_copies_a_shared_tail_and_leaves_the_fork():
+    """A fork taken before the commit shares the context's partly filled
+    block: the commit copies it (never writing an aliased block) and the
+    fork still reads the whole tree."""
+    pool, s, kv, parents = _tree_request(4, 6, 8)   # context ends inside block 1
+    f = pool.fork(s)
+    kf0, vf0 = pool.kv(f)
+    path = _root_path(parents, 7)
+    slots, cows = pool.commit(s, 8, parents, path)
+    assert len(cows) == 1 and cows[0][2] == 6 % 4
+    kf1, vf1 = pool.kv(f)
+    assert np.array_equal(kf0, kf1) and np.array_equal(vf0, vf1)
+    assert pool.table(f)[:2] != pool.table(s)[:2]
+    check_invariants(pool)
+
+
+def test_commit_rejects_a_non_chain_and_changes_nothing():
+    pool, s, kv, parents = _tree_request(5, 4, 6)
+    snap = (pool.table(s), list(pool.ref), pool.length(s))
+    inner = next(a for a in range(6) if parents[a] != -1)
+    for bad in ([inner], [0, 0], [0, 6], [-1]):     # not from a root, repeated, out of range
+        with pytest.raises(Exception):
+            pool.commit(s, 6, parents, bad)
+        assert (pool.table(s), list(pool.ref), pool.length(s)) == snap
+
+
+def test_truncate_then_reappend_restores_the_sequence():
+    pool, s, kv, _ = _tree_request(6, 11, 5)
+    k0, v0 = pool.kv(s)
+    pool.truncate(s, 7)
+    assert pool.length(s) == 7 and len(pool.table(s)) == 2
+    pool.append(s, k0[:, 7:], v0[:, 7:])
+    k1, v1 = pool.kv(s)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    check_invariants(pool)
