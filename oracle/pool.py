@@ -33,6 +33,8 @@ print no algorithm):
   one's parent is -1). The sequence becomes the context followed by the
   accepted nodes' K/V in path order, exactly as if those tokens had been
   appended one after another: truncate to the context, then append them.
+  Like an append, a commit is all or nothing: if the re-append runs out of
+  blocks, the truncation is undone too and ``OOMError`` is raised.
 """
 
 from __future__ import annotations
@@ -204,10 +206,16 @@ class OraclePool:
         pos = [c + a for a in accepted]
         kk = np.array(k[:, pos], copy=True)
         vv = np.array(v[:, pos], copy=True)
+        snap, mat = self._snapshot(), list(self.mat[sid])
         self.truncate(sid, c)
         if not accepted:
             return [], []
-        return self.append(sid, kk, vv)
+        try:
+            return self.append(sid, kk, vv)
+        except OOMError:
+            self._restore(snap)
+            self.mat[sid] = mat
+            raise
 
     def free(self, sid: int) -> None:
         self._check(sid)

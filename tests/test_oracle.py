@@ -596,3 +596,25 @@ def test_truncate_then_reappend_restores_the_sequence():
     k1, v1 = pool.kv(s)
     assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
     check_invariants(pool)
+
+
+def test_commit_that_runs_out_of_blocks_changes_nothing():
+    """The re-append must copy the context's shared, partly filled block; with
+    no free block the commit fails and leaves tables and K/V as they were."""
+    from oracle.pool import OOMError
+    bs = 4
+    pool = OraclePool(2, bs)
+    s = pool.create()
+    kv = np.random.default_rng(7).standard_normal((2, 1, 8, 1, 4)).astype(np.float32)
+    pool.append(s, kv[0][:, :6], kv[1][:, :6])     # context: 6 tokens
+    pool.append(s, kv[0][:, 6:], kv[1][:, 6:])     # tree: nodes 0, 1 (a chain)
+    f = pool.fork(s)
+    snap = (pool.table(s), pool.table(f), list(pool.ref), set(pool.free_blocks), pool.length(s))
+    k0, v0 = pool.kv(s)
+    with pytest.raises(OOMError):
+        pool.commit(s, 2, [-1, 0], [0])
+    assert (pool.table(s), pool.table(f), list(pool.ref), set(pool.free_blocks),
+            pool.length(s)) == snap
+    k1, v1 = pool.kv(s)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    check_invariants(pool)
