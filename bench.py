@@ -252,7 +252,10 @@ def run_tree(args, pkv, torch):
     w = get(args.workload)
     sh = w.shape
     inp = generate(w)
-    c = pkv.PagedKVCache(w.num_blocks_bound() + 8, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D, dtype=sh.dtype)
+    # verify: room for the contexts to grow by the committed paths
+    extra = len(w.query_sids) * (COMMIT_STEPS * w.n_nodes // sh.BS + 2) if w.kind == "verify" else 0
+    c = pkv.PagedKVCache(w.num_blocks_bound() + 8 + extra, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D,
+                         dtype=sh.dtype)
     kv = {i: (k, v) for i, _s, k, v in inp.appends}
     h = {}
     for i, op in enumerate(w.ops):
@@ -315,8 +318,56 @@ def run_tree(args, pkv, torch):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, kernel)},
     }
+    if w.kind == "verify":
+        res["commit"] = commit_leg(c, seqs, w, inp, fn, torch)
     c.close()
     return res
+
+
+COMMIT_STEPS = 20
+
+
+def commit_leg(c, seqs, w, inp, verify, torch):
+    """Speculative steps after the timed verify calls: every request keeps a
+    random root path of its tree (commit), then a new tree of the same shape
+    is appended and verified. Reports the commit's wall time per step (all
+    requests, host planning included) and its kernels' device time."""
+    sh = w.shape
+    R, N = len(seqs), w.n_nodes
+    rng = np.random.default_rng(11)
+    kv = torch.randn((sh.L, R * N, sh.Hkv, sh.D), device="cuda").to(torch.bfloat16)
+    paths = []
+    for _ in range(COMMIT_STEPS):
+        step = []
+        for r in range(R):
+            leaf, path = int(rng.integers(N)), []
+            while leaf != -1:
+                path.append(leaf)
+                leaf = int(inp.parents[r][leaf])
+            step.append(path[::-1])
+        paths.append(step)
+    for k in ("commit_gather", "append"):
+        c.timing_read(k)
+    c.set_option("timing", 1)
+    wall = gather = append = 0.0
+    for i in range(COMMIT_STEPS):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for r in range(R):
+            c.commit(seqs[r], inp.parents[r], paths[i][r])
+        torch.cuda.synchronize()
+        wall += time.perf_counter() - t0
+        gather += c.timing_read("commit_gather")[0]
+        append += c.timing_read("append")[0]
+        c.append(seqs, [N] * R, kv, kv)
+        verify()
+        c.timing_read("append")
+    torch.cuda.synchronize()
+    c.set_option("timing", 0)
+    kept = sum(len(p) for st in paths for p in st) / COMMIT_STEPS
+    return {"steps": COMMIT_STEPS, "requests": R, "kept_tokens_per_step": kept,
+            "ms_per_step": round(wall * 1e3 / COMMIT_STEPS, 4),
+            "gather_ms": round(gather / COMMIT_STEPS, 5), "append_ms": round(append / COMMIT_STEPS, 5)}
 
 
 def main():

@@ -239,6 +239,32 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
                          const int32_t* parents, int32_t n_nodes, int32_t layer, const void* q,
                          float* out, float scale, void* ws, size_t ws_bytes, void* stream);
 
+/* Keeps the first new_len tokens of seq (0 <= new_len <= its length):
+ * blocks that then hold none of its tokens lose its reference (and are
+ * freed at zero); a kept, partly filled last block keeps its count, so a
+ * later append copies it if it is shared ([D-rust]). Host only. */
+int pkv_seq_truncate(pkv_pool* pool, pkv_seq seq, int32_t new_len);
+
+/* Workspace bytes pkv_tree_commit needs to keep n_accepted tokens. */
+int pkv_tree_commit_workspace_size(const pkv_pool* pool, int32_t n_accepted, size_t* bytes);
+
+/* Keeps the accepted path of a verified draft tree ([F4]; Ferrite page,
+ * section 06: speculation never changes the text). seq's last n_nodes
+ * tokens are the tree (node j at position len - n_nodes + j), parents as
+ * for pkv_tree_verify_attn (host int32 [n_nodes]). accepted: host int32
+ * [n_accepted], a chain from a root (parents[accepted[0]] == -1,
+ * parents[accepted[i]] == accepted[i - 1]), 0 <= n_accepted <= n_nodes <=
+ * 64. The sequence becomes its context followed by the accepted nodes' K/V
+ * in path order, exactly as if they had been appended one by one: their
+ * K/V are read into ws (device, >= pkv_tree_commit_workspace_size bytes),
+ * the sequence is truncated to its context, and they are appended again
+ * (copying a shared context tail on write). All or nothing on the host:
+ * PKV_E_OOM (a needed copy finds no free block) or PKV_E_INVALID leave
+ * the tables unchanged. Device work is queued on stream. */
+int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t* parents,
+                    const int32_t* accepted, int32_t n_accepted, void* ws, size_t ws_bytes,
+                    void* stream);
+
 /* ---------------------------------------------------------------- misc */
 
 /* Tuning knobs of the attention planner (defaults in parentheses):
@@ -255,6 +281,9 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  *                       own, 1 or 2; with 2 (head_dim <= 128 only) an item of
  *                       up to 32 rows loads each K/V step once, at the cost of
  *                       occupancy
+ *   "short_items"       1: a narrow item of at most 16 rows and 64 tokens runs on
+ *                       one wave (four such planes per workgroup) instead of four
+ *                       waves that split its steps and merge (0: always four)
  *   "concurrent"        0: 1 runs the wide-item launch on a second stream of the
  *                       library's, forked from and joined back into the caller's
  *                       stream, beside the narrow-item launch
@@ -277,8 +306,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value);
  * "timing" option on): kernel is "attention" (items of few rows),
  * "attention_wide" (items of many rows; the two may overlap in time),
  * "attention_span" (from before the first to after the last attention
- * launch of a call, on the caller's stream), "combine" or "append" (the
- * launch that performs copy-on-write copies and token writes). Waits for
+ * launch of a call, on the caller's stream), "combine", "append" (the
+ * launch that performs copy-on-write copies and token writes) or
+ * "commit_gather" (the read-out of a committed path's K/V). Waits for
  * the last recorded launch, returns the summed milliseconds and the launch
  * (or call) count, and resets both. */
 int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_t* launches);

@@ -94,6 +94,10 @@ _PROTOS = {
     "pkv_verify_workspace_size": [c_void_p, POINTER(PkvSeq), c_int32, c_int32, POINTER(c_size_t)],
     "pkv_tree_verify_attn": [c_void_p, POINTER(PkvSeq), c_int32, POINTER(c_int32), c_int32, c_int32,
                              c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p],
+    "pkv_seq_truncate": [c_void_p, PkvSeq, c_int32],
+    "pkv_tree_commit_workspace_size": [c_void_p, c_int32, POINTER(c_size_t)],
+    "pkv_tree_commit": [c_void_p, PkvSeq, c_int32, POINTER(c_int32), POINTER(c_int32), c_int32,
+                        c_void_p, c_size_t, c_void_p],
     "pkv_pool_set_option": [c_void_p, c_char_p, c_int64],
     "pkv_timing_read": [c_void_p, c_char_p, POINTER(ctypes.c_double), POINTER(c_int64)],
 }

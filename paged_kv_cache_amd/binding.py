@@ -221,6 +221,26 @@ def pkv_tree_verify_attn(pool, reqs: Sequence[PkvSeq], parents, layer: int, q, o
                                    ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def pkv_seq_truncate(pool, seq: PkvSeq, new_len: int) -> None:
+    check(lib.pkv_seq_truncate(pool, seq, int(new_len)))
+
+
+def pkv_tree_commit_workspace_size(pool, n_accepted: int) -> int:
+    out = c_size_t()
+    check(lib.pkv_tree_commit_workspace_size(pool, int(n_accepted), byref(out)))
+    return out.value
+
+
+def pkv_tree_commit(pool, seq: PkvSeq, parents, accepted, ws, stream=None) -> None:
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32).reshape(-1))
+    acc = np.ascontiguousarray(np.asarray(accepted, dtype=np.int32).reshape(-1))
+    acc_buf = acc if acc.size else np.zeros(1, dtype=np.int32)
+    check(lib.pkv_tree_commit(pool, seq, par.size, par.ctypes.data_as(ctypes.POINTER(c_int32)),
+                              acc_buf.ctypes.data_as(ctypes.POINTER(c_int32)), acc.size,
+                              _dev_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream)))
+
+
 def pkv_last_error() -> str:
     return lib.pkv_last_error().decode(errors="replace")
 
@@ -292,6 +312,9 @@ class PagedKVCache:
     def length(self, seq: PkvSeq) -> int:
         return pkv_seq_info(self.handle, seq)[0]
 
+    def truncate(self, seq: PkvSeq, new_len: int) -> None:
+        pkv_seq_truncate(self.handle, seq, new_len)
+
     def refcount(self, block: int) -> int:
         return pkv_block_refcount(self.handle, block)
 
@@ -356,3 +379,8 @@ class PagedKVCache:
         self._check_out(out, (len(reqs), par.shape[-1], self.Hq, self.D))
         pkv_tree_verify_attn(self.handle, reqs, par, layer, q, out, scale, ws, stream)
         return out
+
+    def commit(self, seq: PkvSeq, parents, accepted, stream=None) -> None:
+        """Keeps the accepted root-to-node path of the draft tree that ends seq."""
+        ws = self._workspace(pkv_tree_commit_workspace_size(self.handle, len(accepted)))
+        pkv_tree_commit(self.handle, seq, parents, accepted, ws, stream)

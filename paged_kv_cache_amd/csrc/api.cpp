@@ -79,7 +79,7 @@ struct KernelTimer {
   }
 };
 
-enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_WIDE = 3, T_SPAN = 4, T_KINDS = 5 };
+enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_WIDE = 3, T_SPAN = 4, T_GATHER = 5, T_KINDS = 6 };
 
 struct pkv_pool {
   explicit pkv_pool(const pkv_pool_desc& d) : pool(d) {}
@@ -686,6 +686,110 @@ int pkv_seq_append_kv(pkv_pool* pool, pkv_seq seq, int32_t n, const void* k_new,
   return pkv_append_kv_batch(pool, &seq, &n, 1, k_new, v_new, stream);
 }
 
+int pkv_seq_truncate(pkv_pool* pool, pkv_seq seq, int32_t new_len) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.seq_truncate(seq, new_len);
+  PKV_GUARD_END
+}
+
+int pkv_tree_commit_workspace_size(const pkv_pool* pool, int32_t n_accepted, size_t* bytes) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool) || !bytes) return fail(PKV_E_INVALID, "null argument");
+  if (n_accepted < 0 || n_accepted > kGatherSlots)
+    return fail(PKV_E_INVALID, "commit: n_accepted outside [0, 64]");
+  const pkv_pool_desc& d = pool->pool.desc();
+  const size_t half = ((size_t)d.num_layers * n_accepted * d.num_kv_heads * d.head_dim *
+                           elem_size(d) + 255) & ~size_t(255);
+  *bytes = 2 * half;
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t* parents,
+                    const int32_t* accepted, int32_t n_accepted, void* ws, size_t ws_bytes,
+                    void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  const pkv_pool_desc& d = pool->pool.desc();
+  if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  if (n_nodes < 1 || n_nodes > 64) return fail(PKV_E_INVALID, "commit: n_nodes must be 1..64");
+  if (n_accepted < 0 || n_accepted > n_nodes)
+    return fail(PKV_E_INVALID, "commit: n_accepted outside [0, n_nodes]");
+  if (!parents || (n_accepted > 0 && !accepted)) return fail(PKV_E_INVALID, "commit: null argument");
+  for (int32_t j = 0; j < n_nodes; ++j)
+    if (parents[j] < -1 || parents[j] >= j) return fail(PKV_E_INVALID, "commit: bad parent pointer");
+  int32_t prev = -1;
+  for (int32_t i = 0; i < n_accepted; ++i) {
+    const int32_t a = accepted[i];
+    if (a < 0 || a >= n_nodes || parents[a] != prev)
+      return fail(PKV_E_INVALID, "commit: accepted nodes are not a chain from a root");
+    prev = a;
+  }
+  const Seq* s = pool->pool.get(seq);
+  if (!s) return PKV_E_INVALID;
+  if (s->len < n_nodes) return fail(PKV_E_INVALID, "commit: the sequence is shorter than the tree");
+  size_t need = 0;
+  int rc = pkv_tree_commit_workspace_size(pool, n_accepted, &need);
+  if (rc) return rc;
+  if (n_accepted > 0 && (!ws || ws_bytes < need))
+    return fail(PKV_E_WORKSPACE, "commit: workspace too small");
+  const int64_t bs = d.block_size;
+  const int32_t ctx = s->len - n_nodes;
+  // all or nothing: the re-append needs a copy of a shared partly filled
+  // context tail and blocks for the tokens past it; the truncation frees
+  // the tree's blocks that only this sequence holds
+  {
+    const int32_t keep = (int32_t)((ctx + bs - 1) / bs);
+    int64_t freed = 0;
+    for (size_t i = (size_t)keep; i < s->blocks.size(); ++i) {
+      int32_t rcnt = 0;
+      pool->pool.refcount(s->blocks[i], &rcnt);
+      freed += rcnt == 1 ? 1 : 0;
+    }
+    int64_t needed = 0;
+    if (n_accepted > 0) {
+      const int32_t r = (int32_t)(ctx % bs);
+      int32_t tail_rc = 0;
+      if (r != 0) pool->pool.refcount(s->blocks[(size_t)keep - 1], &tail_rc);
+      needed += (r != 0 && tail_rc > 1) ? 1 : 0;
+      const int64_t room = r != 0 ? bs - r : 0;
+      if (n_accepted > room) needed += (n_accepted - room + bs - 1) / bs;
+    }
+    pkv_stats st;
+    pool->pool.stats(&st);
+    if (needed > st.free_blocks + freed) return fail(PKV_E_OOM, "commit: pool exhausted");
+  }
+  hipStream_t strm = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  const size_t half = need / 2;
+  if (n_accepted > 0) {
+    GatherParams g{};
+    g.k_arena = d.k_arena;
+    g.v_arena = d.v_arena;
+    g.k_out = w;
+    g.v_out = w + half;
+    g.n = n_accepted;
+    g.L = d.num_layers;
+    g.NB = d.num_blocks;
+    g.Hkv = d.num_kv_heads;
+    g.D = d.head_dim;
+    g.BS = d.block_size;
+    for (int32_t i = 0; i < n_accepted; ++i) {
+      const int64_t pos = (int64_t)ctx + accepted[i];
+      g.slots[i] = (int64_t)s->blocks[(size_t)(pos / bs)] * bs + pos % bs;
+    }
+    rc = pool->timed(
+        T_GATHER, [&](const LaunchEvents& ev) { return launch_gather(d.kv_dtype, g, strm, ev); },
+        "gather launch");
+    if (rc) return rc;
+  }
+  if ((rc = pool->pool.seq_truncate(seq, ctx))) return rc;
+  if (n_accepted == 0) return PKV_OK;
+  return pkv_append_kv_batch(pool, &seq, &n_accepted, 1, w, w + half, stream);
+  PKV_GUARD_END
+}
+
 int pkv_seq_info(const pkv_pool* pool, pkv_seq seq, int32_t* len, int32_t* n_blocks) {
   PKV_GUARD_BEGIN
   if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
@@ -872,6 +976,7 @@ int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_
              : k == "attention_span" ? T_SPAN
              : k == "combine" ? T_COMBINE
              : k == "append" ? T_APPEND
+             : k == "commit_gather" ? T_GATHER
                                : -1;
   if (kind < 0) return fail(PKV_E_INVALID, "unknown kernel " + k);
   return pool->timers[kind].read(total_ms, launches);

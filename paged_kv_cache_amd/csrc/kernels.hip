@@ -173,6 +173,31 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 }
 
+// ------------------------------------------------------------- gather
+//
+// One workgroup per (layer, token): the token's K rows (contiguous D per
+// KV head) and V columns (stride BS in the d-major V tile) are copied into
+// [L][n][Hkv][D] outputs. Used to keep a verified draft path: its tokens
+// are read out before the tree is truncated, then appended again.
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
+  const int l = blockIdx.x / p.n, i = blockIdx.x - (blockIdx.x / p.n) * p.n;
+  const int64_t slot = p.slots[i];
+  const int64_t b = slot / p.BS;
+  const int off = (int)(slot - b * p.BS);
+  const int64_t t0 = ((int64_t)l * p.NB + b) * p.Hkv;
+  const T* K = (const T*)p.k_arena;
+  const T* V = (const T*)p.v_arena;
+  T* ko = (T*)p.k_out + ((int64_t)l * p.n + i) * p.Hkv * p.D;
+  T* vo = (T*)p.v_out + ((int64_t)l * p.n + i) * p.Hkv * p.D;
+  for (int e = threadIdx.x; e < p.Hkv * p.D; e += blockDim.x) {
+    const int h = e / p.D, d = e - h * p.D;
+    ko[e] = K[((t0 + h) * p.BS + off) * p.D + d];
+    vo[e] = V[((t0 + h) * p.D + d) * p.BS + off];
+  }
+}
+
 // ----------------------------------------------------- MFMA attention
 //
 // One workgroup (4 waves) per (work item, layer, KV head). A work item is a
@@ -1074,6 +1099,15 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
 }
 
 }  // namespace
+
+hipError_t launch_gather(int dtype, const GatherParams& p, hipStream_t stream,
+                         const LaunchEvents& ev) {
+  if (p.n <= 0) return hipSuccess;
+  if (p.n > kGatherSlots) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(p.n * p.L));
+  if (dtype == 0) return launch(gather_kernel<float>, grid, dim3(256), stream, ev, p);
+  return launch(gather_kernel<uint16_t>, grid, dim3(256), stream, ev, p);
+}
 
 hipError_t launch_append(int dtype, const AppendParams& p, hipStream_t stream,
                          const LaunchEvents& ev) {

@@ -47,6 +47,27 @@ struct AppendParams {
   int32_t inl_tok[kInlineSlots];
 };
 
+// Reads the K/V of n tokens, given by slot (block * BS + offset), out of
+// the arenas into k_out / v_out, each [L][n][Hkv][D] (the layout the
+// append takes). At most kGatherSlots tokens.
+constexpr int kGatherSlots = 64;
+struct GatherParams {
+  const void* k_arena;
+  const void* v_arena;
+  void* k_out;
+  void* v_out;
+  int32_t n;
+  int32_t L;
+  int32_t NB;
+  int32_t Hkv;
+  int32_t D;
+  int32_t BS;
+  int64_t slots[kGatherSlots];
+};
+
+hipError_t launch_gather(int dtype, const GatherParams& p, hipStream_t stream,
+                         const LaunchEvents& ev);
+
 // Block sizes the append kernel is built for.
 bool append_supported(int BS);
 

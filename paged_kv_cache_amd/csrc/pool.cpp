@@ -171,6 +171,22 @@ int Pool::seq_free(pkv_seq h) {
   return PKV_OK;
 }
 
+int Pool::seq_truncate(pkv_seq h, int32_t n) {
+  Seq* s = get_mut(h);
+  if (!s) return PKV_E_INVALID;
+  if (n < 0 || n > s->len) return fail(PKV_E_INVALID, "truncate: length outside [0, len]");
+  const int32_t keep = (int32_t)((n + (int64_t)d_.block_size - 1) / d_.block_size);
+  for (size_t i = (size_t)keep; i < s->blocks.size(); ++i) {
+    const int32_t b = s->blocks[i];
+    if (--ref_[b] == 0) free_.insert(rank_of_[b]);
+    --total_refs_;
+  }
+  s->blocks.resize((size_t)keep);
+  s->len = n;
+  ++mutation_;
+  return PKV_OK;
+}
+
 int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t n,
                             std::vector<int64_t>* slots, std::vector<pkv_cow_op>* cows) {
   if (n < 0 || (n > 0 && (!seqs || !counts))) return fail(PKV_E_INVALID, "append: bad arguments");

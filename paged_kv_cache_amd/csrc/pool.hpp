@@ -58,6 +58,10 @@ class Pool {
   int seq_create(pkv_seq* out);
   int seq_fork(pkv_seq parent, pkv_seq* child);
   int seq_free(pkv_seq s);
+  // Keeps the first n tokens (0 <= n <= len): blocks that then hold none of
+  // the sequence's tokens lose its reference; a kept partly filled block
+  // keeps its count.
+  int seq_truncate(pkv_seq s, int32_t n);
 
   // Plans appends for seqs[i] += counts[i] tokens, in order, all or nothing.
   // Slots are appended to `slots` in (sequence, token) order; copies to `cows`.

@@ -132,6 +132,68 @@ def test_random_traces_bit_exact(pkv, seed):
     assert st["free_blocks"] == nb and st["total_refs"] == 0 and st["live_seqs"] == 0
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_traces_with_truncate_bit_exact(pkv, seed):
+    """Forks, appends and truncations (as a draft-tree commit makes them)
+    give the oracle's tables, counts and free list."""
+    rng = np.random.default_rng(300 + seed)
+    nb = int(rng.integers(12, 40))
+    bs = [1, 2, 4, 16][seed % 4]
+    order = rng.permutation(nb).tolist() if seed % 2 else None
+    c = host_cache(pkv, nb, bs, order)
+    pool = OraclePool(nb, bs, alloc_order=order)
+    handles = {}
+    for _ in range(200):
+        act = int(rng.integers(5)) if handles else 0
+        if act == 0:
+            sid = pool.create()
+            handles[sid] = c.create()
+        elif act == 1:
+            p = list(handles)[rng.integers(len(handles))]
+            sid = pool.fork(p)
+            handles[sid] = c.fork(handles[p])
+        elif act == 2:
+            sid = list(handles)[rng.integers(len(handles))]
+            n = int(rng.integers(0, 3 * bs + 2))
+            try:
+                want = pool.append(sid, zeros(n), zeros(n))
+            except oracle.OOMError:
+                with pytest.raises(pkv.OOM):
+                    c.plan(handles[sid], n)
+            else:
+                got = c.plan(handles[sid], n)
+                assert got[0] == want[0]
+                assert got[1] == [tuple(x) for x in want[1]]
+        elif act == 3:
+            sid = list(handles)[rng.integers(len(handles))]
+            n = int(rng.integers(0, pool.length(sid) + 1))
+            pool.truncate(sid, n)
+            c.truncate(handles[sid], n)
+        else:
+            sid = list(handles)[rng.integers(len(handles))]
+            pool.free(sid)
+            c.free(handles.pop(sid))
+        compare_state(c, pool, handles)
+
+
+def test_truncate_rejects_bad_lengths(pkv):
+    from paged_kv_cache_amd import binding
+    c = host_cache(pkv, 8, 4)
+    s = c.create()
+    c.plan(s, 6)
+    for n in (-1, 7):
+        with pytest.raises(pkv.PkvError) as e:
+            c.truncate(s, n)
+        assert e.value.code == pkv.PKV_E_INVALID
+    assert c.length(s) == 6 and c.table(s) == [0, 1]
+    c.truncate(s, 6)
+    assert c.table(s) == [0, 1]
+    c.truncate(s, 0)
+    assert c.table(s) == [] and c.stats()["free_blocks"] == 8
+    with pytest.raises(pkv.PkvError):      # device call without arenas
+        binding.pkv_tree_commit(c.handle, s, [-1], [0], None)
+
+
 @pytest.mark.parametrize("name", ["beam", "mcts", "agent", "verify", "beam_cow"])
 def test_full_size_tables_bit_exact(pkv, name):
     w = get(name)
