@@ -15,6 +15,11 @@ What it computes, in plain numpy (attention in float64):
   with O(1) CoW forking by shallow pointer copy, and of the rule that a block
   being written may not be aliased (HN page, "How is this different from
   vLLM's paged attention?" and "Why Rust?").
+* A prompt cache inside ``OraclePool``: full blocks keyed by their token ids
+  and the entry before them, longest-prefix match into a new sequence,
+  parked blocks that outlive their sequence, least-recently-used eviction of
+  entries only the cache holds when the pool runs dry. Source: Ferrite
+  project page, section 07 and the "Agents" measurement.
 * ``decode`` -- softmax(q K^T * scale) V over each sequence's materialised
   tokens, one query per sequence and head (grouped-query heads: head h reads
   KV head h // (Hq / Hkv)).
@@ -29,7 +34,9 @@ derivations stored under tests/golden/, closed forms (a single token returns
 its V, a zero query returns the mean of V, equal keys return the mean of V),
 refcount invariants and closed-form refcount histograms, and brute-force
 equivalences (verify on a chain tree equals causal attention; each tree node
-equals a decode over its ancestor path). Every function here is pinned; none
+equals a decode over its ancestor path; a cache match equals the longest
+cached prefix found by spelling out every entry; a resumed sequence equals
+one computed in full), and a hand-derived eviction order. Every function here is pinned; none
 is "parity unpinned".
 """
 

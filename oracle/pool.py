@@ -35,6 +35,32 @@ print no algorithm):
   appended one after another: truncate to the context, then append them.
   Like an append, a commit is all or nothing: if the re-append runs out of
   blocks, the truncation is undone too and ``OOMError`` is raised.
+* Prompt cache (Ferrite page, section 07, and the "Agents" measurement: a
+  conversation is snapshotted at turn boundaries, resumes from the longest
+  match, a system prompt shared by several agents is computed once, and a
+  conversation that loses its slot is parked). Read here as a cache of full
+  blocks keyed by their exact token ids and by the entry of the block before
+  them, so a chain of entries from the root spells a whole token prefix:
+  - insert(sid, tokens) walks the sequence's full blocks among its first
+    len(tokens) positions; a block whose key is present only refreshes that
+    entry, a new key makes an entry that holds one reference on the
+    sequence's block (the block outlives the sequence: it is parked).
+  - match(tokens) makes a new sequence from the longest chain of entries
+    whose tokens are a prefix of ``tokens`` (whole blocks only); each block
+    gains a reference, as in a fork.
+  - Every insert or match is one use: the entries it walks get a fresh
+    stamp. The next entry to evict is, among entries with no child entry
+    whose block only the cache holds, the one with the oldest stamp, the
+    deepest first on a tie (a use stamps one chain, so stamp and depth
+    single one entry out). Evicting drops the entry and its reference, and
+    the block goes back to the free list.
+  - An allocation that finds no free block evicts one entry first. An
+    append checks up front that free blocks plus the entries that eviction
+    could reach (entries whose whole subtree only the cache holds) cover
+    what it needs; else OOMError and no change.
+  - The cache holds at most ``cache_capacity`` entries (default: the pool's
+    block count). An insert that finds it full evicts as above, never an
+    entry this insert has walked; with nothing to evict it stops.
 """
 
 from __future__ import annotations
@@ -75,10 +101,16 @@ class OraclePool:
         self.mat: Dict[int, List[Tuple[np.ndarray, np.ndarray]]] = {}
         self._next_sid = 0
         self.cow_log: List[Tuple[int, int, int]] = []   # every (src, dst, n_valid)
+        # prompt cache: entry id -> record; (parent entry id or -1, tokens) -> entry id
+        self.cache_capacity = num_blocks
+        self.entries: Dict[int, dict] = {}
+        self.entry_of: Dict[Tuple[int, Tuple[int, ...]], int] = {}
+        self._next_eid = 0
+        self._clock = 0
 
     # ----------------------------------------------------------- internals
     def _alloc(self) -> int:
-        if not self.free_blocks:
+        if not self.free_blocks and not self._evict_one():
             raise OOMError("pool exhausted")
         b = min(self.free_blocks, key=self.rank.__getitem__)
         self.free_blocks.remove(b)
@@ -91,11 +123,115 @@ class OraclePool:
 
     def _snapshot(self):
         return (set(self.free_blocks), list(self.ref), copy.deepcopy(self.tables),
-                dict(self.lens), len(self.cow_log))
+                dict(self.lens), len(self.cow_log), copy.deepcopy(self.entries),
+                dict(self.entry_of))
 
     def _restore(self, snap) -> None:
-        self.free_blocks, self.ref, self.tables, self.lens, ncow = snap
+        self.free_blocks, self.ref, self.tables, self.lens, ncow, self.entries, self.entry_of = snap
         del self.cow_log[ncow:]
+
+    # ----------------------------------------------------------- prompt cache
+    def _children(self, eid: int) -> List[int]:
+        return [e for e, r in self.entries.items() if r["parent"] == eid]
+
+    def _victim(self, spare_stamp: Optional[int] = None) -> Optional[int]:
+        """The entry eviction takes next, or None."""
+        best = None
+        for e, r in self.entries.items():
+            if self._children(e) or self.ref[r["block"]] != 1 or r["stamp"] == spare_stamp:
+                continue
+            key = (r["stamp"], -r["depth"])
+            if best is None or key < best[0]:
+                best = (key, e)
+        return None if best is None else best[1]
+
+    def _drop_entry(self, eid: int) -> None:
+        r = self.entries.pop(eid)
+        del self.entry_of[(r["parent"], r["tokens"])]
+        b = r["block"]
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free_blocks.add(b)
+
+    def _evict_one(self, spare_stamp: Optional[int] = None) -> bool:
+        e = self._victim(spare_stamp)
+        if e is None:
+            return False
+        self._drop_entry(e)
+        return True
+
+    def evictable(self) -> int:
+        """How many entries repeated eviction could remove now: those whose
+        whole subtree of entries holds blocks only the cache holds."""
+        def ok(e):
+            return self.ref[self.entries[e]["block"]] == 1 and all(ok(c) for c in self._children(e))
+        return sum(1 for e in self.entries if ok(e))
+
+    def cache_insert(self, sid: int, tokens: Sequence[int]) -> int:
+        """Cache the full blocks of ``sid`` among its first len(tokens)
+        positions, ``tokens`` being their ids. Returns the new entry count."""
+        self._check(sid)
+        tokens = [int(t) for t in tokens]
+        if len(tokens) > self.lens[sid]:
+            raise InvalidError("more token ids than the sequence holds")
+        bs = self.block_size
+        self._clock += 1
+        stamp = self._clock
+        parent, added = -1, 0
+        k = v = None
+        for i in range(len(tokens) // bs):
+            key = (parent, tuple(tokens[i * bs:(i + 1) * bs]))
+            if key in self.entry_of:
+                parent = self.entry_of[key]
+                self.entries[parent]["stamp"] = stamp
+                continue
+            if len(self.entries) >= self.cache_capacity and not self._evict_one(stamp):
+                break
+            if k is None:
+                k, v = self.kv(sid)
+            b = self.tables[sid][i]
+            eid = self._next_eid
+            self._next_eid += 1
+            depth = 1 if parent == -1 else self.entries[parent]["depth"] + 1
+            kv = (np.array(k[:, i * bs:(i + 1) * bs], copy=True),
+                  np.array(v[:, i * bs:(i + 1) * bs], copy=True))
+            for a in kv:
+                a.flags.writeable = False
+            self.entries[eid] = {"parent": parent, "tokens": key[1], "block": b, "depth": depth,
+                                 "stamp": stamp, "kv": kv}
+            self.entry_of[key] = eid
+            self.ref[b] += 1
+            parent = eid
+            added += 1
+        return added
+
+    def cache_match(self, tokens: Sequence[int], sid: Optional[int] = None) -> Tuple[int, int]:
+        """A new sequence holding the longest cached chain of whole blocks
+        that ``tokens`` starts with. Returns (sid, tokens matched)."""
+        tokens = [int(t) for t in tokens]
+        bs = self.block_size
+        self._clock += 1
+        stamp = self._clock
+        chain, parent = [], -1
+        for i in range(len(tokens) // bs):
+            e = self.entry_of.get((parent, tuple(tokens[i * bs:(i + 1) * bs])))
+            if e is None:
+                break
+            self.entries[e]["stamp"] = stamp
+            chain.append(e)
+            parent = e
+        s = self.create(sid)
+        for e in chain:
+            b = self.entries[e]["block"]
+            self.tables[s].append(b)
+            self.ref[b] += 1
+        self.lens[s] = len(chain) * bs
+        self.mat[s] = [self.entries[e]["kv"] for e in chain]
+        return s, len(chain) * bs
+
+    def cache_clear(self) -> None:
+        for e in list(self.entries):
+            self._drop_entry(e)
 
     # ----------------------------------------------------------- verbs
     def create(self, sid: Optional[int] = None) -> int:
@@ -130,6 +266,11 @@ class OraclePool:
         if n == 0:
             return [], []
         bs = self.block_size
+        ln = self.lens[sid]
+        copies = 1 if ln % bs and self.ref[self.tables[sid][-1]] > 1 else 0
+        need = copies + (ln + n + bs - 1) // bs - (ln + bs - 1) // bs
+        if need > len(self.free_blocks) and need > len(self.free_blocks) + self.evictable():
+            raise OOMError("pool exhausted")
         snap = self._snapshot()
         try:
             table = self.tables[sid]

@@ -235,6 +235,9 @@ def check_invariants(pool: OraclePool):
         assert len(set(t)) == len(t)
         for b in t:
             counts[b] += 1
+    for r in pool.entries.values():                              # prompt-cache references
+        counts[r["block"]] += 1
+        assert r["parent"] == -1 or r["parent"] in pool.entries
     assert counts == pool.ref                                    # I1
     used = {b for b in range(pool.num_blocks) if pool.ref[b] > 0}
     assert used.isdisjoint(pool.free_blocks)                     # I2
@@ -617,4 +620,190 @@ def test_commit_that_runs_out_of_blocks_changes_nothing():
             pool.length(s)) == snap
     k1, v1 = pool.kv(s)
     assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    check_invariants(pool)
+
+
+# ------------------------------------------------------ prompt cache (f3)
+
+def _tok_pool(nb=32, bs=4, cap=None):
+    pool = OraclePool(nb, bs)
+    if cap is not None:
+        pool.cache_capacity = cap
+    return pool
+
+
+def _grow(pool, sid, n, rng=None):
+    """Append n tokens with K/V drawn from rng (zeros without one)."""
+    if rng is None:
+        k = np.zeros((1, n, 1, 2), np.float32)
+        pool.append(sid, k, k)
+        return
+    kv = rng.standard_normal((2, 1, n, 1, 2)).astype(np.float32)
+    pool.append(sid, kv[0], kv[1])
+
+
+def _chain_tokens(pool, eid):
+    out = []
+    while eid != -1:
+        r = pool.entries[eid]
+        out = list(r["tokens"]) + out
+        eid = r["parent"]
+    return out
+
+
+def test_match_is_the_longest_cached_prefix_by_brute_force():
+    """After random inserts (and the evictions a small pool forces), a match
+    returns exactly the longest cached token prefix of the query, found by
+    spelling out every entry's chain."""
+    rng = np.random.default_rng(0)
+    bs = 2
+    pool = _tok_pool(nb=40, bs=bs)
+    seqs = {}
+    for step in range(60):
+        toks = [int(t) for t in rng.integers(0, 3, size=int(rng.integers(1, 12)))]
+        try:
+            sid, m = pool.cache_match(toks)
+            _grow(pool, sid, len(toks) - m)
+        except oracle.OOMError:
+            continue
+        pool.cache_insert(sid, toks)
+        seqs[sid] = toks
+        if len(seqs) > 3:
+            victim = sorted(seqs)[int(rng.integers(len(seqs)))]
+            pool.free(victim)
+            del seqs[victim]
+        check_invariants(pool)
+        q = [int(t) for t in rng.integers(0, 3, size=int(rng.integers(0, 14)))]
+        best, best_blocks = 0, []
+        for e in pool.entries:
+            spelled = _chain_tokens(pool, e)
+            if len(spelled) > best and q[:len(spelled)] == spelled:
+                best = len(spelled)
+                chain, x = [], e
+                while x != -1:
+                    chain.append(pool.entries[x]["block"])
+                    x = pool.entries[x]["parent"]
+                best_blocks = chain[::-1]
+        sid, m = pool.cache_match(q)
+        assert m == best and pool.table(sid) == best_blocks
+        pool.free(sid)
+
+
+def test_resumed_sequence_equals_one_computed_in_full():
+    """Match, then append only the unmatched tail: the sequence holds the
+    same K/V, token for token, as one built by appending everything."""
+    rng = np.random.default_rng(1)
+    bs = 4
+    pool = _tok_pool(nb=64, bs=bs)
+    sys_prompt = list(range(100, 122))                    # 22 tokens: 5 full blocks + 2
+    a = pool.create()
+    kv = rng.standard_normal((2, 1, 30, 1, 2)).astype(np.float32)
+    pool.append(a, kv[0][:, :22], kv[1][:, :22])
+    assert pool.cache_insert(a, sys_prompt) == 5
+    ka, va = pool.kv(a)
+    b, m = pool.cache_match(sys_prompt + [7, 8, 9])
+    assert m == 20 and pool.table(b) == pool.table(a)[:5]
+    pool.append(b, kv[0][:, 20:25], kv[1][:, 20:25])  # the unmatched tail, recomputed
+    full = pool.create()
+    pool.append(full, kv[0][:, :25], kv[1][:, :25])
+    kb, vb = pool.kv(b)
+    kf, vf = pool.kv(full)
+    assert np.array_equal(kb, kf) and np.array_equal(vb, vf)
+    assert np.array_equal(kb[:, :22], ka) and np.array_equal(vb[:, :22], va)
+    check_invariants(pool)
+
+
+def test_parked_blocks_outlive_their_sequence():
+    pool = _tok_pool(nb=8, bs=4)
+    a = pool.create()
+    _grow(pool, a, 10)
+    assert pool.cache_insert(a, list(range(10))) == 2     # two full blocks
+    blocks = pool.table(a)
+    pool.free(a)
+    assert pool.ref[blocks[0]] == pool.ref[blocks[1]] == 1 and blocks[2] in pool.free_blocks
+    b, m = pool.cache_match(list(range(10)))
+    assert m == 8 and pool.table(b) == blocks[:2]
+    assert pool.ref[blocks[0]] == 2
+    check_invariants(pool)
+
+
+def test_eviction_order_by_hand():
+    """bs 2, 6 blocks. A = tokens 1..4 (entries a1 -> a2, stamp 1), B = 5, 6
+    (entry b1, stamp 2), then a match of 1, 2 re-stamps a1 (stamp 3). With A
+    and B freed, four allocations evict a2 (oldest leaf), b1, then a1 (a
+    leaf once a2 is gone), and the fourth takes the last free block."""
+    pool = _tok_pool(nb=6, bs=2)
+    a = pool.create()
+    _grow(pool, a, 4)                       # blocks 0, 1
+    b = pool.create()
+    _grow(pool, b, 2)                       # block 2
+    assert pool.cache_insert(a, [1, 2, 3, 4]) == 2
+    assert pool.cache_insert(b, [5, 6]) == 1
+    m, n = pool.cache_match([1, 2, 9])
+    assert n == 2 and pool.table(m) == [0]
+    pool.free(m)
+    pool.free(a)
+    pool.free(b)
+    assert sorted(pool.free_blocks) == [3, 4, 5] and pool.evictable() == 3
+    c = pool.create()
+    _grow(pool, c, 6)                       # takes 3, 4, 5: no eviction
+    assert pool.table(c) == [3, 4, 5] and len(pool.entries) == 3
+    _grow(pool, c, 2)                       # evicts a2 -> block 1
+    assert pool.table(c)[-1] == 1 and len(pool.entries) == 2
+    _grow(pool, c, 2)                       # evicts b1 -> block 2
+    assert pool.table(c)[-1] == 2
+    _grow(pool, c, 2)                       # evicts a1 -> block 0
+    assert pool.table(c)[-1] == 0 and not pool.entries
+    with pytest.raises(oracle.OOMError):
+        _grow(pool, c, 1)
+    check_invariants(pool)
+
+
+def test_blocks_in_use_are_never_evicted():
+    pool = _tok_pool(nb=4, bs=2)
+    a = pool.create()
+    _grow(pool, a, 4)
+    pool.cache_insert(a, [1, 2, 3, 4])      # a still holds both blocks
+    b = pool.create()
+    _grow(pool, b, 4)                       # blocks 2, 3
+    assert pool.evictable() == 0
+    snap = (pool.table(a), pool.table(b), list(pool.ref), set(pool.free_blocks), len(pool.entries))
+    with pytest.raises(oracle.OOMError):
+        _grow(pool, b, 1)
+    assert (pool.table(a), pool.table(b), list(pool.ref), set(pool.free_blocks),
+            len(pool.entries)) == snap
+    pool.free(a)                            # now both entries can go, leaf first
+    assert pool.evictable() == 2
+    _grow(pool, b, 1)
+    assert pool.table(b)[-1] == 1 and len(pool.entries) == 1
+    check_invariants(pool)
+
+
+def test_capacity_stops_an_insert_and_spares_its_own_chain():
+    pool = _tok_pool(nb=16, bs=2, cap=2)
+    a = pool.create()
+    _grow(pool, a, 6)
+    assert pool.cache_insert(a, [1, 2, 3, 4, 5, 6]) == 2  # third block: nothing to evict
+    pool.free(a)                                          # block 2 goes back to the free list
+    b = pool.create()
+    _grow(pool, b, 2)                                     # and b takes it
+    assert pool.cache_insert(b, [7, 8]) == 1              # evicts the older leaf (block 1)
+    assert sorted(r["block"] for r in pool.entries.values()) == [0, 2]
+    _, n = pool.cache_match([1, 2, 3, 4])
+    assert n == 2
+    check_invariants(pool)
+
+
+def test_insert_refreshes_existing_entries_and_clear_releases_all():
+    pool = _tok_pool(nb=16, bs=2)
+    a = pool.create()
+    _grow(pool, a, 4)
+    b = pool.fork(a)
+    assert pool.cache_insert(a, [1, 2, 3, 4]) == 2
+    assert pool.cache_insert(b, [1, 2, 3, 4]) == 0        # same keys: refreshed, not added
+    assert pool.ref[pool.table(a)[0]] == 3
+    pool.cache_clear()
+    assert not pool.entries and pool.ref[pool.table(a)[0]] == 2
+    with pytest.raises(oracle.InvalidError):
+        pool.cache_insert(a, [1, 2, 3, 4, 5])             # more ids than tokens
     check_invariants(pool)
