@@ -19,8 +19,11 @@ kernel alone: the same bytes over its average duration, measured with HIP
 events on the launch stream. ``cpu_baseline`` times the CPU oracle on a
 sample of layers of the same inputs.
 
-Other workloads (``--workload mcts|agent|verify``) time the attention call
-alone on those trees; they are measurements, not the headline line.
+Other workloads (``--workload mcts|agent|verify|prompt_cache``) time the
+attention call alone on those trees; they are measurements, not the
+headline line. ``verify`` also times draft-tree commits; ``prompt_cache``
+builds the agent tree by resuming from the prompt cache and reports the
+cache's host latency and the prompt tokens it saves.
 """
 
 from __future__ import annotations
@@ -269,10 +272,23 @@ def run_tree(args, pkv, torch):
             c.free(h.pop(op.sid))
     seqs = [h[s] for s in w.query_sids]
     q = to_dev(inp.q)
-    uniq_bytes = unique_tokens(c, seqs) * sh.token_kv_bytes * sh.L
+    res = time_attention(args, c, seqs, q, w, torch, f"{w.name}: {w.note}",
+                         inp.parents if w.kind == "verify" else None)
     if w.kind == "verify":
+        res["commit"] = commit_leg(
+            c, seqs, w, inp, lambda: c.verify(seqs, inp.parents, q, scale=w.softmax_scale), torch)
+    c.close()
+    return res
+
+
+def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
+    """Times decode (or, with parents, verify) over seqs: wall time per call
+    and each kernel's device time from HIP events."""
+    sh = w.shape
+    uniq_bytes = unique_tokens(c, seqs) * sh.token_kv_bytes * sh.L
+    if parents is not None:
         out = torch.empty((len(seqs), w.n_nodes, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
-        fn = lambda: c.verify(seqs, inp.parents, q, scale=w.softmax_scale, out=out)  # noqa: E731
+        fn = lambda: c.verify(seqs, parents, q, scale=w.softmax_scale, out=out)  # noqa: E731
         n_queries = len(seqs) * w.n_nodes
     else:
         out = torch.empty((sh.L, len(seqs), sh.Hq, sh.D), dtype=torch.float32, device="cuda")
@@ -303,23 +319,64 @@ def run_tree(args, pkv, torch):
     kernel = "+".join(parts)
     attn_s = (kt["attention"] + kt["attention_wide"]) / 1e3
     achieved = uniq_bytes / attn_s / 1e9
-    res = {
+    return {
         "metric": METRIC, "value": round(uniq_bytes / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.note}", "parallelism": "single GPU"},
+        "config": {"workload": workload, "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * uniq_bytes / dt / 1e9 / HBM_PEAK_GBS, 2),
         "branch_queries_per_s": round(n_queries / dt, 1),
         "unique_kv_bytes_per_step": uniq_bytes,
         "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
-        "plan": c.plan_info(seqs) if w.kind == "decode" else None,
+        "plan": c.plan_info(seqs) if parents is None else None,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, kernel)},
     }
-    if w.kind == "verify":
-        res["commit"] = commit_leg(c, seqs, w, inp, fn, torch)
+
+
+def run_prompt_cache(args, pkv, torch):
+    """The agent workload's tree built through the prompt cache instead of
+    forks: agent 0 computes the system prompt and snapshots it; agents 1-3
+    resume from the longest cached prefix of their own prompt and compute
+    only the rest. Reports the cache's host latency and the prompt tokens
+    it saves, then times decode over the four agents."""
+    from workloads import get
+    w = get("agent")
+    sh = w.shape
+    n_sys, n_agents, n_priv = 13312, 4, 32768
+    c = pkv.PagedKVCache(w.num_blocks_bound() + 8, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D, dtype=sh.dtype)
+    rng = np.random.default_rng(3)
+    system = rng.integers(0, 32000, size=n_sys).astype(np.int32)
+    prompts = [np.concatenate([system, rng.integers(0, 32000, size=n_priv).astype(np.int32)])
+               for _ in range(n_agents)]
+    kv = torch.randn((sh.L, n_sys + n_priv, sh.Hkv, sh.D), device="cuda").to(torch.bfloat16)
+    seqs, computed, match_s, insert_s = [], 0, [], []
+    for a in range(n_agents):
+        t0 = time.perf_counter()
+        s, m = c.cache_match(prompts[a])
+        match_s.append(time.perf_counter() - t0)
+        n = len(prompts[a]) - m
+        c.append([s], [n], kv[:, m:].contiguous(), kv[:, m:].contiguous())
+        computed += n
+        t0 = time.perf_counter()
+        c.cache_insert(s, prompts[a])
+        insert_s.append(time.perf_counter() - t0)
+        seqs.append(s)
+    torch.cuda.synchronize()
+    total = sum(len(p) for p in prompts)
+    q = torch.randn((sh.L, n_agents, sh.Hq, sh.D), device="cuda").to(torch.bfloat16)
+    res = time_attention(args, c, seqs, q, w, torch,
+                         f"agents resumed from the prompt cache: {n_agents} x ({n_sys} cached "
+                         f"system-prompt tokens + {n_priv} own tokens), block_size {sh.BS}")
+    entries, _ = c.cache_info()
+    res["prompt_cache"] = {
+        "prompt_tokens_computed": computed, "prompt_tokens_total": total,
+        "saved_pct": round(100 * (1 - computed / total), 1), "entries": entries,
+        "match_us_median": round(1e6 * float(np.median(match_s[1:])), 1),
+        "insert_us_median": round(1e6 * float(np.median(insert_s)), 1),
+        "blocks_per_prompt": len(prompts[0]) // sh.BS}
     c.close()
     return res
 
@@ -375,7 +432,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="beam", choices=["beam", "mcts", "agent", "verify"])
+    ap.add_argument("--workload", default="beam",
+                    choices=["beam", "mcts", "agent", "verify", "prompt_cache"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -393,6 +451,8 @@ def main():
     torch.cuda.set_device(0)
     if args.workload == "beam":
         res = run_beam(args, pkv, torch)
+    elif args.workload == "prompt_cache":
+        res = run_prompt_cache(args, pkv, torch)
     else:
         res = run_tree(args, pkv, torch)
     print(json.dumps(res), flush=True)

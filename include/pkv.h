@@ -265,6 +265,47 @@ int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t*
                     const int32_t* accepted, int32_t n_accepted, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* ------------------------------------------------------- prompt cache */
+
+/* A cache of full blocks for resuming conversations from their longest
+ * cached prefix (Ferrite page, section 07: snapshots at turn boundaries,
+ * resume from the longest match, a system prompt shared by several agents
+ * computed once, parked conversations). An entry is one full block keyed by
+ * its block_size token ids and by the entry of the block before it, so a
+ * chain of entries from the root spells out a whole token prefix; keys are
+ * compared exactly. An entry holds one reference on its block, so a cached
+ * block outlives the sequence that wrote it.
+ *
+ * Eviction: the next entry to go is, among entries with no child entry
+ * whose block only the cache holds (reference count 1), the one walked
+ * least recently by an insert or match (the deepest on a tie). An
+ * allocation that finds no free block evicts one entry first; an append is
+ * refused with PKV_E_OOM (and changes nothing) unless the free blocks plus
+ * the entries eviction could reach cover it. Host only; no device work. */
+
+/* Caches seq's full blocks among its first n_tokens positions, tokens[i]
+ * being the id of the token at position i (n_tokens <= the sequence's
+ * length). A key already present is refreshed, not duplicated. With the
+ * cache at its capacity ("prefix_cache_blocks") an insert evicts as above,
+ * never an entry it has walked, and stops when nothing can go. n_added
+ * (may be NULL) receives the number of new entries. */
+int pkv_prefix_insert(pkv_pool* pool, pkv_seq seq, const int32_t* tokens, int32_t n_tokens,
+                      int32_t* n_added);
+
+/* Creates a sequence holding the longest chain of cached blocks whose token
+ * ids begin tokens[0 .. n_tokens) (whole blocks only; possibly none): each
+ * block gains a reference, as in a fork. n_matched receives its length, a
+ * multiple of block_size; the caller appends the rest. */
+int pkv_prefix_match(pkv_pool* pool, const int32_t* tokens, int32_t n_tokens, pkv_seq* out,
+                     int32_t* n_matched);
+
+/* Drops every entry (releasing the cache's references). */
+int pkv_prefix_clear(pkv_pool* pool);
+
+/* Entries held, and how many of them eviction could remove now (either
+ * pointer may be NULL). */
+int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
+
 /* ---------------------------------------------------------------- misc */
 
 /* Tuning knobs of the attention planner (defaults in parentheses):
@@ -284,6 +325,8 @@ int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t*
  *   "short_items"       1: a narrow item of at most 16 rows and 64 tokens runs on
  *                       one wave (four such planes per workgroup) instead of four
  *                       waves that split its steps and merge (0: always four)
+ *   "prefix_cache_blocks" num_blocks: most entries the prompt cache holds
+ *                       (0..num_blocks; applies to later inserts)
  *   "concurrent"        0: 1 runs the wide-item launch on a second stream of the
  *                       library's, forked from and joined back into the caller's
  *                       stream, beside the narrow-item launch

@@ -241,6 +241,36 @@ def pkv_tree_commit(pool, seq: PkvSeq, parents, accepted, ws, stream=None) -> No
                               _stream(stream)))
 
 
+def _tokens(tokens):
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    buf = t if t.size else np.zeros(1, dtype=np.int32)
+    return t.size, buf, buf.ctypes.data_as(ctypes.POINTER(c_int32))
+
+
+def pkv_prefix_insert(pool, seq: PkvSeq, tokens) -> int:
+    n, _buf, ptr = _tokens(tokens)
+    added = c_int32()
+    check(lib.pkv_prefix_insert(pool, seq, ptr, n, byref(added)))
+    return added.value
+
+
+def pkv_prefix_match(pool, tokens) -> Tuple[PkvSeq, int]:
+    n, _buf, ptr = _tokens(tokens)
+    out, matched = PkvSeq(), c_int32()
+    check(lib.pkv_prefix_match(pool, ptr, n, byref(out), byref(matched)))
+    return out, matched.value
+
+
+def pkv_prefix_clear(pool) -> None:
+    check(lib.pkv_prefix_clear(pool))
+
+
+def pkv_prefix_info(pool) -> Tuple[int, int]:
+    entries, evictable = c_int32(), c_int32()
+    check(lib.pkv_prefix_info(pool, byref(entries), byref(evictable)))
+    return entries.value, evictable.value
+
+
 def pkv_last_error() -> str:
     return lib.pkv_last_error().decode(errors="replace")
 
@@ -314,6 +344,19 @@ class PagedKVCache:
 
     def truncate(self, seq: PkvSeq, new_len: int) -> None:
         pkv_seq_truncate(self.handle, seq, new_len)
+
+    # prompt cache
+    def cache_insert(self, seq: PkvSeq, tokens) -> int:
+        return pkv_prefix_insert(self.handle, seq, tokens)
+
+    def cache_match(self, tokens) -> Tuple[PkvSeq, int]:
+        return pkv_prefix_match(self.handle, tokens)
+
+    def cache_clear(self) -> None:
+        pkv_prefix_clear(self.handle)
+
+    def cache_info(self) -> Tuple[int, int]:
+        return pkv_prefix_info(self.handle)
 
     def refcount(self, block: int) -> int:
         return pkv_block_refcount(self.handle, block)

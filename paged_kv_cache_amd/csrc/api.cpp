@@ -713,6 +713,8 @@ int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t*
   if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
   const pkv_pool_desc& d = pool->pool.desc();
   if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  if (!append_supported(d.block_size))
+    return fail(PKV_E_UNSUPPORTED, "commit: block_size must be 16, 32 or 64");
   if (n_nodes < 1 || n_nodes > 64) return fail(PKV_E_INVALID, "commit: n_nodes must be 1..64");
   if (n_accepted < 0 || n_accepted > n_nodes)
     return fail(PKV_E_INVALID, "commit: n_accepted outside [0, n_nodes]");
@@ -736,57 +738,69 @@ int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t*
     return fail(PKV_E_WORKSPACE, "commit: workspace too small");
   const int64_t bs = d.block_size;
   const int32_t ctx = s->len - n_nodes;
-  // all or nothing: the re-append needs a copy of a shared partly filled
-  // context tail and blocks for the tokens past it; the truncation frees
-  // the tree's blocks that only this sequence holds
-  {
-    const int32_t keep = (int32_t)((ctx + bs - 1) / bs);
-    int64_t freed = 0;
-    for (size_t i = (size_t)keep; i < s->blocks.size(); ++i) {
-      int32_t rcnt = 0;
-      pool->pool.refcount(s->blocks[i], &rcnt);
-      freed += rcnt == 1 ? 1 : 0;
-    }
-    int64_t needed = 0;
-    if (n_accepted > 0) {
-      const int32_t r = (int32_t)(ctx % bs);
-      int32_t tail_rc = 0;
-      if (r != 0) pool->pool.refcount(s->blocks[(size_t)keep - 1], &tail_rc);
-      needed += (r != 0 && tail_rc > 1) ? 1 : 0;
-      const int64_t room = r != 0 ? bs - r : 0;
-      if (n_accepted > room) needed += (n_accepted - room + bs - 1) / bs;
-    }
-    pkv_stats st;
-    pool->pool.stats(&st);
-    if (needed > st.free_blocks + freed) return fail(PKV_E_OOM, "commit: pool exhausted");
+  GatherParams g{};
+  for (int32_t i = 0; i < n_accepted; ++i) {
+    const int64_t pos = (int64_t)ctx + accepted[i];
+    g.slots[i] = (int64_t)s->blocks[(size_t)(pos / bs)] * bs + pos % bs;
   }
+  // tables first (all or nothing); the device work below reads the kept
+  // nodes before the re-append overwrites or frees their slots
+  std::vector<int64_t> slots;
+  std::vector<pkv_cow_op> cows;
+  if ((rc = pool->pool.truncate_append(seq, ctx, n_accepted, &slots, &cows))) return rc;
+  if (n_accepted == 0) return PKV_OK;
   hipStream_t strm = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   const size_t half = need / 2;
-  if (n_accepted > 0) {
-    GatherParams g{};
-    g.k_arena = d.k_arena;
-    g.v_arena = d.v_arena;
-    g.k_out = w;
-    g.v_out = w + half;
-    g.n = n_accepted;
-    g.L = d.num_layers;
-    g.NB = d.num_blocks;
-    g.Hkv = d.num_kv_heads;
-    g.D = d.head_dim;
-    g.BS = d.block_size;
-    for (int32_t i = 0; i < n_accepted; ++i) {
-      const int64_t pos = (int64_t)ctx + accepted[i];
-      g.slots[i] = (int64_t)s->blocks[(size_t)(pos / bs)] * bs + pos % bs;
-    }
-    rc = pool->timed(
-        T_GATHER, [&](const LaunchEvents& ev) { return launch_gather(d.kv_dtype, g, strm, ev); },
-        "gather launch");
-    if (rc) return rc;
-  }
-  if ((rc = pool->pool.seq_truncate(seq, ctx))) return rc;
-  if (n_accepted == 0) return PKV_OK;
-  return pkv_append_kv_batch(pool, &seq, &n_accepted, 1, w, w + half, stream);
+  g.k_arena = d.k_arena;
+  g.v_arena = d.v_arena;
+  g.k_out = w;
+  g.v_out = w + half;
+  g.n = n_accepted;
+  g.L = d.num_layers;
+  g.NB = d.num_blocks;
+  g.Hkv = d.num_kv_heads;
+  g.D = d.head_dim;
+  g.BS = d.block_size;
+  rc = pool->timed(
+      T_GATHER, [&](const LaunchEvents& ev) { return launch_gather(d.kv_dtype, g, strm, ev); },
+      "gather launch");
+  if (rc) return rc;
+  return enqueue_append(pool, cows.data(), (int32_t)cows.size(), slots.data(),
+                        (int32_t)slots.size(), w, w + half, strm);
+  PKV_GUARD_END
+}
+
+int pkv_prefix_insert(pkv_pool* pool, pkv_seq seq, const int32_t* tokens, int32_t n_tokens,
+                      int32_t* n_added) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.prefix_insert(seq, tokens, n_tokens, n_added);
+  PKV_GUARD_END
+}
+
+int pkv_prefix_match(pkv_pool* pool, const int32_t* tokens, int32_t n_tokens, pkv_seq* out,
+                     int32_t* n_matched) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.prefix_match(tokens, n_tokens, out, n_matched);
+  PKV_GUARD_END
+}
+
+int pkv_prefix_clear(pkv_pool* pool) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  pool->pool.prefix_clear();
+  return PKV_OK;
+  PKV_GUARD_END
+}
+
+int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  if (entries) *entries = pool->pool.prefix_entries();
+  if (evictable) *evictable = pool->pool.prefix_evictable();
+  return PKV_OK;
   PKV_GUARD_END
 }
 
@@ -933,6 +947,8 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "short_items") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "short_items must be 0 or 1");
     pool->opt.short_items = value != 0;
+  } else if (k == "prefix_cache_blocks") {
+    return pool->pool.set_prefix_capacity(value);
   } else if (k == "concurrent") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "concurrent must be 0 or 1");
     pool->concurrent = (int)value;

@@ -67,6 +67,17 @@ void FreeSet::insert(int rank) {
   ++count_;
 }
 
+void FreeSet::erase(int rank) {
+  int i = rank;
+  for (size_t k = 0; k < lv_.size(); ++k) {
+    uint64_t& w = lv_[k][i / 64];
+    w &= ~(1ull << (i % 64));
+    if (w != 0) break;
+    i /= 64;
+  }
+  --count_;
+}
+
 bool FreeSet::contains(int rank) const { return (lv_[0][rank / 64] >> (rank % 64)) & 1ull; }
 
 // --------------------------------------------------------------------- Pool
@@ -80,9 +91,16 @@ Pool::Pool(const pkv_pool_desc& d) : d_(d) {
   d_.alloc_order = nullptr;  // copied; do not keep the caller's pointer
   ref_.assign(nb, 0);
   free_.init(nb);
+  cache_cap_ = nb;
+}
+
+void Pool::release_ref(int32_t b) {
+  --total_refs_;
+  if (--ref_[b] == 0) free_.insert(rank_of_[b]);
 }
 
 int32_t Pool::take_block() {
+  if (free_.count() == 0) evict_one(0);
   int rank = free_.pop_lowest();
   int32_t b = order_[rank];
   ref_[b] = 1;
@@ -92,7 +110,7 @@ int32_t Pool::take_block() {
 
 int Pool::block_alloc(int32_t* id) {
   if (!id) return fail(PKV_E_INVALID, "block_alloc: null output");
-  if (free_.count() == 0) return fail(PKV_E_OOM, "block_alloc: pool exhausted");
+  if (free_.count() == 0 && !evict_one(0)) return fail(PKV_E_OOM, "block_alloc: pool exhausted");
   *id = take_block();
   ++mutation_;
   return PKV_OK;
@@ -187,6 +205,29 @@ int Pool::seq_truncate(pkv_seq h, int32_t n) {
   return PKV_OK;
 }
 
+int Pool::truncate_append(pkv_seq h, int32_t keep_len, int32_t n_new, std::vector<int64_t>* slots,
+                          std::vector<pkv_cow_op>* cows) {
+  Seq* s = get_mut(h);
+  if (!s) return PKV_E_INVALID;
+  if (keep_len < 0 || keep_len > s->len) return fail(PKV_E_INVALID, "truncate: length outside [0, len]");
+  const int32_t old_len = s->len;
+  const int32_t keep = (int32_t)((keep_len + (int64_t)d_.block_size - 1) / d_.block_size);
+  const std::vector<int32_t> tail(s->blocks.begin() + keep, s->blocks.end());
+  int rc = seq_truncate(h, keep_len);
+  if (rc) return rc;
+  rc = append_plan_batch(&h, &n_new, 1, slots, cows);
+  if (rc == PKV_OK) return rc;
+  // the refused append changed nothing: give the tail back its references
+  for (int32_t b : tail) {
+    if (ref_[b] == 0) free_.erase(rank_of_[b]);
+    ++ref_[b];
+    ++total_refs_;
+  }
+  s->blocks.insert(s->blocks.end(), tail.begin(), tail.end());
+  s->len = old_len;
+  return rc;
+}
+
 int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t n,
                             std::vector<int64_t>* slots, std::vector<pkv_cow_op>* cows) {
   if (n < 0 || (n > 0 && (!seqs || !counts))) return fail(PKV_E_INVALID, "append: bad arguments");
@@ -218,7 +259,7 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
     int64_t before = (s->len + bs - 1) / bs, after = (s->len + counts[i] + bs - 1) / bs;
     need += after - before;
   }
-  if (need > free_.count())
+  if (need > free_.count() && need > (int64_t)free_.count() + prefix_evictable())
     return fail(PKV_E_OOM, "append: pool has " + std::to_string(free_.count()) +
                                " free blocks, the append needs " + std::to_string(need));
   // Pass 2: execute (cannot fail).
@@ -242,6 +283,179 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
     }
   }
   if (need || n) ++mutation_;
+  return PKV_OK;
+}
+
+// ------------------------------------------------------------ prompt cache
+
+namespace {
+uint64_t key_hash(int32_t parent, const int32_t* toks, int n) {
+  uint64_t h = 0x9E3779B97F4A7C15ull ^ (uint64_t)(uint32_t)parent;
+  for (int i = 0; i < n; ++i) {
+    h ^= (uint64_t)(uint32_t)toks[i] + 0x9E3779B97F4A7C15ull + (h << 6) + (h >> 2);
+    h *= 0xFF51AFD7ED558CCDull;
+  }
+  return h ^ (h >> 33);
+}
+}  // namespace
+
+int32_t Pool::find_entry(int32_t parent, const int32_t* toks, uint64_t h) const {
+  const int bs = d_.block_size;
+  auto range = ent_index_.equal_range(h);
+  for (auto it = range.first; it != range.second; ++it) {
+    const int32_t e = it->second;
+    if (ents_[e].parent == parent &&
+        std::equal(toks, toks + bs, ent_tok_.begin() + (size_t)e * bs))
+      return e;
+  }
+  return -1;
+}
+
+bool Pool::evict_one(uint64_t spare_stamp) {
+  int32_t best = -1;
+  for (int32_t e = 0; e < (int32_t)ents_.size(); ++e) {
+    const CacheEntry& r = ents_[e];
+    if (!r.live || r.n_child || ref_[r.block] != 1 || r.stamp == spare_stamp) continue;
+    if (best < 0 || r.stamp < ents_[best].stamp ||
+        (r.stamp == ents_[best].stamp && r.depth > ents_[best].depth))
+      best = e;
+  }
+  if (best < 0) return false;
+  drop_entry(best);
+  return true;
+}
+
+void Pool::drop_entry(int32_t e) {
+  CacheEntry& r = ents_[e];
+  auto range = ent_index_.equal_range(r.hash);
+  for (auto it = range.first; it != range.second; ++it)
+    if (it->second == e) {
+      ent_index_.erase(it);
+      break;
+    }
+  if (r.parent >= 0) --ents_[r.parent].n_child;
+  release_ref(r.block);
+  r.live = false;
+  ent_free_.push_back(e);
+  --n_ent_;
+  ++mutation_;
+}
+
+int32_t Pool::prefix_evictable() const {
+  if (n_ent_ == 0) return 0;
+  // an entry can go once its whole subtree can: visit children before parents
+  std::vector<int32_t> ids;
+  ids.reserve((size_t)n_ent_);
+  for (int32_t e = 0; e < (int32_t)ents_.size(); ++e)
+    if (ents_[e].live) ids.push_back(e);
+  std::sort(ids.begin(), ids.end(),
+            [&](int32_t a, int32_t b) { return ents_[a].depth > ents_[b].depth; });
+  std::vector<uint8_t> blocked(ents_.size(), 0);
+  int32_t n = 0;
+  for (int32_t e : ids) {
+    const CacheEntry& r = ents_[e];
+    const bool ok = !blocked[e] && ref_[r.block] == 1;
+    if (ok)
+      ++n;
+    else if (r.parent >= 0)
+      blocked[r.parent] = 1;
+  }
+  return n;
+}
+
+int Pool::prefix_insert(pkv_seq h, const int32_t* tokens, int32_t n, int32_t* added) {
+  const Seq* s = get(h);
+  if (!s) return PKV_E_INVALID;
+  if (n < 0 || (n > 0 && !tokens)) return fail(PKV_E_INVALID, "prefix_insert: bad token list");
+  if (n > s->len) return fail(PKV_E_INVALID, "prefix_insert: more token ids than the sequence holds");
+  const int bs = d_.block_size;
+  const uint64_t stamp = ++clock_;
+  int32_t parent = -1, count = 0;
+  for (int32_t i = 0; i < n / bs; ++i) {
+    const int32_t* t = tokens + (size_t)i * bs;
+    const uint64_t hk = key_hash(parent, t, bs);
+    int32_t e = find_entry(parent, t, hk);
+    if (e >= 0) {
+      ents_[e].stamp = stamp;
+      parent = e;
+      continue;
+    }
+    if (n_ent_ >= cache_cap_ && !evict_one(stamp)) break;
+    if (!ent_free_.empty()) {
+      e = ent_free_.back();
+      ent_free_.pop_back();
+    } else {
+      e = (int32_t)ents_.size();
+      ents_.emplace_back();
+      ent_tok_.resize(ents_.size() * (size_t)bs);
+    }
+    CacheEntry& r = ents_[e];
+    r.parent = parent;
+    r.block = s->blocks[(size_t)i];
+    r.depth = parent < 0 ? 1 : ents_[parent].depth + 1;
+    r.n_child = 0;
+    r.stamp = stamp;
+    r.hash = hk;
+    r.live = true;
+    std::copy(t, t + bs, ent_tok_.begin() + (size_t)e * bs);
+    if (parent >= 0) ++ents_[parent].n_child;
+    ent_index_.emplace(hk, e);
+    ++ref_[r.block];
+    ++total_refs_;
+    ++n_ent_;
+    parent = e;
+    ++count;
+  }
+  if (count) ++mutation_;
+  if (added) *added = count;
+  return PKV_OK;
+}
+
+int Pool::prefix_match(const int32_t* tokens, int32_t n, pkv_seq* out, int32_t* matched) {
+  if (!out) return fail(PKV_E_INVALID, "prefix_match: null output");
+  if (n < 0 || (n > 0 && !tokens)) return fail(PKV_E_INVALID, "prefix_match: bad token list");
+  const int bs = d_.block_size;
+  const uint64_t stamp = ++clock_;
+  std::vector<int32_t> chain;
+  int32_t parent = -1;
+  for (int32_t i = 0; i < n / bs; ++i) {
+    const int32_t* t = tokens + (size_t)i * bs;
+    const int32_t e = find_entry(parent, t, key_hash(parent, t, bs));
+    if (e < 0) break;
+    ents_[e].stamp = stamp;
+    chain.push_back(e);
+    parent = e;
+  }
+  pkv_seq c;
+  int rc = seq_create(&c);
+  if (rc) return rc;
+  Seq& k = seqs_[c.index];
+  for (int32_t e : chain) {
+    k.blocks.push_back(ents_[e].block);
+    ++ref_[ents_[e].block];
+  }
+  total_refs_ += (int64_t)chain.size();
+  k.len = (int32_t)chain.size() * bs;
+  *out = c;
+  if (matched) *matched = k.len;
+  return PKV_OK;
+}
+
+void Pool::prefix_clear() {
+  for (int32_t e = 0; e < (int32_t)ents_.size(); ++e)
+    if (ents_[e].live) release_ref(ents_[e].block);
+  ents_.clear();
+  ent_tok_.clear();
+  ent_free_.clear();
+  ent_index_.clear();
+  n_ent_ = 0;
+  ++mutation_;
+}
+
+int Pool::set_prefix_capacity(int64_t cap) {
+  if (cap < 0 || cap > d_.num_blocks)
+    return fail(PKV_E_INVALID, "prefix cache capacity outside [0, num_blocks]");
+  cache_cap_ = (int32_t)cap;
   return PKV_OK;
 }
 

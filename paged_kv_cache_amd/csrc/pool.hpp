@@ -11,6 +11,7 @@
 
 #include <cstdint>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "pkv.h"
@@ -30,6 +31,7 @@ class FreeSet {
   int count() const { return count_; }
   int pop_lowest();  // -1 if empty
   void insert(int rank);
+  void erase(int rank);  // rank must be free
   bool contains(int rank) const;
 
  private:
@@ -43,6 +45,18 @@ struct Seq {
   bool live = false;
   int32_t len = 0;
   std::vector<int32_t> blocks;
+};
+
+// A prompt-cache entry: one full block, keyed by its token ids and the
+// entry of the block before it (so a chain from the root spells a prefix).
+struct CacheEntry {
+  int32_t parent = -1;  // entry id, -1 at the root
+  int32_t block = -1;
+  int32_t depth = 0;    // 1 for a prompt's first block
+  int32_t n_child = 0;  // live entries whose parent this is
+  uint64_t stamp = 0;   // the last insert or match that walked it
+  uint64_t hash = 0;
+  bool live = false;
 };
 
 class Pool {
@@ -62,6 +76,22 @@ class Pool {
   // the sequence's tokens lose its reference; a kept partly filled block
   // keeps its count.
   int seq_truncate(pkv_seq s, int32_t n);
+  // Truncates s to keep_len tokens, then plans an append of n_new tokens;
+  // if the append is refused, the truncation is undone (all or nothing).
+  int truncate_append(pkv_seq s, int32_t keep_len, int32_t n_new, std::vector<int64_t>* slots,
+                      std::vector<pkv_cow_op>* cows);
+
+  // Prompt cache (Ferrite page, section 07: resume from the longest match;
+  // parked conversations keep their blocks). Entries hold one reference on
+  // their block. The next entry evicted is, among leaf entries whose block
+  // only the cache holds, the one with the oldest stamp (deepest on a tie).
+  // An allocation that finds no free block evicts one entry first.
+  int prefix_insert(pkv_seq s, const int32_t* tokens, int32_t n, int32_t* added);
+  int prefix_match(const int32_t* tokens, int32_t n, pkv_seq* out, int32_t* matched);
+  void prefix_clear();
+  int32_t prefix_entries() const { return n_ent_; }
+  int32_t prefix_evictable() const;
+  int set_prefix_capacity(int64_t cap);
 
   // Plans appends for seqs[i] += counts[i] tokens, in order, all or nothing.
   // Slots are appended to `slots` in (sequence, token) order; copies to `cows`.
@@ -79,7 +109,12 @@ class Pool {
 
  private:
   Seq* get_mut(pkv_seq s);
-  int32_t take_block();  // caller has checked availability
+  int32_t take_block();  // caller has checked availability (free or evictable)
+  void release_ref(int32_t b);
+
+  int32_t find_entry(int32_t parent, const int32_t* toks, uint64_t h) const;
+  bool evict_one(uint64_t spare_stamp);  // false: nothing evictable
+  void drop_entry(int32_t e);
 
   pkv_pool_desc d_;
   std::vector<int32_t> order_;    // rank -> block id
@@ -91,6 +126,14 @@ class Pool {
   int32_t live_ = 0;
   int64_t total_refs_ = 0;
   uint64_t mutation_ = 0;  // bumped by every table change
+
+  std::vector<CacheEntry> ents_;
+  std::vector<int32_t> ent_tok_;  // block_size token ids per entry slot
+  std::vector<int32_t> ent_free_;
+  std::unordered_multimap<uint64_t, int32_t> ent_index_;
+  int32_t n_ent_ = 0;
+  int32_t cache_cap_ = 0;
+  uint64_t clock_ = 0;
 };
 
 }  // namespace pkv

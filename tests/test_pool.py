@@ -194,6 +194,110 @@ def test_truncate_rejects_bad_lengths(pkv):
         binding.pkv_tree_commit(c.handle, s, [-1], [0], None)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_prompt_cache_traces_bit_exact(pkv, seed):
+    """Random traces that mix the prompt cache (insert, match, clear, a
+    capacity) with forks, appends, truncations and frees in a pool small
+    enough to force evictions: tables, counts, free lists, cache sizes and
+    match results equal the oracle's."""
+    rng = np.random.default_rng(700 + seed)
+    nb = int(rng.integers(16, 48))
+    bs = [1, 2, 4, 16][seed % 4]
+    order = rng.permutation(nb).tolist() if seed % 2 else None
+    cap = [nb, 3, 8, 0][seed % 4] if seed >= 4 else nb
+    c = host_cache(pkv, nb, bs, order)
+    c.set_option("prefix_cache_blocks", cap)
+    pool = OraclePool(nb, bs, alloc_order=order)
+    pool.cache_capacity = cap
+    handles, toks = {}, {}
+    vocab = 3 if bs <= 2 else 2
+
+    def new_ids(n):
+        return [int(t) for t in rng.integers(0, vocab, size=n)]
+
+    for _ in range(300):
+        act = int(rng.integers(8)) if handles else 0
+        if act == 0:
+            q = new_ids(int(rng.integers(0, 3 * bs + 2)))
+            if handles and rng.integers(2):      # resume a known conversation
+                src = toks[list(handles)[rng.integers(len(handles))]]
+                q = src[:int(rng.integers(0, len(src) + 1))] + q
+            sid, m = pool.cache_match(q)
+            hd, m2 = c.cache_match(q)
+            assert m2 == m
+            handles[sid], toks[sid] = hd, q[:m]
+        elif act == 1:
+            p = list(handles)[rng.integers(len(handles))]
+            sid = pool.fork(p)
+            handles[sid], toks[sid] = c.fork(handles[p]), list(toks[p])
+        elif act in (2, 3):
+            sid = list(handles)[rng.integers(len(handles))]
+            n = int(rng.integers(0, 2 * bs + 2))
+            try:
+                want = pool.append(sid, zeros(n), zeros(n))
+            except oracle.OOMError:
+                with pytest.raises(pkv.OOM):
+                    c.plan(handles[sid], n)
+            else:
+                got = c.plan(handles[sid], n)
+                assert got[0] == want[0]
+                assert got[1] == [tuple(x) for x in want[1]]
+                toks[sid] += new_ids(n)
+        elif act == 4:
+            sid = list(handles)[rng.integers(len(handles))]
+            n = int(rng.integers(0, len(toks[sid]) + 1))
+            assert pool.cache_insert(sid, toks[sid][:n]) == c.cache_insert(handles[sid], toks[sid][:n])
+        elif act == 5:
+            sid = list(handles)[rng.integers(len(handles))]
+            n = int(rng.integers(0, pool.length(sid) + 1))
+            pool.truncate(sid, n)
+            c.truncate(handles[sid], n)
+            toks[sid] = toks[sid][:n]
+        elif act == 6:
+            sid = list(handles)[rng.integers(len(handles))]
+            pool.free(sid)
+            c.free(handles.pop(sid))
+            del toks[sid]
+        elif rng.integers(4) == 0:
+            pool.cache_clear()
+            c.cache_clear()
+        compare_state(c, pool, handles)
+        assert c.cache_info() == (len(pool.entries), pool.evictable())
+    for sid in list(handles):
+        pool.free(sid)
+        c.free(handles.pop(sid))
+    c.cache_clear()
+    st = c.stats()
+    assert st["free_blocks"] == nb and st["total_refs"] == 0
+
+
+def test_prompt_cache_eviction_order_matches_hand_derivation(pkv):
+    """The oracle's hand-derived case: evictions free blocks 1, 2, then 0."""
+    c = host_cache(pkv, 6, 2)
+    a, b = c.create(), c.create()
+    c.plan(a, 4)
+    c.plan(b, 2)
+    assert c.cache_insert(a, [1, 2, 3, 4]) == 2 and c.cache_insert(b, [5, 6]) == 1
+    m, n = c.cache_match([1, 2, 9])
+    assert n == 2 and c.table(m) == [0]
+    for s in (m, a, b):
+        c.free(s)
+    assert c.cache_info() == (3, 3)
+    d = c.create()
+    c.plan(d, 6)
+    assert c.table(d) == [3, 4, 5]
+    for want in (1, 2, 0):
+        c.plan(d, 2)
+        assert c.table(d)[-1] == want
+    assert c.cache_info() == (0, 0)
+    with pytest.raises(pkv.OOM):
+        c.plan(d, 1)
+    with pytest.raises(pkv.PkvError):
+        c.cache_insert(d, list(range(13)))      # more ids than tokens
+    with pytest.raises(pkv.PkvError):
+        c.set_option("prefix_cache_blocks", 7)  # above num_blocks
+
+
 @pytest.mark.parametrize("name", ["beam", "mcts", "agent", "verify", "beam_cow"])
 def test_full_size_tables_bit_exact(pkv, name):
     w = get(name)
