@@ -322,9 +322,11 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       own, 1 or 2; with 2 (head_dim <= 128 only) an item of
  *                       up to 32 rows loads each K/V step once, at the cost of
  *                       occupancy
- *   "short_items"       1: a narrow item of at most 16 rows and 64 tokens runs on
- *                       one wave (four such planes per workgroup) instead of four
- *                       waves that split its steps and merge (0: always four)
+ *   "short_items"       1: a narrow item of at most 16 rows and "short_tokens"
+ *                       tokens runs on one wave (four such planes per workgroup)
+ *                       instead of four waves that split its steps and merge
+ *                       (0: always four)
+ *   "short_tokens"      256: see "short_items" (32..8192)
  *   "prefix_cache_blocks" num_blocks: most entries the prompt cache holds
  *                       (0..num_blocks; applies to later inserts)
  *   "concurrent"        0: 1 runs the wide-item launch on a second stream of the

@@ -22,8 +22,9 @@ constexpr int32_t kMaxChunkBlocks = 512;
 
 // A narrow item of at most 16 rows and this many tokens is short: one wave
 // does all of it (four items' planes per workgroup) instead of four waves
-// splitting its steps and merging.
-constexpr int32_t kShortTokens = 64;
+// splitting its steps and merging. (A four-wave item pays its start-up
+// chain of dependent loads and the merge for every few steps it loads.)
+constexpr int32_t kShortTokens = 256;
 
 struct WorkItem {
   int32_t blk_off;    // index in blk[] of the chunk's first block

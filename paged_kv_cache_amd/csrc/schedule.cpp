@@ -159,7 +159,7 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   // (short items, one wave each, last); wide groups also by sibling count,
   // so equal counts sit together
   auto is_short = [&](const WorkItem& w) {
-    return opt.short_items && w.n_rows <= 16 && w.n_tok <= kShortTokens;
+    return opt.short_items && w.n_rows <= 16 && w.n_tok <= opt.short_tokens;
   };
   std::stable_sort(narrow.begin(), narrow.end(), [&](const WorkItem& a, const WorkItem& b) {
     const bool sa = is_short(a), sb = is_short(b);

@@ -25,6 +25,7 @@ struct SchedOptions {
   int32_t tokens_per_row = 40;     // chunk length per query row (keeps partial traffic ~5%)
   int32_t max_row_blocks_per_wave = 1;  // 16-row blocks one narrow wave may own (1 or 2)
   bool short_items = true;         // one wave per plane for short narrow items
+  int32_t short_tokens = kShortTokens;  // longest narrow item (of <= 16 rows) that counts as short
 };
 
 struct Schedule {

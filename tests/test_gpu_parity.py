@@ -69,11 +69,12 @@ SMALL_DECODE = [
 
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
-               row_blocks=1, wide_shape=None, concurrent=0, short_items=1):
+               row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("concurrent", concurrent)
     c.set_option("short_items", short_items)
+    c.set_option("short_tokens", short_tokens)
     if wide_shape:
         c.set_option("wide_waves", wide_shape[0])
         c.set_option("wide_row_blocks", wide_shape[1])
@@ -145,14 +146,16 @@ def test_wide_and_narrow_items_agree(w):
     assert errors(chunked, wide)[0] <= 1e-4
 
 
-@pytest.mark.parametrize("w", [SMALL_DECODE[3], SMALL_DECODE[8]], ids=lambda w: w.name)
-@pytest.mark.parametrize("chunk,pf", [(0, 0), (32, 0), (32, 1)])
-def test_short_items_one_wave_each(w, chunk, pf):
-    """Short narrow items (<= 16 rows, <= 64 tokens) run one (layer, head)
+@pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[3], SMALL_DECODE[4], SMALL_DECODE[8]],
+                         ids=lambda w: w.name)
+@pytest.mark.parametrize("chunk,pf,st", [(0, 0, 64), (0, 0, 256), (0, 0, 8192), (32, 0, 256),
+                                         (32, 1, 256), (0, 1, 8192)])
+def test_short_items_one_wave_each(w, chunk, pf, st):
+    """Short narrow items (<= 16 rows, <= st tokens) run one (layer, head)
     plane per wave; the results match the four-wave form to fp32 rounding
     and the oracle to tolerance."""
-    note(f"short items {w.name} chunk={chunk} prefetch={pf}")
-    inp, a = run_decode(w, chunk_tokens=chunk, prefetch=pf, short_items=1)
+    note(f"short items {w.name} chunk={chunk} prefetch={pf} short_tokens={st}")
+    inp, a = run_decode(w, chunk_tokens=chunk, prefetch=pf, short_items=1, short_tokens=st)
     _, b = run_decode(w, chunk_tokens=chunk, prefetch=pf, short_items=0)
     assert errors(a, b)[0] <= 1e-4
     pool = build_oracle(w, inp)
