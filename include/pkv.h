@@ -335,7 +335,8 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *   "wide_fill"         1: fill every wide item of a chunk but the last to the row
  *                       limit (0: split the rows evenly)
  *   "wide_waves"        0: compute waves per wide workgroup, 4, 6 or 8; 0 picks 8
- *                       (the workgroup adds one or two loader waves)
+ *                       up to head_dim 128 and 6 at 256 (the workgroup adds one
+ *                       or two loader waves)
  *   "wide_row_blocks"   0: 16-row blocks each wide compute wave owns, 1 or 2; 0
  *                       picks 2 up to head_dim 128 and 1 at 256 (6 waves, and 8
  *                       at head_dim 256, always own one); a wide item holds at

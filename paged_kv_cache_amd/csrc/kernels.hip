@@ -711,7 +711,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
     l_run[r] = 0.f;
   }
 
-  auto compute = [&](int step, const u32x4* st_sec) __attribute__((always_inline)) {
+  auto compute_rb2 = [&](int step, const u32x4* st_sec) __attribute__((always_inline)) {
     const int s = step;
     if (nrb > 0) {
       f32x4 sc4[RBW][2];
@@ -779,6 +779,103 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
         }
       }
     }
+  };
+  // One row block per wave: operand reads from LDS run ahead of the
+  // products in register rings (the compiler, left alone, waits for each
+  // ds_read right before its product): K sections QD ahead during Q.K, and
+  // the first VD V sections are issued before the softmax so that their
+  // latency hides under it. (Two row blocks per wave leave no registers for
+  // the rings; that form keeps the compiler's schedule.)
+  constexpr int NK = 2 * KS;
+  constexpr int QD = NK < 8 ? NK : 8;
+  constexpr int VD = DB < 8 ? DB : 8;
+  auto compute_rb1 = [&](int step, const u32x4* st_sec) __attribute__((always_inline)) {
+    const int s = step;
+    if (nrb > 0) {
+      f32x4 sc4[RBW][2];
+#pragma unroll
+      for (int r = 0; r < RBW; ++r)
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) sc4[r][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // K sections in the order (ks, tau): consecutive products alternate
+      // between the two score tiles
+      auto ksec = [](int i) { return (i & 1) * KS + (i >> 1); };
+      u32x4 kring[QD];
+#pragma unroll
+      for (int i = 0; i < QD; ++i) kring[i] = st_sec[ksec(i) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        const bf16x8 a = as_bf16x8(kring[i % QD]);
+        if (i + QD < NK) kring[i % QD] = st_sec[ksec(i + QD) * 64 + lane];
+        const int tau = i & 1, ks = i >> 1;
+#pragma unroll
+        for (int r = 0; r < RBW; ++r) sc4[r][tau] = mfma_bf16(a, qv[r][ks], sc4[r][tau]);
+        if (i + QD < NK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, RBW, 0);
+      }
+      u32x4 vring[VD];
+#pragma unroll
+      for (int i = 0; i < VD; ++i) vring[i] = st_sec[(2 * KS + i) * 64 + lane];
+      __builtin_amdgcn_sched_barrier(0);
+      const int tbase = 32 * s;
+      const bool tail = tbase + 32 > it.n_tok;
+      const int tv = tbase + voff;
+      bf16x8 phi[RBW], plo[RBW];
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) {
+        float sc[8];
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[4 * tau + i] = sc4[r][tau][i] * p.scale_log2;
+        if (tail || tree) {  // wave-uniform: only the chunk's last step and masked steps
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = tv + e;
+            if (t >= it.n_tok) sc[e] = kNegInf;
+            const int pos = it.t0 + t;
+            if (tree && pos >= it.mask_from && !((anc[r] >> (pos - it.mask_from)) & 1ull))
+              sc[e] = kNegInf;
+          }
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        mx = max_xor32(max_xor16(mx));
+        rebase(mx, m_run[r], l_run[r], acc[r]);
+        const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pe = fast_exp2(sc[e] - m_use);
+          psum += pe;
+          const __bf16 h = (__bf16)pe;
+          phi[r][e] = h;
+          plo[r][e] = (__bf16)(pe - (float)h);
+        }
+        l_run[r] += psum;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < DB; ++j) {
+        const bf16x8 a = as_bf16x8(vring[j % VD]);
+        if (j + VD < DB) vring[j % VD] = st_sec[(2 * KS + j + VD) * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < RBW; ++r) {
+          acc[r][j] = mfma_bf16(a, phi[r], acc[r][j]);
+          acc[r][j] = mfma_bf16(a, plo[r], acc[r][j]);
+        }
+        if (j + VD < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RBW, 0);
+      }
+    }
+  };
+  auto compute = [&](int step, const u32x4* st_sec) __attribute__((always_inline)) {
+    if constexpr (RBW == 1)
+      compute_rb1(step, st_sec);
+    else
+      compute_rb2(step, st_sec);
   };
   for (int s = 0; s < n_steps; s += 3) {
     __builtin_amdgcn_s_barrier();
@@ -1172,11 +1269,12 @@ hipError_t launch_valu(int D, int BS, const AttnParams& p, dim3 grid, hipStream_
 }  // namespace
 
 void attn_wide_shape(int D, int* waves, int* row_blocks) {
-  // automatic (waves 0 or row_blocks 0): 8 compute waves, two row blocks
-  // each up to head_dim 128 and one at 256 (where two blocks' accumulators
-  // would not fit next to three waves per SIMD)
+  // automatic (waves 0 or row_blocks 0): 8 compute waves with two row
+  // blocks each up to head_dim 128; at 256 (where two blocks' accumulators
+  // would not fit next to three waves per SIMD) 6 waves of one block, which
+  // measured faster than 8 (each step reads its K/V from LDS once per wave)
   const bool auto_w = !(*waves == 4 || *waves == 6 || *waves == 8);
-  int w = auto_w ? 8 : *waves;
+  int w = auto_w ? (D == 256 ? 6 : 8) : *waves;
   int r = *row_blocks == 1 || *row_blocks == 2 ? *row_blocks : (D <= 128 ? 2 : 1);
   if (w == 6 || (D == 256 && w == 8)) r = 1;
   *waves = w;
