@@ -318,10 +318,14 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *   "prefetch"          0: 1 makes each wave of the narrow kernel load its next
  *                       32-token step while the current one computes (with one
  *                       16-row block per wave)
- *   "row_blocks_per_wave" 1: 16-row blocks one wave of the narrow kernel may
+ *   "row_blocks_per_wave" 0: 16-row blocks one wave of the narrow kernel may
  *                       own, 1 or 2; with 2 (head_dim <= 128 only) an item of
  *                       up to 32 rows loads each K/V step once, at the cost of
- *                       occupancy
+ *                       occupancy; 0 picks 2 when items of more than 16 rows
+ *                       hold at least a quarter of the narrow launch's tokens
+ *   "tokens_per_row"    64: chunk length per query row reading it (between
+ *                       "min_chunk_tokens" and 8192 tokens)
+ *   "min_chunk_tokens"  1024: shortest automatic chunk (32..8192)
  *   "short_items"       1: a narrow item of at most 16 rows and "short_tokens"
  *                       tokens runs on one wave (four such planes per workgroup)
  *                       instead of four waves that split its steps and merge

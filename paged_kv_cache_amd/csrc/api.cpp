@@ -342,9 +342,8 @@ SchedOptions planner_options(const pkv_pool* p, bool mfma) {
     o.max_row_blocks_per_wave = 1;
     o.short_items = false;
   } else {
-    o.max_row_blocks_per_wave = std::min(
-        o.max_row_blocks_per_wave, attn_max_row_blocks_per_wave(p->pool.desc().head_dim));
-    if (p->prefetch) o.max_row_blocks_per_wave = 1;
+    if (attn_max_row_blocks_per_wave(p->pool.desc().head_dim) < 2 || p->prefetch)
+      o.max_row_blocks_per_wave = 1;
     // a wide item holds at most what one workgroup of the wide kernel serves
     int w = p->wide_waves, r = p->wide_row_blocks;
     attn_wide_shape(p->pool.desc().head_dim, &w, &r);
@@ -956,7 +955,7 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "concurrent must be 0 or 1");
     pool->concurrent = (int)value;
   } else if (k == "row_blocks_per_wave") {
-    if (value < 1 || value > 2) return fail(PKV_E_INVALID, "row_blocks_per_wave must be 1 or 2");
+    if (value < 0 || value > 2) return fail(PKV_E_INVALID, "row_blocks_per_wave must be 0, 1 or 2");
     pool->opt.max_row_blocks_per_wave = (int32_t)value;
   } else if (k == "wide_waves") {
     if (value != 0 && value != 4 && value != 6 && value != 8)
@@ -975,6 +974,12 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "timing") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "timing must be 0 or 1");
     pool->timing = value != 0;
+  } else if (k == "tokens_per_row") {
+    if (value < 1 || value > 8192) return fail(PKV_E_INVALID, "tokens_per_row must be 1..8192");
+    pool->opt.tokens_per_row = (int32_t)value;
+  } else if (k == "min_chunk_tokens") {
+    if (value < 32 || value > 8192) return fail(PKV_E_INVALID, "min_chunk_tokens must be 32..8192");
+    pool->opt.min_chunk_tokens = (int32_t)value;
   } else if (k == "target_workgroups") {
     if (value < 1 || value > (1 << 24)) return fail(PKV_E_INVALID, "target_workgroups out of range");
     pool->opt.target_workgroups = (int32_t)value;

@@ -150,9 +150,18 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   // a narrow wave owns two 16-row blocks when some item has more than 16
   // rows (and the head size leaves the registers for it); an item with
   // more rows than one wave owns has several waves loading each step
+  // (automatic: only when such items carry a good share of the bytes, since
+  // two blocks per wave cost every item of the launch an occupancy step)
   int32_t max_rows = 0;
-  for (const WorkItem& w : narrow) max_rows = std::max(max_rows, w.n_rows);
-  S->narrow_rw = (max_rows > 16 && opt.max_row_blocks_per_wave >= 2) ? 2 : 1;
+  int64_t tok_all = 0, tok_big = 0;
+  for (const WorkItem& w : narrow) {
+    max_rows = std::max(max_rows, w.n_rows);
+    tok_all += w.n_tok;
+    tok_big += w.n_rows > 16 ? w.n_tok : 0;
+  }
+  const bool two = opt.max_row_blocks_per_wave == 2 ||
+                   (opt.max_row_blocks_per_wave == 0 && 4 * tok_big >= tok_all);
+  S->narrow_rw = (max_rows > 16 && two) ? 2 : 1;
   for (WorkItem& w : narrow)
     if (w.n_rows > 16 * S->narrow_rw) w.reread = 1;
   // longest chunks first, so the tail of each grid holds the short ones

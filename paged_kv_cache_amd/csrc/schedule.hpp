@@ -22,8 +22,10 @@ struct SchedOptions {
   int32_t target_workgroups = 256;  // shorten chunks while the grid has fewer than 3/4 of this
   int32_t min_chunk_tokens = 1024;
   int32_t max_chunk_tokens = 8192;
-  int32_t tokens_per_row = 40;     // chunk length per query row (keeps partial traffic ~5%)
-  int32_t max_row_blocks_per_wave = 1;  // 16-row blocks one narrow wave may own (1 or 2)
+  int32_t tokens_per_row = 64;     // chunk length per query row (keeps partial traffic ~3%)
+  // 16-row blocks one narrow wave may own: 1, 2, or 0 for automatic (2 when
+  // items of more than 16 rows hold at least a quarter of the narrow tokens)
+  int32_t max_row_blocks_per_wave = 0;
   bool short_items = true;         // one wave per plane for short narrow items
   int32_t short_tokens = kShortTokens;  // longest narrow item (of <= 16 rows) that counts as short
 };

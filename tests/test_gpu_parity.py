@@ -101,9 +101,9 @@ def _lib(pkv):
 
 @pytest.mark.parametrize("w", SMALL_DECODE, ids=lambda w: w.name)
 @pytest.mark.parametrize("path,chunk,pf,rbw", [(0, 0, 0, 1), (0, 64, 0, 1), (0, 0, 0, 2), (0, 96, 1, 1),
-                                              (1, 0, 0, 1), (1, 64, 0, 1)],
+                                              (1, 0, 0, 1), (1, 64, 0, 1), (0, 0, 0, 0)],
                          ids=["auto", "auto_split64", "two_blocks_per_wave", "prefetch_split96", "valu",
-                              "valu_split64"])
+                              "valu_split64", "auto_blocks_per_wave"])
 def test_decode_matches_oracle(w, path, chunk, pf, rbw):
     note(f"decode {w.name} path={path} chunk={chunk} prefetch={pf} row_blocks={rbw}")
     inp, got = run_decode(w, path=path, chunk_tokens=chunk, prefetch=pf, row_blocks=rbw)
