@@ -120,10 +120,12 @@ int pkv_block_release(pkv_pool* pool, int32_t id);
 
 /* A new, empty sequence. */
 int pkv_seq_create(pkv_pool* pool, pkv_seq* out);
-/* Fork [D1]: the child's table is a copy of the parent's list of block ids
- * and every listed block gains one reference. The parent is unchanged and
- * no K/V is copied. Cost is linear in the number of blocks, independent of
- * the bytes they hold. */
+/* Fork [D1]: the child's table equals the parent's and every listed block
+ * gains one reference, as seen by pkv_block_refcount. The parent is
+ * unchanged and no K/V is copied. O(1): tables are persistent (a list of
+ * refcounted chunks of 64 block ids), so the fork shares the parent's list
+ * and bumps one count; the first change to a shared list or chunk copies
+ * that part only (at most the list and one chunk per append). */
 int pkv_seq_fork(pkv_pool* pool, pkv_seq parent, pkv_seq* child);
 /* Drop one reference from each block of the sequence (blocks reaching 0
  * become free) and invalidate the handle. */
@@ -180,7 +182,12 @@ int pkv_seq_append_kv(pkv_pool* pool, pkv_seq seq, int32_t n, const void* k_new,
 int pkv_seq_info(const pkv_pool* pool, pkv_seq seq, int32_t* len, int32_t* n_blocks);
 /* Copy up to cap block ids of the sequence's table into out (host). */
 int pkv_seq_blocks(const pkv_pool* pool, pkv_seq seq, int32_t* out, int32_t cap);
+/* References on a block: the live sequences whose table holds it, the
+ * prompt-cache entries that hold it and pkv_block_alloc references. Computed
+ * from the tables on each call (linear in the pool's table entries). */
 int pkv_block_refcount(const pkv_pool* pool, int32_t id, int32_t* count);
+/* The same for blocks 0 .. n-1 in one pass (host array, n <= num_blocks). */
+int pkv_block_refcounts(const pkv_pool* pool, int32_t* counts, int32_t n);
 int pkv_pool_stats(const pkv_pool* pool, pkv_stats* stats);
 /* Bytes of device memory one arena (K or V) must have for this desc. */
 int pkv_arena_bytes(const pkv_pool_desc* desc, size_t* bytes);

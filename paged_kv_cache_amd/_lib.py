@@ -85,6 +85,7 @@ _PROTOS = {
     "pkv_seq_info": [c_void_p, PkvSeq, POINTER(c_int32), POINTER(c_int32)],
     "pkv_seq_blocks": [c_void_p, PkvSeq, POINTER(c_int32), c_int32],
     "pkv_block_refcount": [c_void_p, c_int32, POINTER(c_int32)],
+    "pkv_block_refcounts": [c_void_p, POINTER(c_int32), c_int32],
     "pkv_pool_stats": [c_void_p, POINTER(PkvStats)],
     "pkv_arena_bytes": [POINTER(PkvPoolDesc), POINTER(c_size_t)],
     "pkv_decode_plan_info": [c_void_p, POINTER(PkvSeq), c_int32, c_int32, POINTER(PkvPlanInfo)],

@@ -168,6 +168,12 @@ def pkv_block_refcount(pool, block: int) -> int:
     return rc.value
 
 
+def pkv_block_refcounts(pool, n: int) -> List[int]:
+    out = (c_int32 * max(n, 1))()
+    check(lib.pkv_block_refcounts(pool, out, n))
+    return list(out[:n])
+
+
 def pkv_pool_stats(pool) -> dict:
     st = PkvStats()
     check(lib.pkv_pool_stats(pool, byref(st)))
@@ -360,6 +366,9 @@ class PagedKVCache:
 
     def refcount(self, block: int) -> int:
         return pkv_block_refcount(self.handle, block)
+
+    def refcounts(self) -> List[int]:
+        return pkv_block_refcounts(self.handle, self.NB)
 
     def stats(self) -> dict:
         return pkv_pool_stats(self.handle)

@@ -740,7 +740,7 @@ int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t*
   GatherParams g{};
   for (int32_t i = 0; i < n_accepted; ++i) {
     const int64_t pos = (int64_t)ctx + accepted[i];
-    g.slots[i] = (int64_t)s->blocks[(size_t)(pos / bs)] * bs + pos % bs;
+    g.slots[i] = (int64_t)pool->pool.blocks(*s)[(size_t)(pos / bs)] * bs + pos % bs;
   }
   // tables first (all or nothing); the device work below reads the kept
   // nodes before the re-append overwrites or frees their slots
@@ -821,6 +821,13 @@ int pkv_block_refcount(const pkv_pool* pool, int32_t id, int32_t* count) {
   PKV_GUARD_BEGIN
   if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
   return pool->pool.refcount(id, count);
+  PKV_GUARD_END
+}
+
+int pkv_block_refcounts(const pkv_pool* pool, int32_t* counts, int32_t n) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  return pool->pool.refcounts(counts, n);
   PKV_GUARD_END
 }
 

@@ -95,7 +95,6 @@ Pool::Pool(const pkv_pool_desc& d) : d_(d) {
 }
 
 void Pool::release_ref(int32_t b) {
-  --total_refs_;
   if (--ref_[b] == 0) free_.insert(rank_of_[b]);
 }
 
@@ -104,7 +103,6 @@ int32_t Pool::take_block() {
   int rank = free_.pop_lowest();
   int32_t b = order_[rank];
   ref_[b] = 1;
-  ++total_refs_;
   return b;
 }
 
@@ -119,8 +117,7 @@ int Pool::block_alloc(int32_t* id) {
 int Pool::block_release(int32_t id) {
   if (id < 0 || id >= d_.num_blocks) return fail(PKV_E_INVALID, "block_release: id out of range");
   if (ref_[id] <= 0) return fail(PKV_E_INVALID, "block_release: block is already free");
-  --total_refs_;
-  if (--ref_[id] == 0) free_.insert(rank_of_[id]);
+  release_ref(id);
   ++mutation_;
   return PKV_OK;
 }
@@ -136,6 +133,158 @@ const Seq* Pool::get(pkv_seq s) const {
 
 Seq* Pool::get_mut(pkv_seq s) { return const_cast<Seq*>(get(s)); }
 
+// ------------------------------------------------------ persistent tables
+
+int32_t Pool::new_chunk() {
+  int32_t c;
+  if (!free_chunks_.empty()) {
+    c = free_chunks_.back();
+    free_chunks_.pop_back();
+  } else {
+    c = (int32_t)chunks_.size();
+    chunks_.emplace_back();
+  }
+  chunks_[c].ref = 1;
+  chunks_[c].n = 0;
+  return c;
+}
+
+int32_t Pool::new_list() {
+  int32_t l;
+  if (!free_lists_.empty()) {
+    l = free_lists_.back();
+    free_lists_.pop_back();
+  } else {
+    l = (int32_t)lists_.size();
+    lists_.emplace_back();
+  }
+  lists_[l].ref = 1;
+  lists_[l].chunks.clear();
+  return l;
+}
+
+void Pool::drop_chunk(int32_t c) {
+  TChunk& k = chunks_[c];
+  if (--k.ref > 0) return;
+  for (int32_t i = 0; i < k.n; ++i) release_ref(k.ids[i]);
+  k.n = 0;
+  free_chunks_.push_back(c);
+}
+
+void Pool::drop_list(int32_t l) {
+  if (--lists_[l].ref > 0) return;
+  for (int32_t c : lists_[l].chunks) drop_chunk(c);
+  lists_[l].chunks.clear();
+  free_lists_.push_back(l);
+}
+
+void Pool::own_list(Seq& s) {
+  if (s.list < 0) {
+    s.list = new_list();
+    return;
+  }
+  if (lists_[s.list].ref == 1) return;
+  const int32_t old = s.list;
+  const int32_t l = new_list();  // (may reallocate lists_)
+  lists_[l].chunks = lists_[old].chunks;
+  for (int32_t c : lists_[l].chunks) ++chunks_[c].ref;
+  --lists_[old].ref;  // still held by the sequences that shared it
+  s.list = l;
+}
+
+void Pool::own_last_chunk(Seq& s) {
+  std::vector<int32_t>& cl = lists_[s.list].chunks;
+  const int32_t old = cl.back();
+  if (chunks_[old].ref == 1) return;
+  const int32_t c = new_chunk();  // (may reallocate chunks_)
+  TChunk& k = chunks_[c];
+  const TChunk& o = chunks_[old];
+  k.n = o.n;
+  for (int32_t i = 0; i < o.n; ++i) {
+    k.ids[i] = o.ids[i];
+    ++ref_[o.ids[i]];
+  }
+  --chunks_[old].ref;  // still held by the lists that shared it
+  lists_[s.list].chunks.back() = c;
+}
+
+void Pool::push_id(Seq& s, int32_t b) {
+  own_list(s);
+  std::vector<int32_t>& cl = lists_[s.list].chunks;
+  if (cl.empty() || chunks_[cl.back()].n == kChunk) {
+    const int32_t c = new_chunk();
+    lists_[s.list].chunks.push_back(c);
+  } else {
+    own_last_chunk(s);
+  }
+  TChunk& k = chunks_[lists_[s.list].chunks.back()];
+  k.ids[k.n++] = b;
+  s.flat_ok = false;
+}
+
+void Pool::set_last_id(Seq& s, int32_t b) {
+  own_list(s);
+  own_last_chunk(s);
+  TChunk& k = chunks_[lists_[s.list].chunks.back()];
+  k.ids[k.n - 1] = b;
+  s.flat_ok = false;
+}
+
+void Pool::cut_table(Seq& s, int32_t keep) {
+  if (s.list < 0) return;
+  const int32_t have = (int32_t)((s.len + (int64_t)d_.block_size - 1) / d_.block_size);
+  if (keep >= have) return;
+  s.flat_ok = false;
+  if (keep == 0) {
+    drop_list(s.list);
+    s.list = -1;
+    return;
+  }
+  own_list(s);
+  std::vector<int32_t>& cl = lists_[s.list].chunks;
+  const int32_t keep_chunks = (keep + kChunk - 1) / kChunk;
+  while ((int32_t)cl.size() > keep_chunks) {
+    const int32_t c = cl.back();
+    cl.pop_back();
+    drop_chunk(c);
+  }
+  const int32_t in_last = keep - (keep_chunks - 1) * kChunk;
+  if (chunks_[cl.back()].n > in_last) {
+    own_last_chunk(s);
+    TChunk& k = chunks_[lists_[s.list].chunks.back()];
+    for (int32_t i = in_last; i < k.n; ++i) release_ref(k.ids[i]);
+    k.n = in_last;
+  }
+}
+
+const std::vector<int32_t>& Pool::blocks(const Seq& s) const {
+  if (!s.flat_ok) {
+    s.flat.clear();
+    if (s.list >= 0)
+      for (int32_t c : lists_[s.list].chunks)
+        s.flat.insert(s.flat.end(), chunks_[c].ids, chunks_[c].ids + chunks_[c].n);
+    s.flat_ok = true;
+  }
+  return s.flat;
+}
+
+void Pool::effective_refs(std::vector<int32_t>& out) const {
+  // a chunk stands for as many holders as the sequences of the lists that
+  // hold it; ref_ counts it once
+  out.assign(ref_.begin(), ref_.end());
+  std::vector<int64_t> w(chunks_.size(), 0);
+  for (const TList& l : lists_)
+    if (l.ref > 0)
+      for (int32_t c : l.chunks) w[c] += l.ref;
+  for (size_t c = 0; c < chunks_.size(); ++c) {
+    const TChunk& k = chunks_[c];
+    if (k.ref <= 0) continue;
+    for (int32_t i = 0; i < k.n; ++i) out[k.ids[i]] += (int32_t)(w[c] - 1);
+  }
+}
+
+// -------------------------------------------------------------- sequences
+
 int Pool::seq_create(pkv_seq* out) {
   if (!out) return fail(PKV_E_INVALID, "seq_create: null output");
   int32_t idx;
@@ -149,7 +298,9 @@ int Pool::seq_create(pkv_seq* out) {
   Seq& s = seqs_[idx];
   s.live = true;
   s.len = 0;
-  s.blocks.clear();
+  s.list = -1;
+  s.flat.clear();
+  s.flat_ok = true;
   ++live_;
   ++mutation_;
   *out = pkv_seq{idx, s.gen};
@@ -164,10 +315,10 @@ int Pool::seq_fork(pkv_seq parent, pkv_seq* child) {
   if (rc) return rc;
   const Seq& p = seqs_[parent.index];
   Seq& k = seqs_[c.index];
-  k.blocks = p.blocks;  // shallow: block ids only
+  k.list = p.list;  // shared: one count, whatever the table's length
+  if (k.list >= 0) ++lists_[k.list].ref;
   k.len = p.len;
-  for (int32_t b : k.blocks) ++ref_[b];
-  total_refs_ += (int64_t)k.blocks.size();
+  k.flat_ok = false;
   *child = c;
   return PKV_OK;
 }
@@ -175,11 +326,10 @@ int Pool::seq_fork(pkv_seq parent, pkv_seq* child) {
 int Pool::seq_free(pkv_seq h) {
   Seq* s = get_mut(h);
   if (!s) return PKV_E_INVALID;
-  for (int32_t b : s->blocks) {
-    if (--ref_[b] == 0) free_.insert(rank_of_[b]);
-  }
-  total_refs_ -= (int64_t)s->blocks.size();
-  s->blocks.clear();
+  if (s->list >= 0) drop_list(s->list);
+  s->list = -1;
+  s->flat.clear();
+  s->flat_ok = true;
   s->len = 0;
   s->live = false;
   ++s->gen;
@@ -193,13 +343,7 @@ int Pool::seq_truncate(pkv_seq h, int32_t n) {
   Seq* s = get_mut(h);
   if (!s) return PKV_E_INVALID;
   if (n < 0 || n > s->len) return fail(PKV_E_INVALID, "truncate: length outside [0, len]");
-  const int32_t keep = (int32_t)((n + (int64_t)d_.block_size - 1) / d_.block_size);
-  for (size_t i = (size_t)keep; i < s->blocks.size(); ++i) {
-    const int32_t b = s->blocks[i];
-    if (--ref_[b] == 0) free_.insert(rank_of_[b]);
-    --total_refs_;
-  }
-  s->blocks.resize((size_t)keep);
+  cut_table(*s, (int32_t)((n + (int64_t)d_.block_size - 1) / d_.block_size));
   s->len = n;
   ++mutation_;
   return PKV_OK;
@@ -212,18 +356,19 @@ int Pool::truncate_append(pkv_seq h, int32_t keep_len, int32_t n_new, std::vecto
   if (keep_len < 0 || keep_len > s->len) return fail(PKV_E_INVALID, "truncate: length outside [0, len]");
   const int32_t old_len = s->len;
   const int32_t keep = (int32_t)((keep_len + (int64_t)d_.block_size - 1) / d_.block_size);
-  const std::vector<int32_t> tail(s->blocks.begin() + keep, s->blocks.end());
+  const std::vector<int32_t>& all = blocks(*s);
+  const std::vector<int32_t> tail(all.begin() + keep, all.end());
   int rc = seq_truncate(h, keep_len);
   if (rc) return rc;
   rc = append_plan_batch(&h, &n_new, 1, slots, cows);
   if (rc == PKV_OK) return rc;
-  // the refused append changed nothing: give the tail back its references
+  // the refused append changed nothing a caller sees: give the tail back
+  s = get_mut(h);
   for (int32_t b : tail) {
     if (ref_[b] == 0) free_.erase(rank_of_[b]);
     ++ref_[b];
-    ++total_refs_;
+    push_id(*s, b);
   }
-  s->blocks.insert(s->blocks.end(), tail.begin(), tail.end());
   s->len = old_len;
   return rc;
 }
@@ -232,12 +377,8 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
                             std::vector<int64_t>* slots, std::vector<pkv_cow_op>* cows) {
   if (n < 0 || (n > 0 && (!seqs || !counts))) return fail(PKV_E_INVALID, "append: bad arguments");
   const int64_t bs = d_.block_size;
-  // Pass 1: validate and count the blocks the whole batch needs, following
-  // the same order the execution pass takes (a copy made by an earlier
-  // sequence lowers the count of a tail that a later one may share).
-  std::unordered_map<int32_t, int32_t> dropped;  // block -> refs dropped by earlier copies
+  // Pass 0: validate.
   std::vector<int32_t> seen;
-  int64_t need = 0;
   for (int32_t i = 0; i < n; ++i) {
     const Seq* s = get(seqs[i]);
     if (!s) return PKV_E_INVALID;
@@ -245,18 +386,35 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
     if (std::find(seen.begin(), seen.end(), seqs[i].index) != seen.end())
       return fail(PKV_E_INVALID, "append: a sequence appears twice in one batch");
     seen.push_back(seqs[i].index);
-    if (counts[i] == 0) continue;
     if ((int64_t)s->len + counts[i] > (int64_t)INT32_MAX)
       return fail(PKV_E_INVALID, "append: sequence length overflow");
-    if (s->len % bs != 0) {
-      int32_t last = s->blocks.back();
-      int32_t live_refs = ref_[last] - dropped[last];
-      if (live_refs > 1) {
+  }
+  // Pass 1: give every appending sequence its own list and, where the tail
+  // block is partly filled, its own last chunk (copies of shared table
+  // parts change nothing a caller sees and allocate no block), so that a
+  // tail block's count is the number of its holders' chunks. Then count
+  // the blocks the batch needs in the order pass 2 takes (a copy made by an
+  // earlier sequence lowers the count of a tail that a later one shares).
+  for (int32_t i = 0; i < n; ++i) {
+    if (counts[i] == 0) continue;
+    Seq& s = seqs_[seqs[i].index];
+    own_list(s);
+    if (s.len % bs != 0) own_last_chunk(s);
+  }
+  std::unordered_map<int32_t, int32_t> dropped;  // block -> refs dropped by earlier copies
+  int64_t need = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (counts[i] == 0) continue;
+    const Seq& s = seqs_[seqs[i].index];
+    if (s.len % bs != 0) {
+      const TChunk& k = chunks_[lists_[s.list].chunks.back()];
+      const int32_t last = k.ids[k.n - 1];
+      if (ref_[last] - dropped[last] > 1) {
         ++need;
         ++dropped[last];
       }
     }
-    int64_t before = (s->len + bs - 1) / bs, after = (s->len + counts[i] + bs - 1) / bs;
+    int64_t before = (s.len + bs - 1) / bs, after = (s.len + counts[i] + bs - 1) / bs;
     need += after - before;
   }
   if (need > free_.count() && need > (int64_t)free_.count() + prefix_evictable())
@@ -266,21 +424,31 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
   for (int32_t i = 0; i < n; ++i) {
     if (counts[i] == 0) continue;
     Seq& s = seqs_[seqs[i].index];
-    int32_t r = (int32_t)(s.len % bs);
-    if (r != 0 && ref_[s.blocks.back()] > 1) {
-      int32_t old = s.blocks.back();
-      int32_t fresh = take_block();
-      --ref_[old];
-      --total_refs_;
-      s.blocks.back() = fresh;
-      if (cows) cows->push_back(pkv_cow_op{old, fresh, r});
+    const int32_t r = (int32_t)(s.len % bs);
+    if (r != 0) {
+      const TChunk& k = chunks_[lists_[s.list].chunks.back()];
+      const int32_t old = k.ids[k.n - 1];
+      if (ref_[old] > 1) {
+        const int32_t fresh = take_block();
+        --ref_[old];  // (> 0: another chunk or entry still holds it)
+        set_last_id(s, fresh);
+        if (cows) cows->push_back(pkv_cow_op{old, fresh, r});
+      }
     }
+    int32_t cur = -1;
     for (int32_t t = 0; t < counts[i]; ++t) {
-      int64_t pos = s.len;
-      if (pos % bs == 0) s.blocks.push_back(take_block());
-      if (slots) slots->push_back((int64_t)s.blocks[pos / bs] * bs + pos % bs);
+      const int64_t pos = s.len;
+      if (pos % bs == 0) {
+        cur = take_block();
+        push_id(s, cur);
+      } else if (cur < 0) {
+        const TChunk& k = chunks_[lists_[s.list].chunks.back()];
+        cur = k.ids[k.n - 1];
+      }
+      if (slots) slots->push_back((int64_t)cur * bs + pos % bs);
       ++s.len;
     }
+    s.flat_ok = false;
   }
   if (need || n) ++mutation_;
   return PKV_OK;
@@ -391,7 +559,7 @@ int Pool::prefix_insert(pkv_seq h, const int32_t* tokens, int32_t n, int32_t* ad
     }
     CacheEntry& r = ents_[e];
     r.parent = parent;
-    r.block = s->blocks[(size_t)i];
+    r.block = blocks(*s)[(size_t)i];
     r.depth = parent < 0 ? 1 : ents_[parent].depth + 1;
     r.n_child = 0;
     r.stamp = stamp;
@@ -401,7 +569,6 @@ int Pool::prefix_insert(pkv_seq h, const int32_t* tokens, int32_t n, int32_t* ad
     if (parent >= 0) ++ents_[parent].n_child;
     ent_index_.emplace(hk, e);
     ++ref_[r.block];
-    ++total_refs_;
     ++n_ent_;
     parent = e;
     ++count;
@@ -431,10 +598,9 @@ int Pool::prefix_match(const int32_t* tokens, int32_t n, pkv_seq* out, int32_t* 
   if (rc) return rc;
   Seq& k = seqs_[c.index];
   for (int32_t e : chain) {
-    k.blocks.push_back(ents_[e].block);
     ++ref_[ents_[e].block];
+    push_id(k, ents_[e].block);
   }
-  total_refs_ += (int64_t)chain.size();
   k.len = (int32_t)chain.size() * bs;
   *out = c;
   if (matched) *matched = k.len;
@@ -463,7 +629,7 @@ int Pool::seq_info(pkv_seq h, int32_t* len, int32_t* nblk) const {
   const Seq* s = get(h);
   if (!s) return PKV_E_INVALID;
   if (len) *len = s->len;
-  if (nblk) *nblk = (int32_t)s->blocks.size();
+  if (nblk) *nblk = (int32_t)((s->len + (int64_t)d_.block_size - 1) / d_.block_size);
   return PKV_OK;
 }
 
@@ -471,14 +637,25 @@ int Pool::seq_blocks(pkv_seq h, int32_t* out, int32_t cap) const {
   const Seq* s = get(h);
   if (!s) return PKV_E_INVALID;
   if (cap < 0 || (cap > 0 && !out)) return fail(PKV_E_INVALID, "seq_blocks: bad buffer");
-  int32_t m = std::min<int32_t>(cap, (int32_t)s->blocks.size());
-  std::copy(s->blocks.begin(), s->blocks.begin() + m, out);
+  const std::vector<int32_t>& t = blocks(*s);
+  int32_t m = std::min<int32_t>(cap, (int32_t)t.size());
+  std::copy(t.begin(), t.begin() + m, out);
   return PKV_OK;
 }
 
 int Pool::refcount(int32_t id, int32_t* rc) const {
   if (id < 0 || id >= d_.num_blocks || !rc) return fail(PKV_E_INVALID, "refcount: bad block id");
-  *rc = ref_[id];
+  std::vector<int32_t> all;
+  effective_refs(all);
+  *rc = all[id];
+  return PKV_OK;
+}
+
+int Pool::refcounts(int32_t* out, int32_t n) const {
+  if (n < 0 || n > d_.num_blocks || (n > 0 && !out)) return fail(PKV_E_INVALID, "refcounts: bad buffer");
+  std::vector<int32_t> all;
+  effective_refs(all);
+  std::copy(all.begin(), all.begin() + n, out);
   return PKV_OK;
 }
 
@@ -488,7 +665,12 @@ int Pool::stats(pkv_stats* st) const {
   st->free_blocks = free_.count();
   st->live_seqs = live_;
   st->reserved = 0;
-  st->total_refs = total_refs_;
+  // (sequences, prompt-cache entries and blocks taken with block_alloc)
+  std::vector<int32_t> all;
+  effective_refs(all);
+  int64_t refs = 0;
+  for (int32_t r : all) refs += r;
+  st->total_refs = refs;
   return PKV_OK;
 }
 

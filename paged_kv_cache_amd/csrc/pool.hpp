@@ -40,11 +40,36 @@ class FreeSet {
   int count_ = 0;
 };
 
+// Block tables are persistent and shared: a sequence points at a table
+// list (refcounted), the list at table chunks (refcounted, up to kChunk
+// block ids each). A fork copies the list pointer and bumps one count; a
+// list or chunk is copied only when a sequence that shares it is about to
+// change it. A block's count (ref_) counts the chunks and prompt-cache
+// entries that hold it; what a caller sees (pkv_block_refcount) is the
+// number of sequences and entries that hold it, as before. A block is
+// written in place only if neither its sequence's list, nor its chunk, nor
+// the block itself is shared.
+constexpr int32_t kChunk = 64;
+
+struct TChunk {
+  int32_t ref = 0;
+  int32_t n = 0;
+  int32_t ids[kChunk];
+};
+
+struct TList {
+  int32_t ref = 0;
+  std::vector<int32_t> chunks;
+};
+
 struct Seq {
   uint32_t gen = 1;
   bool live = false;
   int32_t len = 0;
-  std::vector<int32_t> blocks;
+  int32_t list = -1;  // -1: no blocks
+  // the table flattened, built on demand and dropped when the table changes
+  mutable std::vector<int32_t> flat;
+  mutable bool flat_ok = true;
 };
 
 // A prompt-cache entry: one full block, keyed by its token ids and the
@@ -100,17 +125,34 @@ class Pool {
 
   int seq_info(pkv_seq s, int32_t* len, int32_t* nblk) const;
   int seq_blocks(pkv_seq s, int32_t* out, int32_t cap) const;
+  // Sequences and prompt-cache entries holding a block (one pass over the
+  // tables; for inspection, not for the hot path).
   int refcount(int32_t id, int32_t* rc) const;
+  int refcounts(int32_t* out, int32_t n) const;
   int stats(pkv_stats* st) const;
 
   // Validates a handle; returns the sequence or nullptr (error set).
   const Seq* get(pkv_seq s) const;
+  // The sequence's block ids in logical order.
+  const std::vector<int32_t>& blocks(const Seq& s) const;
   uint64_t mutation() const { return mutation_; }
 
  private:
   Seq* get_mut(pkv_seq s);
   int32_t take_block();  // caller has checked availability (free or evictable)
   void release_ref(int32_t b);
+
+  // persistent tables
+  int32_t new_chunk();
+  int32_t new_list();
+  void drop_chunk(int32_t c);   // one reference less; at zero its blocks lose one
+  void drop_list(int32_t l);    // one reference less; at zero its chunks lose one
+  void own_list(Seq& s);        // s's list, copied first if shared (created if none)
+  void own_last_chunk(Seq& s);  // s's last chunk, copied first if shared
+  void push_id(Seq& s, int32_t b);     // appends block b (one more reference on it)
+  void set_last_id(Seq& s, int32_t b); // replaces the last block id (no count change)
+  void cut_table(Seq& s, int32_t keep);  // keeps the first `keep` block ids
+  void effective_refs(std::vector<int32_t>& out) const;
 
   int32_t find_entry(int32_t parent, const int32_t* toks, uint64_t h) const;
   bool evict_one(uint64_t spare_stamp);  // false: nothing evictable
@@ -123,8 +165,11 @@ class Pool {
   FreeSet free_;
   std::vector<Seq> seqs_;
   std::vector<int32_t> free_seq_slots_;
+  std::vector<TChunk> chunks_;
+  std::vector<int32_t> free_chunks_;
+  std::vector<TList> lists_;
+  std::vector<int32_t> free_lists_;
   int32_t live_ = 0;
-  int64_t total_refs_ = 0;
   uint64_t mutation_ = 0;  // bumped by every table change
 
   std::vector<CacheEntry> ents_;

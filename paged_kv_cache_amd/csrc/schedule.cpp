@@ -302,8 +302,9 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   std::vector<int32_t> distinct;
   for (int32_t i = 0; i < n; ++i) {
     const Seq& s = *sv[i];
-    for (int32_t j = 0; j < (int32_t)s.blocks.size(); ++j) {
-      const int32_t b = s.blocks[j];
+    const std::vector<int32_t>& sb = pool.blocks(s);
+    for (int32_t j = 0; j < (int32_t)sb.size(); ++j) {
+      const int32_t b = sb[j];
       const int32_t v = std::min(bs, s.len - j * bs);
       if (X->stamp[b] != ep) {
         X->stamp[b] = ep;
@@ -329,7 +330,7 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
     }
     hold_all.resize(o);
     for (int32_t i = 0; i < n; ++i)
-      for (int32_t b : sv[i]->blocks) hold_all[X->off[b] + X->fill[b]++] = i;
+      for (int32_t b : pool.blocks(*sv[i])) hold_all[X->off[b] + X->fill[b]++] = i;
   }
   auto same_holders = [&](int32_t a, int32_t b) {
     return X->cnt[a] == X->cnt[b] &&
@@ -339,10 +340,10 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   // segments: maximal runs with one holder set, found by the first holder
   std::vector<Segment> segs;
   for (int32_t i = 0; i < n; ++i) {
-    const Seq& s = *sv[i];
+    const std::vector<int32_t>& sb = pool.blocks(*sv[i]);
     int32_t cur = -1, prev = -1;
-    for (int32_t j = 0; j < (int32_t)s.blocks.size(); ++j) {
-      const int32_t b = s.blocks[j];
+    for (int32_t j = 0; j < (int32_t)sb.size(); ++j) {
+      const int32_t b = sb[j];
       if (X->seg[b] >= 0) {
         cur = -1;
         prev = b;
@@ -377,7 +378,7 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   for (int32_t i = 0; i < n; ++i) {
     S->comb_ptr[i] = (int32_t)S->comb_rows.size();
     int32_t last = -1;
-    for (int32_t b : sv[i]->blocks) {
+    for (int32_t b : pool.blocks(*sv[i])) {
       const int32_t sgi = X->seg[b];
       if (sgi == last) continue;
       last = sgi;
@@ -423,7 +424,7 @@ int build_verify_schedule(const Pool& pool, const pkv_seq* reqs, int32_t n_req,
     }
     ctx[r] = s->len - n_nodes;
     Segment sg;
-    sg.blocks = s->blocks;
+    sg.blocks = pool.blocks(*s);
     sg.t0 = 0;
     sg.n_tok = s->len;
     sg.hold_off = (int32_t)S->holders.size();

@@ -82,8 +82,7 @@ def compare_state(c, pool: OraclePool, handles):
     for sid, hd in handles.items():
         assert c.table(hd) == pool.table(sid)
         assert c.length(hd) == pool.length(sid)
-    for b in range(pool.num_blocks):
-        assert c.refcount(b) == pool.refcount(b)
+    assert c.refcounts() == [pool.refcount(b) for b in range(pool.num_blocks)]
     st = c.stats()
     assert st["free_blocks"] == len(pool.free_blocks)
     assert st["live_seqs"] == len(pool.live())
@@ -174,6 +173,74 @@ def test_random_traces_with_truncate_bit_exact(pkv, seed):
             pool.free(sid)
             c.free(handles.pop(sid))
         compare_state(c, pool, handles)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_long_tables_across_chunks_bit_exact(pkv, seed):
+    """Tables of hundreds of blocks (several 64-id chunks of the persistent
+    table): forks of forks, appends and truncations that cross chunk
+    boundaries, copy-on-write of shared tails, frees; tables and counts
+    equal the oracle's after every step."""
+    rng = np.random.default_rng(900 + seed)
+    bs = [1, 2][seed % 2]
+    nb = 1200
+    order = rng.permutation(nb).tolist() if seed % 3 == 0 else None
+    c = host_cache(pkv, nb, bs, order)
+    pool = OraclePool(nb, bs, alloc_order=order)
+    root = pool.create()
+    handles = {root: c.create()}
+    n = int(rng.integers(150, 300)) * bs + int(rng.integers(bs))
+    pool.append(root, zeros(n), zeros(n))
+    c.plan(handles[root], n)
+    for _ in range(120):
+        act = int(rng.integers(5))
+        sid = list(handles)[rng.integers(len(handles))]
+        if act == 0 and len(handles) < 12:
+            k = pool.fork(sid)
+            handles[k] = c.fork(handles[sid])
+        elif act in (1, 2):
+            m = int(rng.integers(0, 70 * bs))
+            try:
+                want = pool.append(sid, zeros(m), zeros(m))
+            except oracle.OOMError:
+                with pytest.raises(pkv.OOM):
+                    c.plan(handles[sid], m)
+            else:
+                got = c.plan(handles[sid], m)
+                assert got[0] == want[0] and got[1] == [tuple(x) for x in want[1]]
+        elif act == 3:
+            m = int(rng.integers(0, pool.length(sid) + 1))
+            pool.truncate(sid, m)
+            c.truncate(handles[sid], m)
+        elif len(handles) > 1:
+            pool.free(sid)
+            c.free(handles.pop(sid))
+        compare_state(c, pool, handles)
+
+
+def test_fork_cost_does_not_grow_with_the_table(pkv):
+    """A fork shares the parent's table: forking a 16,384-block sequence
+    costs about what forking a 16-block one does (both are dominated by
+    the call itself), where copying the table would cost a thousand times
+    more work."""
+    import time
+    c = host_cache(pkv, 20000, 1)
+    small, big = c.create(), c.create()
+    c.plan(small, 16)
+    c.plan(big, 16384)
+
+    def cost(seq, reps=3000):
+        best = float("inf")
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                c.free(c.fork(seq))
+            best = min(best, time.perf_counter() - t0)
+        return best / reps
+
+    assert cost(big) < 4 * cost(small)
+    k = c.fork(big)
+    assert c.table(k) == c.table(big) and c.refcount(c.table(big)[0]) == 2
 
 
 def test_truncate_rejects_bad_lengths(pkv):
