@@ -34,7 +34,10 @@ print no algorithm):
   accepted nodes' K/V in path order, exactly as if those tokens had been
   appended one after another: truncate to the context, then append them.
   Like an append, a commit is all or nothing: if the re-append runs out of
-  blocks, the truncation is undone too and ``OOMError`` is raised.
+  blocks, the truncation is undone too and ``OOMError`` is raised. A batch
+  of commits (one verify step over several requests) truncates every
+  request first and then appends the kept paths in request order, all or
+  nothing over the batch.
 * Prompt cache (Ferrite page, section 07, and the "Agents" measurement: a
   conversation is snapshotted at turn boundaries, resumes from the longest
   match, a system prompt shared by several agents is computed once, and a
@@ -356,6 +359,39 @@ class OraclePool:
         except OOMError:
             self._restore(snap)
             self.mat[sid] = mat
+            raise
+
+    def commit_batch(self, items):
+        """Commit several draft trees of one verify step: ``items`` is a
+        list of (sid, n_nodes, parents, accepted) for distinct sequences.
+        Every request is truncated to its context first, then the kept paths
+        are appended in list order; if an append runs out of blocks,
+        everything is undone and ``OOMError`` is raised."""
+        sids = [it[0] for it in items]
+        if len(set(sids)) != len(sids):
+            raise InvalidError("a sequence appears twice")
+        gathered = []
+        for sid, n_nodes, parents, accepted in items:
+            self._check(sid)
+            if n_nodes < 1 or n_nodes > self.lens[sid] or len(parents) != n_nodes:
+                raise InvalidError("tree size does not fit the sequence")
+            self.check_path(parents, accepted)
+            c = self.lens[sid] - n_nodes
+            k, v = self.kv(sid)
+            pos = [c + a for a in accepted]
+            gathered.append((c, np.array(k[:, pos], copy=True), np.array(v[:, pos], copy=True)))
+        snap = self._snapshot()
+        mats = {sid: list(self.mat[sid]) for sid in sids}
+        for sid, (c, _, _) in zip(sids, gathered):
+            self.truncate(sid, c)
+        try:
+            for sid, (_, kk, vv) in zip(sids, gathered):
+                if kk.shape[1]:
+                    self.append(sid, kk, vv)
+        except OOMError:
+            self._restore(snap)
+            for sid in sids:
+                self.mat[sid] = mats[sid]
             raise
 
     def free(self, sid: int) -> None:

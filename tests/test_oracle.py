@@ -807,3 +807,68 @@ def test_insert_refreshes_existing_entries_and_clear_releases_all():
     with pytest.raises(oracle.InvalidError):
         pool.cache_insert(a, [1, 2, 3, 4, 5])             # more ids than tokens
     check_invariants(pool)
+
+
+def test_commit_batch_equals_commits_by_value():
+    """A batch of commits leaves every request with the same K/V as
+    committing them one at a time; a batch of one is a commit exactly."""
+    for seed in range(4):
+        pools = []
+        for _ in range(2):
+            rng = np.random.default_rng(50 + seed)
+            pool = OraclePool(96, 4)
+            root = pool.create()
+            ctx = int(rng.integers(3, 14))
+            kv = rng.standard_normal((2, 1, ctx, 1, 4)).astype(np.float32)
+            pool.append(root, kv[0], kv[1])
+            reqs = [pool.fork(root) for _ in range(3)]
+            trees = []
+            for r in reqs:
+                n = int(rng.integers(1, 10))
+                t = rng.standard_normal((2, 1, n, 1, 4)).astype(np.float32)
+                pool.append(r, t[0], t[1])
+                par = [-1] + [int(rng.integers(-1, j)) for j in range(1, n)]
+                trees.append((r, n, par, _root_path(par, int(rng.integers(n)))))
+            pools.append((pool, trees))
+        (a, trees), (b, _) = pools
+        a.commit_batch(trees)
+        for r, n, par, acc in trees:
+            b.commit(r, n, par, acc)
+        for r, *_ in trees:
+            ka, va = a.kv(r)
+            kb, vb = b.kv(r)
+            assert np.array_equal(ka, kb) and np.array_equal(va, vb)
+        check_invariants(a)
+    pool, s, kv, parents = _tree_request(8, 7, 9)
+    twin, s2, _, _ = _tree_request(8, 7, 9)
+    path = _root_path(parents, 8)
+    pool.commit_batch([(s, 9, parents, path)])
+    twin.commit(s2, 9, parents, path)
+    assert pool.table(s) == twin.table(s2) and pool.ref == twin.ref
+
+
+def test_commit_batch_out_of_blocks_changes_nothing():
+    """Requests a and b each keep one node; forks taken after their trees
+    share both context tails, so each re-append must copy its tail. One
+    block is free: a alone would fit, the batch does not, and the batch
+    leaves a untouched too."""
+    from oracle.pool import OOMError
+    pool = OraclePool(4, 4)
+    z = np.zeros((1, 8, 1, 2), np.float32)
+    a = pool.create()
+    pool.append(a, z[:, :6], z[:, :6])                     # context: blocks 0, 1 (2 of 4)
+    pool.append(a, z[:, :2], z[:, :2])                     # tree: 2 nodes, fills block 1
+    b = pool.create()
+    pool.append(b, z[:, :2], z[:, :2])                     # context: block 2 (2 of 4)
+    pool.append(b, z[:, :2], z[:, :2])                     # tree: 2 nodes, fills block 2
+    fa, fb = pool.fork(a), pool.fork(b)
+    assert sorted(pool.free_blocks) == [3]
+    state = lambda: (pool.table(a), pool.table(b), pool.length(a), pool.length(b),
+                     list(pool.ref), set(pool.free_blocks))
+    snap = state()
+    with pytest.raises(OOMError):
+        pool.commit_batch([(a, 2, [-1, 0], [0]), (b, 2, [-1, 0], [0])])
+    assert state() == snap
+    pool.commit_batch([(a, 2, [-1, 0], [0])])              # alone, a fits
+    assert pool.length(a) == 7 and pool.table(a)[1] == 3
+    check_invariants(pool)
