@@ -386,9 +386,10 @@ COMMIT_STEPS = 20
 
 def commit_leg(c, seqs, w, inp, verify, torch):
     """Speculative steps after the timed verify calls: every request keeps a
-    random root path of its tree (commit), then a new tree of the same shape
-    is appended and verified. Reports the commit's wall time per step (all
-    requests, host planning included) and its kernels' device time."""
+    random root path of its tree (one batch commit for all requests), then a
+    new tree of the same shape is appended and verified. Reports the
+    commit's wall time per step (host planning included) and its kernels'
+    device time."""
     sh = w.shape
     R, N = len(seqs), w.n_nodes
     rng = np.random.default_rng(11)
@@ -410,8 +411,7 @@ def commit_leg(c, seqs, w, inp, verify, torch):
     for i in range(COMMIT_STEPS):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for r in range(R):
-            c.commit(seqs[r], inp.parents[r], paths[i][r])
+        c.commit_batch(seqs, inp.parents, paths[i])
         torch.cuda.synchronize()
         wall += time.perf_counter() - t0
         gather += c.timing_read("commit_gather")[0]

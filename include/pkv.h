@@ -252,7 +252,8 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
  * later append copies it if it is shared ([D-rust]). Host only. */
 int pkv_seq_truncate(pkv_pool* pool, pkv_seq seq, int32_t new_len);
 
-/* Workspace bytes pkv_tree_commit needs to keep n_accepted tokens. */
+/* Workspace bytes pkv_tree_commit(_batch) needs to keep n_accepted tokens
+ * (for a batch: the sum over its requests). */
 int pkv_tree_commit_workspace_size(const pkv_pool* pool, int32_t n_accepted, size_t* bytes);
 
 /* Keeps the accepted path of a verified draft tree ([F4]; Ferrite page,
@@ -271,6 +272,18 @@ int pkv_tree_commit_workspace_size(const pkv_pool* pool, int32_t n_accepted, siz
 int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t* parents,
                     const int32_t* accepted, int32_t n_accepted, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* pkv_tree_commit for n_req distinct requests of one verify step, with one
+ * set of launches: parents and accepted are host int32 [n_req][n_nodes]
+ * (row r of accepted holds request r's path in its first n_accepted[r]
+ * entries), n_accepted host int32 [n_req]. Every request is truncated to
+ * its context, then all kept paths are appended in request order as one
+ * batch append; all or nothing over the batch (on PKV_E_OOM or
+ * PKV_E_INVALID no table changes). ws: >= pkv_tree_commit_workspace_size
+ * of the summed n_accepted. */
+int pkv_tree_commit_batch(pkv_pool* pool, const pkv_seq* seqs, int32_t n_req, int32_t n_nodes,
+                          const int32_t* parents, const int32_t* accepted,
+                          const int32_t* n_accepted, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------- prompt cache */
 

@@ -99,6 +99,8 @@ _PROTOS = {
     "pkv_tree_commit_workspace_size": [c_void_p, c_int32, POINTER(c_size_t)],
     "pkv_tree_commit": [c_void_p, PkvSeq, c_int32, POINTER(c_int32), POINTER(c_int32), c_int32,
                         c_void_p, c_size_t, c_void_p],
+    "pkv_tree_commit_batch": [c_void_p, POINTER(PkvSeq), c_int32, c_int32, POINTER(c_int32),
+                              POINTER(c_int32), POINTER(c_int32), c_void_p, c_size_t, c_void_p],
     "pkv_prefix_insert": [c_void_p, PkvSeq, POINTER(c_int32), c_int32, POINTER(c_int32)],
     "pkv_prefix_match": [c_void_p, POINTER(c_int32), c_int32, POINTER(PkvSeq), POINTER(c_int32)],
     "pkv_prefix_clear": [c_void_p],

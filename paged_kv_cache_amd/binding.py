@@ -247,6 +247,26 @@ def pkv_tree_commit(pool, seq: PkvSeq, parents, accepted, ws, stream=None) -> No
                               _stream(stream)))
 
 
+def pkv_tree_commit_batch(pool, seqs: Sequence[PkvSeq], parents, accepted: Sequence[Sequence[int]],
+                          ws, stream=None) -> None:
+    par = np.ascontiguousarray(np.asarray(parents, dtype=np.int32))
+    n_req, n_nodes = par.shape
+    acc = np.full((n_req, n_nodes), -1, dtype=np.int32)
+    na = np.zeros(n_req, dtype=np.int32)
+    for r, path in enumerate(accepted):
+        path = list(path)
+        if len(path) > n_nodes:
+            raise ValueError("a path is longer than the tree")
+        acc[r, :len(path)] = path
+        na[r] = len(path)
+    check(lib.pkv_tree_commit_batch(pool, _seq_array(seqs), n_req, n_nodes,
+                                    par.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                    acc.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                    na.ctypes.data_as(ctypes.POINTER(c_int32)),
+                                    _dev_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream)))
+
+
 def _tokens(tokens):
     t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
     buf = t if t.size else np.zeros(1, dtype=np.int32)
@@ -436,3 +456,11 @@ class PagedKVCache:
         """Keeps the accepted root-to-node path of the draft tree that ends seq."""
         ws = self._workspace(pkv_tree_commit_workspace_size(self.handle, len(accepted)))
         pkv_tree_commit(self.handle, seq, parents, accepted, ws, stream)
+
+    def commit_batch(self, seqs: Sequence[PkvSeq], parents, accepted, stream=None) -> None:
+        """commit for several requests of one verify step in one call."""
+        if len(accepted) != len(seqs):
+            raise ValueError("one accepted path per request")
+        total = sum(len(a) for a in accepted)
+        ws = self._workspace(pkv_tree_commit_workspace_size(self.handle, total))
+        pkv_tree_commit_batch(self.handle, seqs, parents, accepted, ws, stream)

@@ -695,8 +695,7 @@ int pkv_seq_truncate(pkv_pool* pool, pkv_seq seq, int32_t new_len) {
 int pkv_tree_commit_workspace_size(const pkv_pool* pool, int32_t n_accepted, size_t* bytes) {
   PKV_GUARD_BEGIN
   if (!pool_ok(pool) || !bytes) return fail(PKV_E_INVALID, "null argument");
-  if (n_accepted < 0 || n_accepted > kGatherSlots)
-    return fail(PKV_E_INVALID, "commit: n_accepted outside [0, 64]");
+  if (n_accepted < 0) return fail(PKV_E_INVALID, "commit: negative token count");
   const pkv_pool_desc& d = pool->pool.desc();
   const size_t half = ((size_t)d.num_layers * n_accepted * d.num_kv_heads * d.head_dim *
                            elem_size(d) + 255) & ~size_t(255);
@@ -705,68 +704,106 @@ int pkv_tree_commit_workspace_size(const pkv_pool* pool, int32_t n_accepted, siz
   PKV_GUARD_END
 }
 
-int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t* parents,
-                    const int32_t* accepted, int32_t n_accepted, void* ws, size_t ws_bytes,
-                    void* stream) {
+int pkv_tree_commit_batch(pkv_pool* pool, const pkv_seq* seqs, int32_t n_req, int32_t n_nodes,
+                          const int32_t* parents, const int32_t* accepted,
+                          const int32_t* n_accepted, void* ws, size_t ws_bytes, void* stream) {
   PKV_GUARD_BEGIN
   if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
   const pkv_pool_desc& d = pool->pool.desc();
   if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
   if (!append_supported(d.block_size))
     return fail(PKV_E_UNSUPPORTED, "commit: block_size must be 16, 32 or 64");
+  if (n_req < 1 || !seqs || !parents || !n_accepted)
+    return fail(PKV_E_INVALID, "commit: empty batch or null argument");
   if (n_nodes < 1 || n_nodes > 64) return fail(PKV_E_INVALID, "commit: n_nodes must be 1..64");
-  if (n_accepted < 0 || n_accepted > n_nodes)
-    return fail(PKV_E_INVALID, "commit: n_accepted outside [0, n_nodes]");
-  if (!parents || (n_accepted > 0 && !accepted)) return fail(PKV_E_INVALID, "commit: null argument");
-  for (int32_t j = 0; j < n_nodes; ++j)
-    if (parents[j] < -1 || parents[j] >= j) return fail(PKV_E_INVALID, "commit: bad parent pointer");
-  int32_t prev = -1;
-  for (int32_t i = 0; i < n_accepted; ++i) {
-    const int32_t a = accepted[i];
-    if (a < 0 || a >= n_nodes || parents[a] != prev)
-      return fail(PKV_E_INVALID, "commit: accepted nodes are not a chain from a root");
-    prev = a;
+  int64_t total = 0;
+  for (int32_t r = 0; r < n_req; ++r) {
+    const int32_t na = n_accepted[r];
+    if (na < 0 || na > n_nodes) return fail(PKV_E_INVALID, "commit: n_accepted outside [0, n_nodes]");
+    if (na > 0 && !accepted) return fail(PKV_E_INVALID, "commit: null argument");
+    const int32_t* par = parents + (size_t)r * n_nodes;
+    for (int32_t j = 0; j < n_nodes; ++j)
+      if (par[j] < -1 || par[j] >= j) return fail(PKV_E_INVALID, "commit: bad parent pointer");
+    const int32_t* acc = accepted ? accepted + (size_t)r * n_nodes : nullptr;
+    int32_t prev = -1;
+    for (int32_t i = 0; i < na; ++i) {
+      const int32_t a = acc[i];
+      if (a < 0 || a >= n_nodes || par[a] != prev)
+        return fail(PKV_E_INVALID, "commit: accepted nodes are not a chain from a root");
+      prev = a;
+    }
+    const Seq* s = pool->pool.get(seqs[r]);
+    if (!s) return PKV_E_INVALID;
+    if (s->len < n_nodes) return fail(PKV_E_INVALID, "commit: a sequence is shorter than its tree");
+    total += na;
   }
-  const Seq* s = pool->pool.get(seq);
-  if (!s) return PKV_E_INVALID;
-  if (s->len < n_nodes) return fail(PKV_E_INVALID, "commit: the sequence is shorter than the tree");
+  if (total > INT32_MAX / 2) return fail(PKV_E_INVALID, "commit: too many tokens");
   size_t need = 0;
-  int rc = pkv_tree_commit_workspace_size(pool, n_accepted, &need);
+  int rc = pkv_tree_commit_workspace_size(pool, (int32_t)total, &need);
   if (rc) return rc;
-  if (n_accepted > 0 && (!ws || ws_bytes < need))
-    return fail(PKV_E_WORKSPACE, "commit: workspace too small");
+  if (total > 0 && (!ws || ws_bytes < need)) return fail(PKV_E_WORKSPACE, "commit: workspace too small");
+  // slots of the kept nodes, read from the tables before they change
   const int64_t bs = d.block_size;
-  const int32_t ctx = s->len - n_nodes;
-  GatherParams g{};
-  for (int32_t i = 0; i < n_accepted; ++i) {
-    const int64_t pos = (int64_t)ctx + accepted[i];
-    g.slots[i] = (int64_t)pool->pool.blocks(*s)[(size_t)(pos / bs)] * bs + pos % bs;
+  std::vector<int64_t> gslots;
+  std::vector<int32_t> keep((size_t)n_req);
+  gslots.reserve((size_t)total);
+  for (int32_t r = 0; r < n_req; ++r) {
+    const Seq* s = pool->pool.get(seqs[r]);
+    const std::vector<int32_t>& t = pool->pool.blocks(*s);
+    keep[r] = s->len - n_nodes;
+    for (int32_t i = 0; i < n_accepted[r]; ++i) {
+      const int64_t pos = (int64_t)keep[r] + accepted[(size_t)r * n_nodes + i];
+      gslots.push_back((int64_t)t[(size_t)(pos / bs)] * bs + pos % bs);
+    }
   }
-  // tables first (all or nothing); the device work below reads the kept
-  // nodes before the re-append overwrites or frees their slots
+  // tables (all or nothing), then the device work: the gathers read the
+  // kept nodes before the append overwrites or reuses their slots
   std::vector<int64_t> slots;
   std::vector<pkv_cow_op> cows;
-  if ((rc = pool->pool.truncate_append(seq, ctx, n_accepted, &slots, &cows))) return rc;
-  if (n_accepted == 0) return PKV_OK;
+  if ((rc = pool->pool.truncate_append_batch(seqs, keep.data(), n_accepted, n_req, &slots, &cows)))
+    return rc;
+  if (total == 0) return PKV_OK;
   hipStream_t strm = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   const size_t half = need / 2;
-  g.k_arena = d.k_arena;
-  g.v_arena = d.v_arena;
-  g.k_out = w;
-  g.v_out = w + half;
-  g.n = n_accepted;
-  g.L = d.num_layers;
-  g.NB = d.num_blocks;
-  g.Hkv = d.num_kv_heads;
-  g.D = d.head_dim;
-  g.BS = d.block_size;
-  rc = pool->timed(
-      T_GATHER, [&](const LaunchEvents& ev) { return launch_gather(d.kv_dtype, g, strm, ev); },
-      "gather launch");
-  if (rc) return rc;
+  for (int64_t g0 = 0; g0 < total; g0 += kGatherSlots) {
+    GatherParams g{};
+    g.k_arena = d.k_arena;
+    g.v_arena = d.v_arena;
+    g.k_out = w;
+    g.v_out = w + half;
+    g.n = (int32_t)std::min<int64_t>(kGatherSlots, total - g0);
+    g.row0 = (int32_t)g0;
+    g.n_rows = (int32_t)total;
+    g.L = d.num_layers;
+    g.NB = d.num_blocks;
+    g.Hkv = d.num_kv_heads;
+    g.D = d.head_dim;
+    g.BS = d.block_size;
+    for (int32_t i = 0; i < g.n; ++i) g.slots[i] = gslots[(size_t)(g0 + i)];
+    rc = pool->timed(
+        T_GATHER, [&](const LaunchEvents& ev) { return launch_gather(d.kv_dtype, g, strm, ev); },
+        "gather launch");
+    if (rc) return rc;
+  }
   return enqueue_append(pool, cows.data(), (int32_t)cows.size(), slots.data(),
                         (int32_t)slots.size(), w, w + half, strm);
+  PKV_GUARD_END
+}
+
+int pkv_tree_commit(pkv_pool* pool, pkv_seq seq, int32_t n_nodes, const int32_t* parents,
+                    const int32_t* accepted, int32_t n_accepted, void* ws, size_t ws_bytes,
+                    void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  if (n_nodes < 1 || n_nodes > 64) return fail(PKV_E_INVALID, "commit: n_nodes must be 1..64");
+  if (n_accepted < 0 || n_accepted > n_nodes)
+    return fail(PKV_E_INVALID, "commit: n_accepted outside [0, n_nodes]");
+  if (n_accepted > 0 && !accepted) return fail(PKV_E_INVALID, "commit: null argument");
+  int32_t row[64];
+  for (int32_t i = 0; i < n_accepted; ++i) row[i] = accepted[i];
+  return pkv_tree_commit_batch(pool, &seq, 1, n_nodes, parents, n_accepted ? row : nullptr,
+                               &n_accepted, ws, ws_bytes, stream);
   PKV_GUARD_END
 }
 

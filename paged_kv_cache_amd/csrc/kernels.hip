@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 //
 // One workgroup per (layer, token): the token's K rows (contiguous D per
 // KV head) and V columns (stride BS in the d-major V tile) are copied into
-// [L][n][Hkv][D] outputs. Used to keep a verified draft path: its tokens
+// [L][n_rows][Hkv][D] outputs. Used to keep a verified draft path: its tokens
 // are read out before the tree is truncated, then appended again.
 
 template <typename T>
@@ -189,8 +189,8 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherParams p) {
   const int64_t t0 = ((int64_t)l * p.NB + b) * p.Hkv;
   const T* K = (const T*)p.k_arena;
   const T* V = (const T*)p.v_arena;
-  T* ko = (T*)p.k_out + ((int64_t)l * p.n + i) * p.Hkv * p.D;
-  T* vo = (T*)p.v_out + ((int64_t)l * p.n + i) * p.Hkv * p.D;
+  T* ko = (T*)p.k_out + ((int64_t)l * p.n_rows + p.row0 + i) * p.Hkv * p.D;
+  T* vo = (T*)p.v_out + ((int64_t)l * p.n_rows + p.row0 + i) * p.Hkv * p.D;
   for (int e = threadIdx.x; e < p.Hkv * p.D; e += blockDim.x) {
     const int h = e / p.D, d = e - h * p.D;
     ko[e] = K[((t0 + h) * p.BS + off) * p.D + d];

@@ -48,15 +48,18 @@ struct AppendParams {
 };
 
 // Reads the K/V of n tokens, given by slot (block * BS + offset), out of
-// the arenas into k_out / v_out, each [L][n][Hkv][D] (the layout the
-// append takes). At most kGatherSlots tokens.
-constexpr int kGatherSlots = 64;
+// the arenas into rows row0 .. row0 + n - 1 of k_out / v_out, each
+// [L][n_rows][Hkv][D] (the layout the append takes). At most kGatherSlots
+// tokens per launch.
+constexpr int kGatherSlots = 256;
 struct GatherParams {
   const void* k_arena;
   const void* v_arena;
   void* k_out;
   void* v_out;
-  int32_t n;
+  int32_t n;        // tokens in this launch
+  int32_t row0;     // their first row in the output
+  int32_t n_rows;   // rows of the output ([L][n_rows][Hkv][D])
   int32_t L;
   int32_t NB;
   int32_t Hkv;

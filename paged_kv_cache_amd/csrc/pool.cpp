@@ -351,25 +351,45 @@ int Pool::seq_truncate(pkv_seq h, int32_t n) {
 
 int Pool::truncate_append(pkv_seq h, int32_t keep_len, int32_t n_new, std::vector<int64_t>* slots,
                           std::vector<pkv_cow_op>* cows) {
-  Seq* s = get_mut(h);
-  if (!s) return PKV_E_INVALID;
-  if (keep_len < 0 || keep_len > s->len) return fail(PKV_E_INVALID, "truncate: length outside [0, len]");
-  const int32_t old_len = s->len;
-  const int32_t keep = (int32_t)((keep_len + (int64_t)d_.block_size - 1) / d_.block_size);
-  const std::vector<int32_t>& all = blocks(*s);
-  const std::vector<int32_t> tail(all.begin() + keep, all.end());
-  int rc = seq_truncate(h, keep_len);
-  if (rc) return rc;
-  rc = append_plan_batch(&h, &n_new, 1, slots, cows);
-  if (rc == PKV_OK) return rc;
-  // the refused append changed nothing a caller sees: give the tail back
-  s = get_mut(h);
-  for (int32_t b : tail) {
-    if (ref_[b] == 0) free_.erase(rank_of_[b]);
-    ++ref_[b];
-    push_id(*s, b);
+  return truncate_append_batch(&h, &keep_len, &n_new, 1, slots, cows);
+}
+
+int Pool::truncate_append_batch(const pkv_seq* seqs, const int32_t* keep_lens, const int32_t* n_new,
+                                int32_t n, std::vector<int64_t>* slots,
+                                std::vector<pkv_cow_op>* cows) {
+  if (n < 0 || (n > 0 && (!seqs || !keep_lens || !n_new)))
+    return fail(PKV_E_INVALID, "truncate_append: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq* s = get(seqs[i]);
+    if (!s) return PKV_E_INVALID;
+    if (keep_lens[i] < 0 || keep_lens[i] > s->len)
+      return fail(PKV_E_INVALID, "truncate: length outside [0, len]");
+    for (int32_t j = 0; j < i; ++j)
+      if (seqs[j].index == seqs[i].index)
+        return fail(PKV_E_INVALID, "truncate_append: a sequence appears twice");
   }
-  s->len = old_len;
+  std::vector<std::vector<int32_t>> tails((size_t)n);
+  std::vector<int32_t> old_len((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = seqs_[seqs[i].index];
+    old_len[i] = s.len;
+    const int32_t keep = (int32_t)((keep_lens[i] + (int64_t)d_.block_size - 1) / d_.block_size);
+    const std::vector<int32_t>& all = blocks(s);
+    tails[i].assign(all.begin() + keep, all.end());
+    seq_truncate(seqs[i], keep_lens[i]);
+  }
+  int rc = append_plan_batch(seqs, n_new, n, slots, cows);
+  if (rc == PKV_OK) return rc;
+  // the refused append changed nothing a caller sees: give the tails back
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = seqs_[seqs[i].index];
+    for (int32_t b : tails[i]) {
+      if (ref_[b] == 0) free_.erase(rank_of_[b]);
+      ++ref_[b];
+      push_id(s, b);
+    }
+    s.len = old_len[i];
+  }
   return rc;
 }
 

@@ -105,6 +105,11 @@ class Pool {
   // if the append is refused, the truncation is undone (all or nothing).
   int truncate_append(pkv_seq s, int32_t keep_len, int32_t n_new, std::vector<int64_t>* slots,
                       std::vector<pkv_cow_op>* cows);
+  // The same for n distinct sequences: all are truncated, then one batch
+  // append plans seqs[i] += n_new[i] in order; if it is refused, every
+  // truncation is undone.
+  int truncate_append_batch(const pkv_seq* seqs, const int32_t* keep_lens, const int32_t* n_new,
+                            int32_t n, std::vector<int64_t>* slots, std::vector<pkv_cow_op>* cows);
 
   // Prompt cache (Ferrite page, section 07: resume from the longest match;
   // parked conversations keep their blocks). Entries hold one reference on

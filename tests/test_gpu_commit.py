@@ -213,3 +213,81 @@ def test_commit_errors_change_nothing(pkv):
     c.commit(h[sid], par, [0, 2, 3])
     same_state(c, h, pool, "after the commit")
     c.close()
+
+
+@pytest.mark.parametrize("w", COMMIT_CASES[:3], ids=lambda w: w.name)
+def test_commit_batch_matches_oracle(pkv, w):
+    """All requests of a verify step committed in one call (one random root
+    path, one empty path, one deepest path, cycling), with a fork of the
+    first request sharing its context tail: tables, counts and K/V bits
+    equal the oracle's batch commit; decode afterwards agrees."""
+    note(f"commit batch {w.name}")
+    inp = generate(w)
+    c, h = build_library(pkv, w, inp)
+    pool = build_oracle(w, inp)
+    reqs = list(w.query_sids)
+    fsid = pool.fork(reqs[0])
+    h[fsid] = c.fork(h[reqs[0]])
+    rng = np.random.default_rng(6)
+    N = w.n_nodes
+    items = []
+    for r, sid in enumerate(reqs):
+        par = [int(x) for x in inp.parents[r]]
+        if r % 3 == 1:
+            path = []
+        elif r % 3 == 2:
+            depth = [len(root_path(par, j)) for j in range(N)]
+            path = root_path(par, int(np.argmax(depth)))
+        else:
+            path = root_path(par, int(rng.integers(N)))
+        items.append((sid, N, par, path))
+    pool.commit_batch(items)
+    c.commit_batch([h[sid] for sid in reqs], np.array([it[2] for it in items]),
+                   [it[3] for it in items])
+    same_state(c, h, pool, f"{w.name} after the batch")
+    sh = w.shape
+    live = [s for s in reqs + [fsid] if pool.length(s) > 0]
+    q = draw(np.random.default_rng(10), (sh.L, len(live), sh.Hq, sh.D), "bf16")
+    got = c.decode([h[s] for s in live], to_device(q), scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    want = oracle.decode(pool, live, q.f32(), w.softmax_scale)
+    check_close(got.cpu().numpy(), want, f"decode after batch commit {w.name}")
+    c.close()
+
+
+def test_commit_batch_out_of_blocks_changes_nothing(pkv):
+    """The oracle's hand-built case on the device (block size 16): the first
+    request alone would fit, the batch does not, and nothing changes."""
+    L, Hkv, Hq, D, bs = 1, 1, 2, 64, 16
+    c = pkv.PagedKVCache(4, bs, L, Hkv, Hq, D, dtype="bf16", device="cuda")
+    pool = oracle.OraclePool(4, bs)
+    rng = np.random.default_rng(12)
+    h = {}
+
+    def grow(sid, n):
+        k = draw(rng, (L, n, Hkv, D), "bf16")
+        v = draw(rng, (L, n, Hkv, D), "bf16")
+        pool.append(sid, k.f32(), v.f32())
+        c.append([h[sid]], [n], to_device(k), to_device(v))
+
+    a = pool.create()
+    h[a] = c.create()
+    grow(a, 24)                                    # context: block 0, block 1 (8 of 16)
+    grow(a, 8)                                     # tree: 8 nodes fill block 1
+    b = pool.create()
+    h[b] = c.create()
+    grow(b, 8)                                     # context: block 2 (8 of 16)
+    grow(b, 8)                                     # tree: 8 nodes fill block 2
+    for s in (a, b):
+        f = pool.fork(s)
+        h[f] = c.fork(h[s])
+    chain = [-1] + list(range(7))
+    with pytest.raises(oracle.OOMError):
+        pool.commit_batch([(a, 8, chain, [0]), (b, 8, chain, [0])])
+    with pytest.raises(pkv.OOM):
+        c.commit_batch([h[a], h[b]], np.array([chain, chain]), [[0], [0]])
+    same_state(c, h, pool, "after the refused batch")
+    pool.commit_batch([(a, 8, chain, [0, 1, 2])])
+    c.commit_batch([h[a]], np.array([chain]), [[0, 1, 2]])
+    same_state(c, h, pool, "after a alone")
+    c.close()
