@@ -62,6 +62,56 @@ def measured_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
+def record_traffic(workload: str, fetch_dir: str, write_dir: str, source: str) -> dict:
+    """Turns two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then
+    WRITE_SIZE, each with --calibrate-copy) into the per-launch HBM bytes of
+    the attention kernels and stores them in profiles/traffic.json under
+    the current kernel source hash. The counters are scaled by what they
+    read for the calibration copy (1 GiB read, 1 GiB written)."""
+    import csv
+    import glob
+
+    def rows(d, counter):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        if not out:
+            raise SystemExit(f"no {counter} rows under {d}")
+        return out
+
+    res = {"kernel": None, "kernel_hash": kernel_source_hash(), "source": source}
+    total = 0.0
+    names = []
+    for counter, d, key in (("FETCH_SIZE", fetch_dir, "read"), ("WRITE_SIZE", write_dir, "write")):
+        rr = rows(d, counter)
+        copy_kib = max(v for n, v in rr if "copyBuffer" in n)
+        scale = round((1 << 30) / (copy_kib * 1024) * 4) / 4   # to a quarter: 2.0 / 1.0 here
+        per = 0.0
+        names = []
+        for kname in ("attn_mfma_kernel", "attn_wide_kernel"):
+            vals = [v for n, v in rr if kname in n]
+            if vals:
+                names.append(kname)
+                per += sum(vals) / len(vals) * 1024 * scale
+                res[f"dispatches_{kname}"] = len(vals)
+        res[f"{key}_bytes"] = int(per)
+        res[f"{'fetch' if key == 'read' else 'write'}_scale"] = scale
+        total += per
+    res["kernel"] = "+".join(names)
+    res["bytes_per_launch"] = int(total)
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = res
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+        f.write("\n")
+    return res
+
+
 def warm_up(args, step, torch, min_seconds: float = 0.3):
     """W untimed steps, continued until min_seconds have passed: a fresh GPU
     needs a fraction of a second of load before its clocks settle."""
@@ -438,7 +488,14 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="store the HBM bytes of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                         "of this workload in profiles/traffic.json, then exit (no GPU needed)")
+    ap.add_argument("--traffic-source", default="", help="the profile summary to cite")
     args = ap.parse_args()
+    if args.record_traffic:
+        print(json.dumps(record_traffic(args.workload, *args.record_traffic, args.traffic_source)))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(this library has no multi-GPU path)", file=sys.stderr)
