@@ -12,7 +12,10 @@
  *        must never be aliased.
  *   [F4] Ferrite project page, section 04 "DFlash2 verify trees and copy
  *        rows": drafted tokens are verified as best-first trees in one pass
- *        of the model.
+ *        of the model; section 06: speculation never changes the text.
+ *   [F7] Ferrite project page, section 07 "Prompt cache for agents":
+ *        conversations snapshotted at turn boundaries resume from the
+ *        longest match; a parked conversation keeps its blocks.
  *
  * Conventions (every call):
  *   - Return value: PKV_OK (0) or a negative PKV_E_* code. On error a
