@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak of MI355X
 METRIC = "unique-KV HBM GB/s (% of peak) and branch-queries/sec, paged decode attn"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -383,7 +384,23 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, kernel)},
+        "mfma": mfma_rate(c, seqs, w, parents, attn_s) if parents is not None else None,
     }
+
+
+def mfma_rate(c, seqs, w, parents, attn_s):
+    """Matrix-core rate of a verify launch: 4*D flop per (query row, token
+    of its request) by definition (Q.K and P.V; the tree's few masked nodes
+    included), and 6*D as issued (P enters P.V as a bf16 pair)."""
+    sh = w.shape
+    rows = w.n_nodes * sh.G                      # query rows per (request, KV head)
+    tokens = sum(c.length(s) for s in seqs)      # the kernel reads every token for every row
+    row_tok = rows * tokens * sh.Hkv
+    algo = 4 * sh.D * row_tok / attn_s / 1e12
+    issued = 6 * sh.D * row_tok / attn_s / 1e12
+    return {"unit": "TFLOP/s", "peak": MFMA_BF16_PEAK_TFLOPS, "algorithmic": round(algo, 1),
+            "issued": round(issued, 1), "frac_algorithmic": round(algo / MFMA_BF16_PEAK_TFLOPS, 4),
+            "frac_issued": round(issued / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def run_prompt_cache(args, pkv, torch):
