@@ -101,7 +101,10 @@ __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
 // with 16-byte vectors and patched in registers. No other workgroup writes
 // the destination block, and a copy's source is shared, so no write
 // touches it: copies and writes need no ordering. The remaining workgroups
-// write one (layer, token) of the write list each, all KV heads.
+// write one (layer, token) of the write list each, all KV heads. Copies are
+// written with non-temporal stores: a decode usually follows, and with the
+// copied tiles left in the caches the attention launch after the append
+// ran ~2% slower (beam step: 97.9 -> 95.7 us with streaming stores).
 
 template <typename T, int BS>
 __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l, int h) {
@@ -124,7 +127,7 @@ __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l,
         t < nv ? (const u32x4*)(K + st * tile + (int64_t)t * p.D) + c
                : (const u32x4*)(kn + (((int64_t)l * p.n_tok + tok0 + t - nv) * p.Hkv + h) * p.D) + c;
     const u32x4 x = *from;
-    ((u32x4*)(K + dt * tile + (int64_t)t * p.D))[c] = x;
+    __builtin_nontemporal_store(x, (u32x4*)(K + dt * tile + (int64_t)t * p.D) + c);
   }
   // V rows: whole rows from the source, new tokens patched in (slot k of
   // the row is visited with a compile-time index, so the row stays in
@@ -141,7 +144,7 @@ __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l,
       if (k >= nv && k < nv + m) row[k / EPV][k % EPV] = vnew[(int64_t)(k - nv) * p.Hkv * p.D];
     vecT* vd = (vecT*)(V + dt * tile + (int64_t)d * BS);
 #pragma unroll
-    for (int c = 0; c < RV; ++c) vd[c] = row[c];
+    for (int c = 0; c < RV; ++c) __builtin_nontemporal_store(row[c], vd + c);
   }
 }
 
