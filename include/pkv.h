@@ -354,6 +354,10 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       instead of four waves that split its steps and merge
  *                       (0: always four)
  *   "short_tokens"      256: see "short_items" (32..8192)
+ *   "fold_tokens"       64: a shared segment of fewer tokens is read by each
+ *                       branch that holds it, together with the branch's
+ *                       neighbouring short segments, instead of once for all
+ *                       (its partial states would outweigh its K/V); 0: never
  *   "prefix_cache_blocks" num_blocks: most entries the prompt cache holds
  *                       (0..num_blocks; applies to later inserts)
  *   "concurrent"        0: 1 runs the wide-item launch on a second stream of the

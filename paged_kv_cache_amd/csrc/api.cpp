@@ -990,6 +990,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "short_tokens") {
     if (value < 32 || value > 8192) return fail(PKV_E_INVALID, "short_tokens must be 32..8192");
     pool->opt.short_tokens = (int32_t)value;
+  } else if (k == "fold_tokens") {
+    if (value < 0 || value > 8192) return fail(PKV_E_INVALID, "fold_tokens must be 0..8192");
+    pool->opt.fold_tokens = (int32_t)value;
   } else if (k == "short_items") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "short_items must be 0 or 1");
     pool->opt.short_items = value != 0;

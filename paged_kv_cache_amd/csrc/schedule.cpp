@@ -370,6 +370,70 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   }
   S->n_segments = (int32_t)segs.size();
   for (const Segment& sg : segs) S->unique_tokens += sg.n_tok;
+  // each branch's segments in logical order
+  std::vector<std::vector<int32_t>> path((size_t)n);
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t last = -1;
+    for (int32_t b : pool.blocks(*sv[i]))
+      if (X->seg[b] != last) path[i].push_back(last = X->seg[b]);
+  }
+  // Short shared segments are folded into per-branch segments: a shared
+  // segment writes one partial state per row it serves, and when it holds
+  // few tokens (an MCTS edge: 32 tokens for up to 128 rows per KV head)
+  // those states outweigh its K/V; re-reading it once per branch (mostly
+  // from the caches, siblings run side by side) and merging it into one
+  // state per branch with the branch's other short segments costs less.
+  if (opt.fold_tokens > 0) {
+    std::vector<char> fold(segs.size(), 0);
+    bool any = false;
+    for (size_t k = 0; k < segs.size(); ++k) {
+      fold[k] = segs[k].n_hold > 1 && segs[k].n_tok < opt.fold_tokens;
+      any = any || fold[k];
+    }
+    if (any) {
+      // a branch's private segments join its runs too (they are per-branch
+      // already): a leaf's folded edges and its own tail make one item
+      for (size_t k = 0; k < segs.size(); ++k) fold[k] = fold[k] || segs[k].n_hold == 1;
+      std::vector<Segment> out;
+      std::vector<int32_t> holders, remap(segs.size(), -1);
+      for (size_t k = 0; k < segs.size(); ++k) {
+        if (fold[k]) continue;
+        remap[k] = (int32_t)out.size();
+        Segment sg = segs[k];
+        sg.hold_off = (int32_t)holders.size();
+        holders.insert(holders.end(), S->holders.begin() + segs[k].hold_off,
+                       S->holders.begin() + segs[k].hold_off + segs[k].n_hold);
+        out.push_back(std::move(sg));
+      }
+      for (int32_t i = 0; i < n; ++i) {
+        std::vector<int32_t> np;
+        int32_t run = -1;  // this branch's open folded segment
+        for (int32_t sgi : path[i]) {
+          if (!fold[sgi]) {
+            run = -1;
+            np.push_back(remap[sgi]);
+            continue;
+          }
+          if (run < 0) {
+            Segment sg;
+            sg.t0 = segs[sgi].t0;
+            sg.hold_off = (int32_t)holders.size();
+            sg.n_hold = 1;
+            holders.push_back(i);
+            run = (int32_t)out.size();
+            out.push_back(std::move(sg));
+            np.push_back(run);
+          }
+          Segment& r = out[run];
+          r.blocks.insert(r.blocks.end(), segs[sgi].blocks.begin(), segs[sgi].blocks.end());
+          r.n_tok += segs[sgi].n_tok;
+        }
+        path[i] = std::move(np);
+      }
+      segs = std::move(out);
+      S->holders = std::move(holders);
+    }
+  }
   const std::vector<Chunk> chunks = emit_chunks(segs, bs, G, n_layers, d.num_kv_heads, opt, S);
   // combine lists: for each branch, its segments in logical order, each
   // segment's chunks in order; the entry is the partial row of q-head
@@ -377,11 +441,7 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   S->comb_ptr.resize(n + 1);
   for (int32_t i = 0; i < n; ++i) {
     S->comb_ptr[i] = (int32_t)S->comb_rows.size();
-    int32_t last = -1;
-    for (int32_t b : pool.blocks(*sv[i])) {
-      const int32_t sgi = X->seg[b];
-      if (sgi == last) continue;
-      last = sgi;
+    for (int32_t sgi : path[i]) {
       const Segment& sg = segs[sgi];
       const int32_t* h0 = S->holders.data() + sg.hold_off;
       const int32_t hidx = (int32_t)(std::lower_bound(h0, h0 + sg.n_hold, i) - h0);

@@ -28,6 +28,7 @@ struct SchedOptions {
   int32_t max_row_blocks_per_wave = 0;
   bool short_items = true;         // one wave per plane for short narrow items
   int32_t short_tokens = kShortTokens;  // longest narrow item (of <= 16 rows) that counts as short
+  int32_t fold_tokens = 64;        // shared segments shorter than this are read per branch (0: never)
 };
 
 struct Schedule {

@@ -69,9 +69,10 @@ SMALL_DECODE = [
 
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
-               row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256):
+               row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256, fold=64):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    c.set_option("fold_tokens", fold)
     c.set_option("concurrent", concurrent)
     c.set_option("short_items", short_items)
     c.set_option("short_tokens", short_tokens)
@@ -161,6 +162,21 @@ def test_short_items_one_wave_each(w, chunk, pf, st):
     pool = build_oracle(w, inp)
     want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
     check_close(a, want, f"{w.name} short items chunk={chunk}")
+
+
+@pytest.mark.parametrize("w", [SMALL_DECODE[1], SMALL_DECODE[3], SMALL_DECODE[8]], ids=lambda w: w.name)
+@pytest.mark.parametrize("fold", [0, 32, 64, 200])
+def test_folded_short_segments_match_oracle(w, fold):
+    """Short shared segments read per branch (folded into the branch's
+    neighbouring short segments) give the oracle's outputs, and agree with
+    the unfolded plan to fp32 rounding."""
+    note(f"fold {w.name} fold_tokens={fold}")
+    inp, a = run_decode(w, fold=fold)
+    _, b = run_decode(w, fold=0)
+    assert errors(a, b)[0] <= 1e-4
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(a, want, f"{w.name} fold_tokens={fold}")
 
 
 @pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[8]], ids=lambda w: w.name)

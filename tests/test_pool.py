@@ -503,11 +503,35 @@ def test_plan_segments_closed_form(pkv, name, segments):
         else:
             c.free(h.pop(op.sid))
     seqs = [h[s] for s in w.query_sids]
+    c.set_option("fold_tokens", 0)
     info = c.plan_info(seqs)
     assert info["n_segments"] == segments
     assert info["unique_tokens"] == distinct_tokens(c, seqs)
     assert info["n_chunks"] >= segments
     assert info["workspace_bytes"] > 0
+
+
+def test_plan_folds_short_edges_per_leaf(pkv):
+    """With fold_tokens above the MCTS edge length (32 tokens), every leaf
+    reads its 6 edges (the 5 shared ones and its own) as one item: chunks =
+    the root's + one per leaf, and the partial rows per plane drop from one
+    per (edge, row) to one per leaf row; segments and unique tokens describe
+    the tree as before."""
+    w = get("mcts")
+    c, seqs = build_host_tree(pkv, w)
+    G = w.shape.Hq // w.shape.Hkv
+    c.set_option("fold_tokens", 0)
+    plain = c.plan_info(seqs)
+    c.set_option("fold_tokens", 64)
+    folded = c.plan_info(seqs)
+    assert plain["n_segments"] == folded["n_segments"] == 127
+    assert plain["unique_tokens"] == folded["unique_tokens"]
+    root_chunks = plain["n_chunks"] - 126
+    assert folded["n_chunks"] == root_chunks + 64
+    assert plain["partial_rows"] == root_chunks * 64 * G + 6 * 64 * G
+    assert folded["partial_rows"] == root_chunks * 64 * G + 64 * G
+    c.set_option("fold_tokens", 16)                    # shorter than the edges: no folding
+    assert c.plan_info(seqs) == plain
 
 
 def build_host_tree(pkv, w):
