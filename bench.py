@@ -47,8 +47,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", "kernels.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (first 16 hex) of the kernels and of the planner that cuts
+    their work (both decide the HBM traffic)."""
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "attn_plan.h", "schedule.hpp", "schedule.cpp"):
+        with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str):
