@@ -65,6 +65,8 @@ SMALL_DECODE = [
            edge_len=19),
     scaled("beam", "beam_wide_d256", shape=replace_shape(AG, L=1, Hq=24, Hkv=2), root_len=150,
            n_branches=9, branch_len=40),
+    # the tiny tree in bf16 too (the oracle reads the same rounded values)
+    scaled("tiny_b", "tiny_b_bf16", shape=replace_shape(configs.TINY, dtype="bf16")),
 ]
 
 
