@@ -147,6 +147,40 @@ def unique_tokens(cache, seqs) -> int:
     return sum(valid.values())
 
 
+def percentiles(xs):
+    """p10, p50, p90 of per-step durations (ms), nearest rank."""
+    if not xs:
+        return None
+    ys = sorted(xs)
+    pick = lambda p: ys[min(len(ys) - 1, int(p * (len(ys) - 1) + 0.5))]  # noqa: E731
+    return [round(pick(0.1), 5), round(pick(0.5), 5), round(pick(0.9), 5)]
+
+
+def side_bytes(sh, n_layers, n_rows, info):
+    """Bytes a decode moves beside the unique K/V, per call: the queries
+    (n_layers x n_rows x Hq x D in the K/V dtype), the float32 output, the
+    float32 partial states (D values + running max and sum per partial row
+    and plane, written by attention and read by the combine) and the plan
+    records uploaded with it."""
+    eb = 2 if sh.dtype == "bf16" else 4
+    q = n_layers * n_rows * sh.Hq * sh.D * eb
+    out = n_layers * n_rows * sh.Hq * sh.D * 4
+    part = 2 * info["partial_rows"] * n_layers * sh.Hkv * (sh.D + 2) * 4
+    meta = max(info["workspace_bytes"] - part // 2, 0)
+    return {"q": q, "out": out, "partials": part, "plan_upload": meta}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -246,8 +280,19 @@ def run_beam(args, pkv, torch):
     for _ in range(args.steps):
         beam_step(c, beams, step_k, step_v, q, out, scale)
     torch.cuda.synchronize()
-    c.set_option("timing", 0)
     ktimes = {k: c.timing_read(k) for k in ("attention", "combine", "append")}
+    # and once more, read back after each step for the spread of the attention
+    # time (the synchronization idles the GPU between steps, so the average
+    # above comes from the unsynchronized run)
+    per_step = []
+    for _ in range(args.steps):
+        beam_step(c, beams, step_k, step_v, q, out, scale)
+        torch.cuda.synchronize()
+        ms, n = c.timing_read("attention")
+        per_step.append(ms / max(n, 1))
+    c.set_option("timing", 0)
+    for kname in ("combine", "append"):
+        c.timing_read(kname)
     if args.calibrate_copy:
         calibrate_copy(torch)
     ms_step = dt / args.steps * 1e3
@@ -270,8 +315,10 @@ def run_beam(args, pkv, torch):
         "branch_queries_per_s": round(8 * sh.L / (dt / args.steps), 1),
         "unique_kv_bytes_per_step": uniq_bytes,
         "kernel_ms": {k: round(v[0] / max(v[1], 1), 5) for k, v in ktimes.items()},
+        "attention_ms_p10_p50_p90": percentiles(per_step),
         "host_ms_per_step": round(t_host / args.steps * 1e3, 4),
         "plan": info,
+        "other_bytes_per_step": side_bytes(sh, sh.L, 8, info),
         "roofline": {"bound": "hbm", "kernel": "attn_mfma_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
@@ -281,7 +328,8 @@ def run_beam(args, pkv, torch):
         reps, t = cpu_baseline_beam(w, inp, args.cpu_budget)
         res["cpu_baseline"] = {
             "value": round(uniq_bytes * reps / t / 1e9, 4), "unit": "GB/s",
-            "cores": blas_threads(), "kind": "oracle",
+            "cores": blas_threads(), "kind": "oracle", "cpu": cpu_model(),
+            "host_cpus": os.cpu_count(),
             "sample": f"{reps} full oracle decode pass(es) of the 8 beams x 32 layers "
                       f"({t:.1f} s), same inputs, float64 numpy",
             "branch_queries_per_s": round(8 * sh.L * reps / t, 1)}
@@ -363,9 +411,16 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
     for _ in range(args.steps):
         fn()
     torch.cuda.synchronize()
-    c.set_option("timing", 0)
     # per call: summed device time of each kernel kind (0 if it did not run)
     kt = {k: v[0] / args.steps for k, v in ((k, c.timing_read(k)) for k in names)}
+    # the spread, from a run read back after each call
+    per_call = []
+    for _ in range(args.steps):
+        fn()
+        torch.cuda.synchronize()
+        per_call.append(c.timing_read("attention")[0] + c.timing_read("attention_wide")[0])
+    c.set_option("timing", 0)
+    c.timing_read("combine")
     if args.calibrate_copy:
         calibrate_copy(torch)
     # the attention bytes are split between the narrow and the wide launch:
@@ -375,6 +430,7 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
     kernel = "+".join(parts)
     attn_s = (kt["attention"] + kt["attention_wide"]) / 1e3
     achieved = uniq_bytes / attn_s / 1e9
+    info = c.plan_info(seqs) if parents is None else None
     return {
         "metric": METRIC, "value": round(uniq_bytes / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
@@ -385,7 +441,9 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
         "branch_queries_per_s": round(n_queries / dt, 1),
         "unique_kv_bytes_per_step": uniq_bytes,
         "kernel_ms": {k: round(v, 5) for k, v in kt.items()},
-        "plan": c.plan_info(seqs) if parents is None else None,
+        "attention_ms_p10_p50_p90": percentiles(per_call),
+        "plan": info,
+        "other_bytes_per_step": side_bytes(sh, sh.L, len(seqs), info) if info else None,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, kernel)},

@@ -346,9 +346,12 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       up to 32 rows loads each K/V step once, at the cost of
  *                       occupancy; 0 picks 2 when items of more than 16 rows
  *                       hold at least a quarter of the narrow launch's tokens
- *   "tokens_per_row"    64: chunk length per query row reading it (between
- *                       "min_chunk_tokens" and 8192 tokens)
- *   "min_chunk_tokens"  1024: shortest automatic chunk (32..8192)
+ *   "tokens_per_row"    0: chunk length per query row reading it (between
+ *                       "min_chunk_tokens" and 8192 tokens; 1..8192), 0 for
+ *                       64 up to head_dim 128 and 32 above
+ *   "min_chunk_tokens"  0: shortest automatic chunk (32..8192), 0 for 1024 up
+ *                       to head_dim 128 and 768 above (a 256-dim token is
+ *                       twice the bytes)
  *   "short_items"       1: a narrow item of at most 16 rows and "short_tokens"
  *                       tokens runs on one wave (four such planes per workgroup)
  *                       instead of four waves that split its steps and merge

@@ -336,6 +336,9 @@ bool use_mfma(const pkv_pool* p) {
 // The planner options for the kernel path in use.
 SchedOptions planner_options(const pkv_pool* p, bool mfma) {
   SchedOptions o = p->opt;
+  const bool wide_head = p->pool.desc().head_dim > 128;
+  if (o.min_chunk_tokens == 0) o.min_chunk_tokens = wide_head ? 768 : 1024;
+  if (o.tokens_per_row == 0) o.tokens_per_row = wide_head ? 32 : 64;
   if (!mfma) {
     o.rows_per_item = std::min<int32_t>(o.rows_per_item, 16);
     o.wide = false;
@@ -1022,10 +1025,11 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "timing must be 0 or 1");
     pool->timing = value != 0;
   } else if (k == "tokens_per_row") {
-    if (value < 1 || value > 8192) return fail(PKV_E_INVALID, "tokens_per_row must be 1..8192");
+    if (value < 0 || value > 8192) return fail(PKV_E_INVALID, "tokens_per_row must be 0..8192");
     pool->opt.tokens_per_row = (int32_t)value;
   } else if (k == "min_chunk_tokens") {
-    if (value < 32 || value > 8192) return fail(PKV_E_INVALID, "min_chunk_tokens must be 32..8192");
+    if (value != 0 && (value < 32 || value > 8192))
+      return fail(PKV_E_INVALID, "min_chunk_tokens must be 0 or 32..8192");
     pool->opt.min_chunk_tokens = (int32_t)value;
   } else if (k == "target_workgroups") {
     if (value < 1 || value > (1 << 24)) return fail(PKV_E_INVALID, "target_workgroups out of range");

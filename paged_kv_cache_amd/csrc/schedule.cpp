@@ -49,17 +49,19 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   // tokens * 2 * D elements), short enough to fill the machine
   // no chunk spans more than kMaxChunkBlocks blocks
   const int32_t cap = (kMaxChunkBlocks / step_blocks) * step;
+  const int32_t min_chunk = opt.min_chunk_tokens > 0 ? opt.min_chunk_tokens : 1024;
+  const int32_t per_row = opt.tokens_per_row > 0 ? opt.tokens_per_row : 64;
   auto base_len = [&](const Segment& s) {
     if (opt.chunk_tokens > 0) return std::min(round_up(opt.chunk_tokens, step), cap);
     int32_t rows = s.n_hold * G;
-    int32_t t = round_up(std::max(opt.min_chunk_tokens, opt.tokens_per_row * rows), step);
+    int32_t t = round_up(std::max(min_chunk, per_row * rows), step);
     return std::min({t, round_up(opt.max_chunk_tokens, step), cap});
   };
   auto count_wgs = [&](int32_t div) {
     int64_t w = 0;
     for (const Segment& s : segs) {
       int32_t len =
-          std::min(cap, std::max(round_up(opt.min_chunk_tokens, step), round_up(base_len(s) / div, step)));
+          std::min(cap, std::max(round_up(min_chunk, step), round_up(base_len(s) / div, step)));
       if (opt.chunk_tokens > 0) len = base_len(s);
       int64_t chunks = (s.n_tok + len - 1) / len;
       const int64_t rows = (int64_t)s.n_hold * G;
@@ -82,7 +84,7 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
     Segment& s = segs[si];
     int32_t len = opt.chunk_tokens > 0
                       ? base_len(s)
-                      : std::min(cap, std::max(round_up(opt.min_chunk_tokens, step),
+                      : std::min(cap, std::max(round_up(min_chunk, step),
                                                round_up(base_len(s) / div, step)));
     const int32_t nb = (int32_t)s.blocks.size();
     int32_t k = (s.n_tok + len - 1) / len;

@@ -20,9 +20,13 @@ struct SchedOptions {
   int32_t wide_rows = 256;         // rows per wide item at most (also capped by the kernel shape)
   bool wide_fill = true;           // wide items full but the last (else an even split)
   int32_t target_workgroups = 256;  // shorten chunks while the grid has fewer than 3/4 of this
-  int32_t min_chunk_tokens = 1024;
+  // shortest automatic chunk, and chunk length per query row (keeps the
+  // partial states ~3% of the K/V bytes); 0: by head size (1024 and 64 up to
+  // D = 128, 768 and 32 above: a 256-dim step is twice the bytes, and a
+  // wave's chain of dependent steps is what bounds a long narrow item)
+  int32_t min_chunk_tokens = 0;
   int32_t max_chunk_tokens = 8192;
-  int32_t tokens_per_row = 64;     // chunk length per query row (keeps partial traffic ~3%)
+  int32_t tokens_per_row = 0;
   // 16-row blocks one narrow wave may own: 1, 2, or 0 for automatic (2 when
   // items of more than 16 rows hold at least a quarter of the narrow tokens)
   int32_t max_row_blocks_per_wave = 0;

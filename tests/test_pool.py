@@ -580,3 +580,19 @@ def test_fork_many_and_free_many(pkv):
     c.free_many(kids)
     assert [c.refcount(b) for b in c.table(p)] == [1, 1]
     assert c.stats()["live_seqs"] == 1
+
+
+@pytest.mark.parametrize("name,min_chunk,per_row", [("agent", 768, 32), ("beam", 1024, 64), ("mcts", 1024, 64)])
+def test_chunk_defaults_follow_head_size(pkv, name, min_chunk, per_row):
+    """min_chunk_tokens / tokens_per_row 0 (the default) resolve by head
+    size: 768 and 32 above 128 dims (the agent tree, D = 256), 1024 and 64
+    up to 128 (beam, MCTS); set explicitly, the plan is the same."""
+    w = get(name)
+    c, seqs = build_host_tree(pkv, w)
+    auto = c.plan_info(seqs)
+    c.set_option("min_chunk_tokens", min_chunk)
+    c.set_option("tokens_per_row", per_row)
+    assert c.plan_info(seqs) == auto
+    c.set_option("min_chunk_tokens", 0)
+    c.set_option("tokens_per_row", 0)
+    assert c.plan_info(seqs) == auto
