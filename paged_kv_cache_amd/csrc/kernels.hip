@@ -774,6 +774,9 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
     l_run[r] = 0.f;
   }
 
+  // Every row block of the wave is computed, also one past the item's last
+  // (its query is zero and its state is never stored): a guard per product
+  // splits the code into blocks that each wait for their own LDS read.
   auto compute_rb2 = [&](int step, const u32x4* st_sec) __attribute__((always_inline)) {
     const int s = step;
     if (nrb > 0) {
@@ -789,7 +792,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
           const bf16x8 a = as_bf16x8(st_sec[(tau * KS + ks) * 64 + lane]);
 #pragma unroll
           for (int r = 0; r < RBW; ++r)
-            if (r < nrb) sc4[r][tau] = mfma_bf16(a, qv[r][ks], sc4[r][tau]);
+            sc4[r][tau] = mfma_bf16(a, qv[r][ks], sc4[r][tau]);
         }
       const int tbase = 32 * s;
       const bool tail = tbase + 32 > it.n_tok;
@@ -797,7 +800,6 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
       bf16x8 phi[RBW], plo[RBW];
 #pragma unroll
       for (int r = 0; r < RBW; ++r) {
-        if (r > 0 && r >= nrb) continue;
         float sc[8];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
@@ -835,10 +837,8 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
         const bf16x8 a = as_bf16x8(st_sec[(2 * KS + j) * 64 + lane]);
 #pragma unroll
         for (int r = 0; r < RBW; ++r) {
-          if (r == 0 || r < nrb) {
-            acc[r][j] = mfma_bf16(a, phi[r], acc[r][j]);
-            acc[r][j] = mfma_bf16(a, plo[r], acc[r][j]);
-          }
+          acc[r][j] = mfma_bf16(a, phi[r], acc[r][j]);
+          acc[r][j] = mfma_bf16(a, plo[r], acc[r][j]);
         }
       }
     }
