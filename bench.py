@@ -47,10 +47,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash() -> str:
-    """sha256 (first 16 hex) of the kernels and of the planner that cuts
-    their work (both decide the HBM traffic)."""
+    """sha256 (first 16 hex) of the kernels, the planner that cuts their
+    work and the entry points that set its defaults (all decide the HBM
+    traffic)."""
     h = hashlib.sha256()
-    for name in ("kernels.hip", "attn_plan.h", "schedule.hpp", "schedule.cpp"):
+    for name in ("kernels.hip", "attn_plan.h", "schedule.hpp", "schedule.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
