@@ -436,6 +436,8 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.n_branch = S.n_branch;
   a.P = S.P;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.abs_scale_log2 = std::max(std::fabs(a.scale_log2), 1e-30f);
+  a.q_flip = scale < 0.f ? 0x80008000u : 0u;
   // P enters P.V as bf16 plus its bf16 rounding residual: with P alone in
   // bf16 a row whose weight sits on a few keys is off by up to 2^-9 |v|
   const bool lo_split = true;

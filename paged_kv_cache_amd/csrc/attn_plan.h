@@ -70,6 +70,12 @@ struct AttnParams {
   int32_t n_branch;
   int32_t P;
   float scale_log2;         // softmax scale * log2(e)
+  // The wide kernel takes scores unscaled and folds the scale into the
+  // exponent: max(|scale| * log2(e), 1e-30) (a zero scale becomes a tiny
+  // one, so that a masked -inf score still gives 0), with q's sign bits
+  // flipped (q_flip = 0x80008000 on bf16 pairs) when the scale is negative.
+  float abs_scale_log2;
+  uint32_t q_flip;
 };
 
 struct CombineParams {

@@ -243,6 +243,37 @@ __device__ __forceinline__ void rebase(float mx, float& m_ref, float& l_run, f32
   }
 }
 
+// Probabilities of one 16-row block's eight scores per lane: p = 2^(s c - m)
+// with the scale c folded into one FMA (scores stay unscaled until here),
+// converted to bf16 two at a time (v_cvt_pk_bf16_f32), with LO the bf16
+// rounding residual p - bf16(p) as well. Returns the lane's sum of p. Used
+// by the wide kernel, whose math bounds it (MCTS root 228 -> 221 us, verify
+// 280 -> 277 us); in the memory-bound narrow kernel the same change measured
+// 1-1.5% slower, so it keeps the scaled-score form.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <bool LO>
+__device__ __forceinline__ float probs8(const float (&sc)[8], float c, float m_use, bf16x8& phi,
+                                        bf16x8& plo) {
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float p0 = fast_exp2(__builtin_fmaf(sc[e], c, -m_use));
+    const float p1 = fast_exp2(__builtin_fmaf(sc[e + 1], c, -m_use));
+    psum += p0 + p1;
+    const bf16x2 h = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+    phi[e] = h[0];
+    phi[e + 1] = h[1];
+    if (LO) {
+      const f32x2 hf = __builtin_convertvector(h, f32x2);
+      const bf16x2 l = __builtin_convertvector((f32x2){p0 - hf[0], p1 - hf[1]}, bf16x2);
+      plo[e] = l[0];
+      plo[e + 1] = l[1];
+    }
+  }
+  return psum;
+}
+
 // A chunk's block ids are copied to LDS when the workgroup starts (at most
 // kMaxChunkBlocks of them; the planner cuts chunks to fit) and read from
 // there at wave-uniform indexes. Read from global memory as each step
@@ -756,7 +787,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 raw = {0u, 0u, 0u, 0u};
-      if (row_ok[r]) raw = ld16(qp + 32 * ks);
+      if (row_ok[r]) raw = ld16(qp + 32 * ks) ^ p.q_flip;
       qv[r][ks] = as_bf16x8(raw);
     }
     anc[r] = (tree && row_ok[r]) ? p.anc[branch] : ~0ull;
@@ -804,7 +835,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[4 * tau + i] = sc4[r][tau][i] * p.scale_log2;
+          for (int i = 0; i < 4; ++i) sc[4 * tau + i] = sc4[r][tau][i];
         if (tail || tree) {  // wave-uniform: only the chunk's last step and masked steps
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -818,19 +849,10 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
         float mx = sc[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-        mx = max_xor32(max_xor16(mx));
+        mx = max_xor32(max_xor16(mx)) * p.abs_scale_log2;
         rebase(mx, m_run[r], l_run[r], acc[r]);
         const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(sc[e] - m_use);
-          psum += pe;
-          const __bf16 h = (__bf16)pe;
-          phi[r][e] = h;
-          plo[r][e] = (__bf16)(pe - (float)h);
-        }
-        l_run[r] += psum;
+        l_run[r] += probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);
       }
 #pragma unroll
       for (int j = 0; j < DB; ++j) {
@@ -891,7 +913,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[4 * tau + i] = sc4[r][tau][i] * p.scale_log2;
+          for (int i = 0; i < 4; ++i) sc[4 * tau + i] = sc4[r][tau][i];
         if (tail || tree) {  // wave-uniform: only the chunk's last step and masked steps
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
@@ -905,19 +927,10 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
         float mx = sc[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-        mx = max_xor32(max_xor16(mx));
+        mx = max_xor32(max_xor16(mx)) * p.abs_scale_log2;
         rebase(mx, m_run[r], l_run[r], acc[r]);
         const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = fast_exp2(sc[e] - m_use);
-          psum += pe;
-          const __bf16 h = (__bf16)pe;
-          phi[r][e] = h;
-          plo[r][e] = (__bf16)(pe - (float)h);
-        }
-        l_run[r] += psum;
+        l_run[r] += probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -71,7 +71,8 @@ SMALL_DECODE = [
 
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
-               row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256, fold=64):
+               row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256, fold=64,
+               scale=None):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("fold_tokens", fold)
@@ -90,7 +91,7 @@ def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1
         c.set_option("rows_per_item", rows_per_item)
     seqs = [h[s] for s in w.query_sids]
     q = to_device(inp.q)
-    out = c.decode(seqs, q, scale=w.softmax_scale)
+    out = c.decode(seqs, q, scale=w.softmax_scale if scale is None else scale)
     torch.cuda.synchronize()
     res = out.cpu().numpy()
     c.close()
@@ -206,6 +207,20 @@ def test_wide_shapes_match_oracle(w, shape):
     check_close(got, want, f"{w.name} wide {shape}")
 
 
+@pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
+@pytest.mark.parametrize("factor", [-1.0, 0.0, 3.0])
+def test_softmax_scale_sign_and_zero(w, factor):
+    """A negative, zero or large softmax scale: the wide kernel folds the
+    scale into the exponent (unscaled scores, the sign moved onto q), the
+    narrow one scales the scores; both must match the oracle."""
+    scale = factor * w.softmax_scale
+    note(f"scale {w.name} {scale:+.4f}")
+    inp, got = run_decode(w, scale=scale)
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), scale)
+    check_close(got, want, f"{w.name} scale {scale:+.4f}")
+
+
 @pytest.mark.parametrize("name,keep_root", [("tiny_a", True), ("tiny_b", True), ("tiny_b", False)])
 def test_cow_and_writes_bit_exact(name, keep_root):
     """Every live sequence, read through the library's table from the device
@@ -285,7 +300,7 @@ def test_random_traces_device_bit_exact(pkv, seed, dtype, bs):
 
 # ------------------------------------------------------------------ verify
 
-def run_verify(w, order=None, chunk_tokens=0, parents=None, wide_shape=None):
+def run_verify(w, order=None, chunk_tokens=0, parents=None, wide_shape=None, scale=None):
     inp = generate(w)
     if parents is not None:
         inp.parents = parents
@@ -295,7 +310,7 @@ def run_verify(w, order=None, chunk_tokens=0, parents=None, wide_shape=None):
         c.set_option("wide_row_blocks", wide_shape[1])
     c.set_option("chunk_tokens", chunk_tokens)
     reqs = [h[s] for s in w.query_sids]
-    out = c.verify(reqs, inp.parents, to_device(inp.q), scale=w.softmax_scale)
+    out = c.verify(reqs, inp.parents, to_device(inp.q), scale=w.softmax_scale if scale is None else scale)
     torch.cuda.synchronize()
     res = out.cpu().numpy()
     c.close()
@@ -334,6 +349,19 @@ def test_verify_wide_shapes(shape):
         pool = build_oracle(w, inp)
         want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), w.softmax_scale)
         check_close(got, want, f"verify {w.name} wide {shape}")
+
+
+@pytest.mark.parametrize("factor", [-1.0, 0.0])
+def test_verify_scale_sign_and_zero(factor):
+    """Draft-tree verify (the wide kernel, masked tree positions) with a
+    negative or zero softmax scale."""
+    for w in (SMALL_VERIFY[0], SMALL_VERIFY[1]):
+        scale = factor * w.softmax_scale
+        note(f"verify {w.name} scale {scale:+.4f}")
+        inp, got = run_verify(w, scale=scale)
+        pool = build_oracle(w, inp)
+        want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), scale)
+        check_close(got, want, f"verify {w.name} scale {scale:+.4f}")
 
 
 def test_verify_chain_and_star_trees():
