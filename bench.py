@@ -254,6 +254,48 @@ def cpu_baseline_beam(w, inp, budget_s: float):
     return reps, dt
 
 
+def plan_host_us(c, seqs, n_layers) -> float:
+    """Host time of one decode plan (segments, chunks, items), median of 21:
+    the plan cache is keyed by the sequence list, so alternating its order
+    forces a rebuild each call (the same work either way)."""
+    ts = []
+    rev = list(seqs)[::-1]
+    for i in range(21):
+        t0 = time.perf_counter()
+        c.plan_info(rev if i & 1 else seqs, n_layers)
+        ts.append(time.perf_counter() - t0)
+    c.plan_info(seqs)
+    return round(sorted(ts)[len(ts) // 2] * 1e6, 1)
+
+
+def per_layer_launches(c, seqs, q, out, scale, n_layers, torch, reps=5) -> dict:
+    """The secondary figure: the same decode as n_layers single-layer calls
+    (each plans, uploads and launches for its layer). Device time is the
+    summed attention + combine launches per pass (HIP events); wall time
+    includes the host work of every call."""
+    names = ("attention", "attention_wide", "combine")
+
+    def one_pass():
+        for l in range(n_layers):
+            c.decode(seqs, q[l:l + 1], layer0=l, n_layers=1, scale=scale, out=out[l:l + 1])
+
+    one_pass()
+    torch.cuda.synchronize()
+    for k in names:
+        c.timing_read(k)
+    c.set_option("timing", 1)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        one_pass()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / reps
+    c.set_option("timing", 0)
+    dev = {k: c.timing_read(k)[0] / reps for k in names}
+    return {"launches_per_pass": n_layers,
+            "attention_ms": round(dev["attention"] + dev["attention_wide"], 4),
+            "combine_ms": round(dev["combine"], 4), "wall_ms": round(wall * 1e3, 4)}
+
+
 def run_beam(args, pkv, torch):
     w, inp, c, beams, step_k, step_v, q, out = setup_beam(pkv, torch)
     sh = w.shape
@@ -294,6 +336,13 @@ def run_beam(args, pkv, torch):
     c.set_option("timing", 0)
     for kname in ("combine", "append"):
         c.timing_read(kname)
+    # secondary figures on a step's tree kept alive: single-layer launches
+    # and the host planning time
+    kids = beam_step(c, beams, step_k, step_v, q, out, scale, keep=True)
+    torch.cuda.synchronize()
+    layered = per_layer_launches(c, kids, q, out, scale, sh.L, torch)
+    plan_us = plan_host_us(c, kids, sh.L)
+    c.free_many(kids)
     if args.calibrate_copy:
         calibrate_copy(torch)
     ms_step = dt / args.steps * 1e3
@@ -318,6 +367,14 @@ def run_beam(args, pkv, torch):
         "kernel_ms": {k: round(v[0] / max(v[1], 1), 5) for k, v in ktimes.items()},
         "attention_ms_p10_p50_p90": percentiles(per_step),
         "host_ms_per_step": round(t_host / args.steps * 1e3, 4),
+        "plan_host_us": plan_us,
+        "per_layer_launches": layered,
+        # the step's copy-on-write: 8 partly filled tails (15 of 16 slots) copied
+        # for every layer and KV head, K and V (bytes read = bytes written)
+        "cow": {"ops": 8, "bytes_read": 8 * 2 * sh.L * sh.Hkv * 15 * sh.D * 2,
+                "append_ms": round(ktimes["append"][0] / max(ktimes["append"][1], 1), 5),
+                "GB_s": round(2 * 8 * 2 * sh.L * sh.Hkv * 15 * sh.D * 2
+                              / (ktimes["append"][0] / max(ktimes["append"][1], 1) / 1e3) / 1e9, 1)},
         "plan": info,
         "other_bytes_per_step": side_bytes(sh, sh.L, 8, info),
         "roofline": {"bound": "hbm", "kernel": "attn_mfma_kernel", "achieved": round(achieved, 1),
@@ -379,6 +436,11 @@ def run_tree(args, pkv, torch):
     q = to_dev(inp.q)
     res = time_attention(args, c, seqs, q, w, torch, f"{w.name}: {w.note}",
                          inp.parents if w.kind == "verify" else None)
+    if w.kind != "verify":
+        res["plan_host_us"] = plan_host_us(c, seqs, sh.L)
+        if sh.L > 1:
+            out = torch.empty((sh.L, len(seqs), sh.Hq, sh.D), dtype=torch.float32, device="cuda")
+            res["per_layer_launches"] = per_layer_launches(c, seqs, q, out, w.softmax_scale, sh.L, torch)
     if w.kind == "verify":
         res["commit"] = commit_leg(
             c, seqs, w, inp, lambda: c.verify(seqs, inp.parents, q, scale=w.softmax_scale), torch)
