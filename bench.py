@@ -338,11 +338,13 @@ def run_beam(args, pkv, torch):
         c.timing_read(kname)
     # secondary figures on a step's tree kept alive: single-layer launches
     # and the host planning time
-    kids = beam_step(c, beams, step_k, step_v, q, out, scale, keep=True)
-    torch.cuda.synchronize()
-    layered = per_layer_launches(c, kids, q, out, scale, sh.L, torch)
-    plan_us = plan_host_us(c, kids, sh.L)
-    c.free_many(kids)
+    layered = plan_us = None
+    if not args.no_secondary:
+        kids = beam_step(c, beams, step_k, step_v, q, out, scale, keep=True)
+        torch.cuda.synchronize()
+        layered = per_layer_launches(c, kids, q, out, scale, sh.L, torch)
+        plan_us = plan_host_us(c, kids, sh.L)
+        c.free_many(kids)
     if args.calibrate_copy:
         calibrate_copy(torch)
     ms_step = dt / args.steps * 1e3
@@ -436,7 +438,7 @@ def run_tree(args, pkv, torch):
     q = to_dev(inp.q)
     res = time_attention(args, c, seqs, q, w, torch, f"{w.name}: {w.note}",
                          inp.parents if w.kind == "verify" else None)
-    if w.kind != "verify":
+    if w.kind != "verify" and not args.no_secondary:
         res["plan_host_us"] = plan_host_us(c, seqs, sh.L)
         if sh.L > 1:
             out = torch.empty((sh.L, len(seqs), sh.Hq, sh.D), dtype=torch.float32, device="cuda")
@@ -629,6 +631,9 @@ def main():
                     choices=["beam", "mcts", "agent", "verify", "prompt_cache"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary figures (single-layer launches, host planning); "
+                         "for profiler runs, whose per-kernel averages they would mix")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
