@@ -426,6 +426,7 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.n_order = S.n_order_narrow;
   a.n_long = (S.n_narrow - S.n_short) * S.n_layers * d.num_kv_heads;
   a.n_codes = S.n_narrow * S.n_layers * d.num_kv_heads;
+  a.short_by_plane = S.folded ? 1 : 0;
   a.n_items = (int32_t)S.items.size();
   a.n_layers = S.n_layers;
   a.layer0 = layer0;

@@ -60,6 +60,7 @@ struct AttnParams {
   // workgroup takes four codes of short items, one per wave.
   int32_t n_long;
   int32_t n_codes;
+  int32_t short_by_plane;   // short workgroups take four items of one plane (else four planes of one item)
   int32_t n_items;
   int32_t n_layers;
   int32_t layer0;

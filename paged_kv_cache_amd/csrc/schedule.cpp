@@ -196,11 +196,17 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
 void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
   const int32_t LH = n_layers * Hkv;
   order.clear();
-  // narrow launch: no table (code = blockIdx for long items, four codes per
-  // workgroup for the short ones)
+  // narrow launch: no table (code = blockIdx for long items; four short
+  // codes per workgroup: four planes of one item, or, when short shared
+  // segments were folded into per-branch items, four items of one plane with
+  // a plane's workgroups 8 apart: ceil(LH / 8) groups of 8 planes,
+  // ceil(n_short / 4) rounds each)
   const int64_t long_codes = (int64_t)(n_narrow - n_short) * LH;
   const int64_t short_codes = (int64_t)n_short * LH;
-  n_order_narrow = (int32_t)(long_codes + (short_codes + 3) / 4);
+  const int64_t short_wgs = n_short == 0 ? 0
+                            : folded  ? (int64_t)((LH + 7) / 8) * 8 * ((n_short + 3) / 4)
+                                      : (short_codes + 3) / 4;
+  n_order_narrow = (int32_t)(long_codes + short_wgs);
   // wide launch: a unit is (sibling group, plane); the R siblings of a unit
   // are placed 8 workgroups apart, so that with workgroups dealt round-robin
   // to the 8 XCDs they share one XCD (and its L2) and start together
@@ -392,6 +398,7 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
       fold[k] = segs[k].n_hold > 1 && segs[k].n_tok < opt.fold_tokens;
       any = any || fold[k];
     }
+    S->folded = any;
     if (any) {
       // a branch's private segments join its runs too (they are per-branch
       // already): a leaf's folded edges and its own tail make one item

@@ -39,6 +39,7 @@ struct Schedule {
   std::vector<WorkItem> items;     // narrow items (long, then short), then wide items
   int32_t n_narrow = 0;
   int32_t n_short = 0;             // short narrow items (the last n_short of the narrow ones)
+  bool folded = false;             // short shared segments were folded into per-branch items
   int32_t narrow_rw = 1;           // 16-row blocks per wave in the narrow launch
   std::vector<int32_t> order;      // workgroup order of the wide launch
   int32_t n_order_narrow = 0;      // workgroups of the narrow launch (no table)
