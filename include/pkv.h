@@ -363,6 +363,13 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       (its partial states would outweigh its K/V); 0: never
  *   "prefix_cache_blocks" num_blocks: most entries the prompt cache holds
  *                       (0..num_blocks; applies to later inserts)
+ *   "finalize"          1: when every branch has one chunk read by narrow items and
+ *                       the rest by wide items (an MCTS tree: the wide root, each
+ *                       leaf's folded path narrow), the narrow launch, which runs
+ *                       after the wide one, merges each row's partial states and
+ *                       writes the output rows itself: no combine launch; the
+ *                       outputs are bit-identical to the combine's (0: always
+ *                       combine; also off with "concurrent" 1)
  *   "concurrent"        0: 1 runs the wide-item launch on a second stream of the
  *                       library's, forked from and joined back into the caller's
  *                       stream, beside the narrow-item launch

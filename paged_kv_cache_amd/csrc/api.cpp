@@ -427,6 +427,10 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.n_long = (S.n_narrow - S.n_short) * S.n_layers * d.num_kv_heads;
   a.n_codes = S.n_narrow * S.n_layers * d.num_kv_heads;
   a.short_by_plane = S.folded ? 1 : 0;
+  a.comb_ptr = (const int32_t*)(w + S.off_comb_ptr);
+  a.comb_rows = (const int32_t*)(w + S.off_comb_rows);
+  a.out = out;
+  a.finalize = 0;  // set below, once the launches' streams are known
   a.n_items = (int32_t)S.items.size();
   a.n_layers = S.n_layers;
   a.layer0 = layer0;
@@ -447,6 +451,9 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   // chunks and write disjoint partial rows, and together they keep more
   // loads in flight than either alone.
   const bool fork = a.n_order > 0 && S.n_order_wide > 0 && p->concurrent;
+  // the narrow launch writes the outputs itself when the plan allows it and
+  // the wide launch precedes it on the same stream
+  a.finalize = (S.finalize && mfma && !fork && a.n_order > 0) ? 1 : 0;
   hipStream_t wstream = stream;
   LaunchEvents span;  // both attention launches, start to end, on the caller's stream
   if (p->timing) {
@@ -495,6 +502,7 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
     hipError_t e = hipEventRecord(span.stop, stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
+  if (a.finalize) return PKV_OK;
   CombineParams c;
   c.part_ml = a.part_ml;
   c.part_acc = a.part_acc;
@@ -1004,6 +1012,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
     pool->opt.short_items = value != 0;
   } else if (k == "prefix_cache_blocks") {
     return pool->pool.set_prefix_capacity(value);
+  } else if (k == "finalize") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "finalize must be 0 or 1");
+    pool->opt.finalize = value != 0;
   } else if (k == "concurrent") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "concurrent must be 0 or 1");
     pool->concurrent = (int)value;

@@ -61,6 +61,13 @@ struct AttnParams {
   int32_t n_long;
   int32_t n_codes;
   int32_t short_by_plane;   // short workgroups take four items of one plane (else four planes of one item)
+  // With finalize, the narrow launch runs after the wide one and each of its
+  // rows merges its branch's other partial states (comb_ptr / comb_rows, as
+  // the combine reads them) and writes the output row instead of a partial.
+  int32_t finalize;
+  const int32_t* comb_ptr;  // [n_branch + 1]
+  const int32_t* comb_rows; // partial row of q-head offset 0, in logical order
+  float* out;               // [n_layers][n_branch][Hq][D]
   int32_t n_items;
   int32_t n_layers;
   int32_t layer0;

@@ -642,6 +642,54 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     for (int r = 0; r < RW; ++r) {
       if (!row_ok[r]) continue;
       const int row = (rg * RW + r) * 16 + n;
+      if (p.finalize) {
+        // the branch's other partial states (written by the wide launch,
+        // which ran first) merged with this row's, in the combine's order
+        // and arithmetic: per batch of eight, the batch maximum first, then
+        // the entries in logical order; the output row is written here
+        const int crow = it.r0 + row;
+        const int hold = crow / p.G;
+        const int gq = crow - hold * p.G;
+        const int branch = p.holders[it.hold_off + hold];
+        const int64_t pl = (int64_t)(li * p.Hkv + kvh) * p.P;
+        const int own = it.part_row + row;
+        const int e0 = p.comb_ptr[branch], e1 = p.comb_ptr[branch + 1];
+        float M = kNegInf, L = 0.f;
+        f32x4 o[DB];
+#pragma unroll
+        for (int j = 0; j < DB; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int e = e0; e < e1; e += 8) {
+          const int ne = min(8, e1 - e);
+          float bm = kNegInf;
+          for (int k = 0; k < ne; ++k) {
+            const int rk = p.comb_rows[e + k] + gq;
+            bm = fmaxf(bm, rk == own ? m_run[r] : p.part_ml[2 * (pl + rk)]);
+          }
+          const float Mn = fmaxf(M, bm);
+          if (Mn == kNegInf) continue;
+          const float a = M == kNegInf ? 0.f : fast_exp2(M - Mn);
+          L *= a;
+#pragma unroll
+          for (int j = 0; j < DB; ++j) o[j] *= a;
+          for (int k = 0; k < ne; ++k) {
+            const int rk = p.comb_rows[e + k] + gq;
+            const bool mine = rk == own;
+            const float mk = mine ? m_run[r] : p.part_ml[2 * (pl + rk)];
+            const float lk = mine ? l_fin[r] : p.part_ml[2 * (pl + rk) + 1];
+            const float wk = mk == kNegInf ? 0.f : fast_exp2(mk - Mn);
+            L += lk * wk;
+            const float* pa = p.part_acc + (pl + rk) * D;
+#pragma unroll
+            for (int j = 0; j < DB; ++j)
+              o[j] += (mine ? acc[r][j] : *(const f32x4*)(pa + 16 * j + 4 * g)) * wk;
+          }
+          M = Mn;
+        }
+        float* orow = p.out + (((int64_t)li * p.n_branch + branch) * p.Hq + kvh * p.G + gq) * D;
+#pragma unroll
+        for (int j = 0; j < DB; ++j) *(f32x4*)(orow + 16 * j + 4 * g) = o[j] / L;
+        continue;
+      }
       const int64_t prow = (int64_t)(li * p.Hkv + kvh) * p.P + it.part_row + row;
       if (g == 0) {
         p.part_ml[2 * prow] = m_run[r];

@@ -459,6 +459,22 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
     }
   }
   S->comb_ptr[n] = (int32_t)S->comb_rows.size();
+  // final outputs from the narrow launch: every branch has one narrow chunk
+  // and at least one wide item exists (a chunk's items are all wide or all
+  // narrow, by its row count)
+  if (opt.finalize && opt.wide && S->n_narrow < (int32_t)S->items.size()) {
+    const int32_t rpi = std::max<int32_t>(1, opt.rows_per_item);
+    bool ok = true;
+    for (int32_t i = 0; i < n && ok; ++i) {
+      int32_t narrow_chunks = 0;
+      for (int32_t sgi : path[i]) {
+        const Segment& sg = segs[sgi];
+        if (sg.n_hold * G <= rpi) narrow_chunks += sg.chunk_end - sg.chunk_begin;
+      }
+      ok = narrow_chunks == 1;
+    }
+    S->finalize = ok;
+  }
   (void)layer0;
   S->layout(d.num_kv_heads, d.head_dim);
   return PKV_OK;

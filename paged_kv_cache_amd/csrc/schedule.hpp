@@ -33,6 +33,7 @@ struct SchedOptions {
   bool short_items = true;         // one wave per plane for short narrow items
   int32_t short_tokens = kShortTokens;  // longest narrow item (of <= 16 rows) that counts as short
   int32_t fold_tokens = 64;        // shared segments shorter than this are read per branch (0: never)
+  bool finalize = true;            // the narrow launch may write final outputs (see Schedule::finalize)
 };
 
 struct Schedule {
@@ -40,6 +41,10 @@ struct Schedule {
   int32_t n_narrow = 0;
   int32_t n_short = 0;             // short narrow items (the last n_short of the narrow ones)
   bool folded = false;             // short shared segments were folded into per-branch items
+  // Every branch has exactly one chunk read by narrow items and its other
+  // chunks by wide items: the wide launch runs first, so each narrow row can
+  // merge its branch's wide partials itself and write the output (no combine).
+  bool finalize = false;
   int32_t narrow_rw = 1;           // 16-row blocks per wave in the narrow launch
   std::vector<int32_t> order;      // workgroup order of the wide launch
   int32_t n_order_narrow = 0;      // workgroups of the narrow launch (no table)

@@ -195,6 +195,37 @@ def test_concurrent_launches_bit_identical(w):
 WIDE_SHAPES = [(8, 1), (6, 1), (4, 1), (4, 2), (8, 2)]
 
 
+@pytest.mark.parametrize("w", [SMALL_DECODE[3], SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
+def test_final_rows_from_the_narrow_launch(w):
+    """When every branch has one narrow chunk and the rest wide (MCTS-like
+    trees: the root wide, each leaf's folded path narrow), the narrow launch
+    merges the wide partial states and writes the outputs itself, with the
+    combine's arithmetic: the outputs are bit-identical to the combine path
+    (finalize 0) and meet the oracle bar."""
+    inp = generate(w)
+    outs = []
+    for fin in (1, 0):
+        c, h = build_library(pytest.pkv, w, inp)
+        c.set_option("finalize", fin)
+        seqs = [h[s] for s in w.query_sids]
+        for k in ("combine",):
+            c.timing_read(k)
+        c.set_option("timing", 1)
+        out = c.decode(seqs, to_device(inp.q), scale=w.softmax_scale)
+        torch.cuda.synchronize()
+        c.set_option("timing", 0)
+        n_combine = c.timing_read("combine")[1]
+        note(f"{w.name} finalize={fin}: combine launches {n_combine}")
+        outs.append((out.cpu().numpy(), n_combine))
+        c.close()
+    (got, n1), (ref, n0) = outs
+    assert n0 == 1
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), w.name
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"{w.name} final rows from the narrow launch (combine launches {n1})")
+
+
 @pytest.mark.parametrize("w", [SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
 @pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: f"{s[0]}w{s[1]}b")
 def test_wide_shapes_match_oracle(w, shape):
