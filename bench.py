@@ -268,6 +268,26 @@ def plan_host_us(c, seqs, n_layers) -> float:
     return round(sorted(ts)[len(ts) // 2] * 1e6, 1)
 
 
+def fork_ns(c, seq, n=4096, reps=5) -> dict:
+    """Host cost of fork and of free, per sequence: n forks of one sequence
+    in one C call (pkv_seq_fork_many, the argument arrays built beforehand,
+    so the library's loop is what is timed), then one pkv_seq_free_many;
+    best of reps."""
+    from paged_kv_cache_amd import _lib
+    parents = (_lib.PkvSeq * n)(*([seq] * n))
+    kids = (_lib.PkvSeq * n)()
+    best_f = best_d = float("inf")
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        _lib.check(_lib.lib.pkv_seq_fork_many(c.handle, parents, n, kids))
+        t1 = time.perf_counter()
+        _lib.check(_lib.lib.pkv_seq_free_many(c.handle, kids, n))
+        t2 = time.perf_counter()
+        best_f, best_d = min(best_f, t1 - t0), min(best_d, t2 - t1)
+    return {"table_blocks": len(c.table(seq)), "fork_ns": round(best_f / n * 1e9, 1),
+            "free_ns": round(best_d / n * 1e9, 1)}
+
+
 def per_layer_launches(c, seqs, q, out, scale, n_layers, torch, reps=5) -> dict:
     """The secondary figure: the same decode as n_layers single-layer calls
     (each plans, uploads and launches for its layer). Device time is the
@@ -338,12 +358,13 @@ def run_beam(args, pkv, torch):
         c.timing_read(kname)
     # secondary figures on a step's tree kept alive: single-layer launches
     # and the host planning time
-    layered = plan_us = None
+    layered = plan_us = forks = None
     if not args.no_secondary:
         kids = beam_step(c, beams, step_k, step_v, q, out, scale, keep=True)
         torch.cuda.synchronize()
         layered = per_layer_launches(c, kids, q, out, scale, sh.L, torch)
         plan_us = plan_host_us(c, kids, sh.L)
+        forks = fork_ns(c, kids[0])
         c.free_many(kids)
     if args.calibrate_copy:
         calibrate_copy(torch)
@@ -371,6 +392,7 @@ def run_beam(args, pkv, torch):
         "host_ms_per_step": round(t_host / args.steps * 1e3, 4),
         "plan_host_us": plan_us,
         "per_layer_launches": layered,
+        "fork": forks,
         # the step's copy-on-write: 8 partly filled tails (15 of 16 slots) copied
         # for every layer and KV head, K and V (bytes read = bytes written)
         "cow": {"ops": 8, "bytes_read": 8 * 2 * sh.L * sh.Hkv * 15 * sh.D * 2,
@@ -440,6 +462,7 @@ def run_tree(args, pkv, torch):
                          inp.parents if w.kind == "verify" else None)
     if w.kind != "verify" and not args.no_secondary:
         res["plan_host_us"] = plan_host_us(c, seqs, sh.L)
+        res["fork"] = fork_ns(c, seqs[0])
         if sh.L > 1:
             out = torch.empty((sh.L, len(seqs), sh.Hq, sh.D), dtype=torch.float32, device="cuda")
             res["per_layer_launches"] = per_layer_launches(c, seqs, q, out, w.softmax_scale, sh.L, torch)

@@ -614,11 +614,16 @@ int pkv_seq_free_many(pkv_pool* pool, const pkv_seq* seqs, int32_t n) {
   PKV_GUARD_BEGIN
   if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
   if (n < 0 || (n > 0 && !seqs)) return fail(PKV_E_INVALID, "free_many: bad arguments");
+  // every handle valid and listed once (sorted slot indexes; the check is
+  // all-or-nothing, before anything is freed)
+  std::vector<uint32_t> idx((size_t)n);
   for (int32_t i = 0; i < n; ++i) {
     if (!pool->pool.get(seqs[i])) return PKV_E_INVALID;
-    for (int32_t j = 0; j < i; ++j)
-      if (seqs[j].index == seqs[i].index) return fail(PKV_E_INVALID, "free_many: handle listed twice");
+    idx[i] = (uint32_t)seqs[i].index;
   }
+  std::sort(idx.begin(), idx.end());
+  if (std::adjacent_find(idx.begin(), idx.end()) != idx.end())
+    return fail(PKV_E_INVALID, "free_many: handle listed twice");
   for (int32_t i = 0; i < n; ++i) (void)pool->pool.seq_free(seqs[i]);
   return PKV_OK;
   PKV_GUARD_END

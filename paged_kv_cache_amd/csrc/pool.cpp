@@ -8,6 +8,14 @@
 namespace pkv {
 
 namespace {
+
+// Whether a sequence appears more than once in a batch (O(n log n)).
+bool listed_twice(const pkv_seq* seqs, int32_t n) {
+  std::vector<int32_t> idx((size_t)n);
+  for (int32_t i = 0; i < n; ++i) idx[i] = seqs[i].index;
+  std::sort(idx.begin(), idx.end());
+  return std::adjacent_find(idx.begin(), idx.end()) != idx.end();
+}
 thread_local std::string g_err;
 }
 
@@ -364,10 +372,8 @@ int Pool::truncate_append_batch(const pkv_seq* seqs, const int32_t* keep_lens, c
     if (!s) return PKV_E_INVALID;
     if (keep_lens[i] < 0 || keep_lens[i] > s->len)
       return fail(PKV_E_INVALID, "truncate: length outside [0, len]");
-    for (int32_t j = 0; j < i; ++j)
-      if (seqs[j].index == seqs[i].index)
-        return fail(PKV_E_INVALID, "truncate_append: a sequence appears twice");
   }
+  if (listed_twice(seqs, n)) return fail(PKV_E_INVALID, "truncate_append: a sequence appears twice");
   std::vector<std::vector<int32_t>> tails((size_t)n);
   std::vector<int32_t> old_len((size_t)n);
   for (int32_t i = 0; i < n; ++i) {
@@ -398,14 +404,11 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
   if (n < 0 || (n > 0 && (!seqs || !counts))) return fail(PKV_E_INVALID, "append: bad arguments");
   const int64_t bs = d_.block_size;
   // Pass 0: validate.
-  std::vector<int32_t> seen;
+  if (listed_twice(seqs, n)) return fail(PKV_E_INVALID, "append: a sequence appears twice in one batch");
   for (int32_t i = 0; i < n; ++i) {
     const Seq* s = get(seqs[i]);
     if (!s) return PKV_E_INVALID;
     if (counts[i] < 0) return fail(PKV_E_INVALID, "append: negative token count");
-    if (std::find(seen.begin(), seen.end(), seqs[i].index) != seen.end())
-      return fail(PKV_E_INVALID, "append: a sequence appears twice in one batch");
-    seen.push_back(seqs[i].index);
     if ((int64_t)s->len + counts[i] > (int64_t)INT32_MAX)
       return fail(PKV_E_INVALID, "append: sequence length overflow");
   }
