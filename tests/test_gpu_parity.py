@@ -226,6 +226,38 @@ def test_final_rows_from_the_narrow_launch(w):
     check_close(got, want, f"{w.name} final rows from the narrow launch (combine launches {n1})")
 
 
+@pytest.mark.parametrize("rpi", [16, 12, 8])
+def test_final_rows_with_other_item_sizes(rpi):
+    """Final rows with other narrow item sizes on ragged chunks (G = 12):
+    with 16 or 12 rows per item each tail is one narrow item and writes its
+    rows; with 8 the tails go wide and the combine runs; either way the
+    outputs are bit-identical to the combine path."""
+    w = SMALL_DECODE[9]          # beam_wide_d256: G = 12, wide root, narrow tails
+    inp = generate(w)
+    outs = []
+    for fin in (1, 0):
+        c, h = build_library(pytest.pkv, w, inp)
+        c.set_option("finalize", fin)
+        c.set_option("rows_per_item", rpi)
+        seqs = [h[s] for s in w.query_sids]
+        c.timing_read("combine")
+        c.set_option("timing", 1)
+        out = c.decode(seqs, to_device(inp.q), scale=w.softmax_scale)
+        torch.cuda.synchronize()
+        c.set_option("timing", 0)
+        outs.append((out.cpu().numpy(), c.timing_read("combine")[1]))
+        c.close()
+    (got, n1), (ref, n0) = outs
+    # a tail's 12 rows are narrow only while they fit one item (rows above
+    # rows_per_item go to wide items, so a narrow chunk is never split)
+    assert (n1, n0) == ((0, 1) if rpi >= 12 else (1, 1)), (rpi, n1, n0)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), rpi
+    outs = [got]
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(outs[0], want, f"final rows, rows_per_item {rpi}")
+
+
 @pytest.mark.parametrize("w", [SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
 @pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: f"{s[0]}w{s[1]}b")
 def test_wide_shapes_match_oracle(w, shape):
