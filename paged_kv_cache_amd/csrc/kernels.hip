@@ -104,7 +104,9 @@ __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
 // write one (layer, token) of the write list each, all KV heads. Copies are
 // written with non-temporal stores: a decode usually follows, and with the
 // copied tiles left in the caches the attention launch after the append
-// ran ~2% slower (beam step: 97.9 -> 95.7 us with streaming stores).
+// ran ~2% slower (beam step: 97.9 -> 95.7 us with streaming stores). Their
+// sources are read with non-temporal loads too (read once: append 9.65 ->
+// 9.5 us).
 
 template <typename T, int BS>
 __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l, int h) {
@@ -126,7 +128,7 @@ __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l,
     const u32x4* from =
         t < nv ? (const u32x4*)(K + st * tile + (int64_t)t * p.D) + c
                : (const u32x4*)(kn + (((int64_t)l * p.n_tok + tok0 + t - nv) * p.Hkv + h) * p.D) + c;
-    const u32x4 x = *from;
+    const u32x4 x = __builtin_nontemporal_load(from);
     __builtin_nontemporal_store(x, (u32x4*)(K + dt * tile + (int64_t)t * p.D) + c);
   }
   // V rows: whole rows from the source, new tokens patched in (slot k of
@@ -137,7 +139,7 @@ __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l,
     const vecT* vs = (const vecT*)(V + st * tile + (int64_t)d * BS);
     vecT row[RV];
 #pragma unroll
-    for (int c = 0; c < RV; ++c) row[c] = vs[c];
+    for (int c = 0; c < RV; ++c) row[c] = __builtin_nontemporal_load(vs + c);
     const T* vnew = vn + (((int64_t)l * p.n_tok + tok0) * p.Hkv + h) * p.D + d;
 #pragma unroll
     for (int k = 0; k < BS; ++k)
