@@ -157,18 +157,24 @@ def percentiles(xs):
     return [round(pick(0.1), 5), round(pick(0.5), 5), round(pick(0.9), 5)]
 
 
+# largest plan the library passes in the kernel launches' own arguments
+INLINE_PLAN_BYTES = 3072
+
+
 def side_bytes(sh, n_layers, n_rows, info):
     """Bytes a decode moves beside the unique K/V, per call: the queries
     (n_layers x n_rows x Hq x D in the K/V dtype), the float32 output, the
     float32 partial states (D values + running max and sum per partial row
     and plane, written by attention and read by the combine) and the plan
-    records uploaded with it."""
+    records (in the launch arguments when they fit in 3072 bytes, else
+    copied to the device before the launches)."""
     eb = 2 if sh.dtype == "bf16" else 4
     q = n_layers * n_rows * sh.Hq * sh.D * eb
     out = n_layers * n_rows * sh.Hq * sh.D * 4
     part = 2 * info["partial_rows"] * n_layers * sh.Hkv * (sh.D + 2) * 4
-    meta = max(info["workspace_bytes"] - part // 2, 0)
-    return {"q": q, "out": out, "partials": part, "plan_upload": meta}
+    plan = info["plan_bytes"]
+    return {"q": q, "out": out, "partials": part, "plan": plan,
+            "plan_in_launch_args": plan <= INLINE_PLAN_BYTES}
 
 
 def cpu_model() -> str:

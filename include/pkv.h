@@ -205,6 +205,9 @@ typedef struct {
   int32_t partial_rows;   /* partial states per (layer, KV head) */
   int64_t unique_tokens;  /* distinct token slots read per (layer, KV head) */
   int64_t workspace_bytes;
+  int64_t plan_bytes;     /* the plan's arrays: carried in the kernel launches'
+                             arguments when at most 3072 bytes (option
+                             "inline_plan"), else copied into the workspace */
 } pkv_plan_info;
 
 /* Plans decode attention for these sequences (as pkv_decode_workspace_size
@@ -370,6 +373,11 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       writes the output rows itself: no combine launch; the
  *                       outputs are bit-identical to the combine's (0: always
  *                       combine; also off with "concurrent" 1)
+ *   "inline_plan"       1: a decode or verify plan whose arrays fit in 3 KiB (and
+ *                       whose combine lists fit in 1 KiB) travels in the kernel
+ *                       launches' own arguments, so no host-to-device copy of
+ *                       the plan precedes them; outputs are bit-identical either
+ *                       way (0: always stage and copy the plan into the workspace)
  *   "concurrent"        0: 1 runs the wide-item launch on a second stream of the
  *                       library's, forked from and joined back into the caller's
  *                       stream, beside the narrow-item launch

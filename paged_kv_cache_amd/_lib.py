@@ -51,7 +51,8 @@ class PkvStats(ctypes.Structure):
 
 class PkvPlanInfo(ctypes.Structure):
     _fields_ = [("n_segments", c_int32), ("n_chunks", c_int32), ("n_items", c_int32),
-                ("partial_rows", c_int32), ("unique_tokens", c_int64), ("workspace_bytes", c_int64)]
+                ("partial_rows", c_int32), ("unique_tokens", c_int64), ("workspace_bytes", c_int64),
+                ("plan_bytes", c_int64)]
 
 
 class PkvError(RuntimeError):

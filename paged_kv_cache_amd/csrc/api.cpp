@@ -112,6 +112,7 @@ struct pkv_pool {
   int wide_row_blocks = 0;  // 16-row blocks per wave of the wide kernel (1, 2; 0 automatic)
   int prefetch = 0;    // narrow matrix-core kernel loads one step ahead
   int concurrent = 0;  // narrow and wide launches on two streams
+  int inline_plan = 1;  // small schedules travel in the launch arguments (no upload)
 
   // A second stream (default priority) for the wide launch, so that it runs
   // beside the narrow one; created on first use, on the device current then.
@@ -410,25 +411,38 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   if ((uintptr_t)ws % 256) return fail(PKV_E_INVALID, "workspace must be 256-byte aligned");
   if (!std::isfinite(scale)) return fail(PKV_E_INVALID, "scale must be finite");
   uint8_t* w = (uint8_t*)ws;
-  int rc = p->upload(w, S.meta_bytes, stream, [&](uint8_t* h) { S.pack_meta(h); });
-  if (rc) return rc;
+  // A schedule that fits in the launch arguments (the combine's lists in
+  // its own) goes with the launches; otherwise it is staged and copied into
+  // the workspace first.
+  const size_t list_bytes = S.off_anc - S.off_comb_ptr;  // comb_ptr, comb_rows
+  const bool inl = p->inline_plan && S.meta_bytes <= (size_t)kInlineMetaBytes &&
+                   list_bytes <= (size_t)kInlineListBytes;
+  int rc = PKV_OK;
   AttnParams a;
+  if (inl) {
+    S.pack_meta(a.meta.b);
+  } else {
+    rc = p->upload(w, S.meta_bytes, stream, [&](uint8_t* h) { S.pack_meta(h); });
+    if (rc) return rc;
+  }
   a.k_arena = d.k_arena;
   a.v_arena = d.v_arena;
   a.q = q;
   a.part_ml = (float*)(w + S.off_ml);
   a.part_acc = (float*)(w + S.off_acc);
-  a.items = (const WorkItem*)(w + S.off_items);
-  a.blk = (const int32_t*)(w + S.off_blk);
-  a.holders = (const int32_t*)(w + S.off_holders);
-  a.anc = (const uint64_t*)(w + S.off_anc);
-  a.order = (const int32_t*)(w + S.off_order);
+  a.meta_dev = w;
+  a.meta_inline = inl ? 1 : 0;
+  a.off_items = (int32_t)S.off_items;
+  a.off_blk = (int32_t)S.off_blk;
+  a.off_holders = (int32_t)S.off_holders;
+  a.off_anc = (int32_t)S.off_anc;
+  a.off_order = (int32_t)S.off_order;
+  a.off_comb_ptr = (int32_t)S.off_comb_ptr;
+  a.off_comb_rows = (int32_t)S.off_comb_rows;
   a.n_order = S.n_order_narrow;
   a.n_long = (S.n_narrow - S.n_short) * S.n_layers * d.num_kv_heads;
   a.n_codes = S.n_narrow * S.n_layers * d.num_kv_heads;
   a.short_by_plane = S.folded ? 1 : 0;
-  a.comb_ptr = (const int32_t*)(w + S.off_comb_ptr);
-  a.comb_rows = (const int32_t*)(w + S.off_comb_rows);
   a.out = out;
   a.finalize = 0;  // set below, once the launches' streams are known
   a.n_items = (int32_t)S.items.size();
@@ -470,7 +484,6 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   }
   if (S.n_order_wide > 0) {
     AttnParams aw = a;
-    aw.order = a.order;
     aw.n_order = S.n_order_wide;
     rc = p->timed(
         T_WIDE,
@@ -506,8 +519,16 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   CombineParams c;
   c.part_ml = a.part_ml;
   c.part_acc = a.part_acc;
-  c.comb_ptr = (const int32_t*)(w + S.off_comb_ptr);
-  c.comb_rows = (const int32_t*)(w + S.off_comb_rows);
+  c.meta_dev = w;
+  c.lists_inline = inl ? 1 : 0;
+  c.off_comb_ptr = (int32_t)S.off_comb_ptr;
+  c.off_comb_rows = (int32_t)S.off_comb_rows;
+  if (inl) {
+    // the lists keep their offsets relative to the first of them
+    std::memcpy(c.lists, a.meta.b + S.off_comb_ptr, list_bytes);
+    c.off_comb_ptr = 0;
+    c.off_comb_rows = (int32_t)(S.off_comb_rows - S.off_comb_ptr);
+  }
   c.out = out;
   c.n_layers = S.n_layers;
   c.n_branch = S.n_branch;
@@ -929,6 +950,7 @@ int pkv_decode_plan_info(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, in
   info->partial_rows = S.P;
   info->unique_tokens = S.unique_tokens;
   info->workspace_bytes = (int64_t)S.total_bytes;
+  info->plan_bytes = (int64_t)S.meta_bytes;
   return PKV_OK;
   PKV_GUARD_END
 }
@@ -1020,6 +1042,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "finalize") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "finalize must be 0 or 1");
     pool->opt.finalize = value != 0;
+  } else if (k == "inline_plan") {
+    if (value < 0 || value > 1) return fail(PKV_E_INVALID, "inline_plan must be 0 or 1");
+    pool->inline_plan = (int)value;
   } else if (k == "concurrent") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "concurrent must be 0 or 1");
     pool->concurrent = (int)value;

@@ -25,6 +25,12 @@ constexpr int32_t kMaxChunkBlocks = 512;
 // splitting its steps and merging. (A four-wave item pays its start-up
 // chain of dependent loads and the merge for every few steps it loads.)
 constexpr int32_t kShortTokens = 256;
+// Largest schedule (all its arrays, 16-byte aligned) that a launch carries in
+// its own arguments, and the same for the combine's lists. Kernel arguments
+// are written by the runtime as part of the dispatch, so such a call needs no
+// separate host-to-device copy before its first launch.
+constexpr int32_t kInlineMetaBytes = 3072;
+constexpr int32_t kInlineListBytes = 1024;
 
 struct WorkItem {
   int32_t blk_off;    // index in blk[] of the chunk's first block
@@ -43,17 +49,25 @@ static_assert(sizeof(WorkItem) == 48, "WorkItem layout");
 
 // Device-side pointers to a decode / verify schedule and its partials.
 // Partial states are stored per plane (layer, KV head): P rows each.
-struct AttnParams {
+struct AttnCore {
   const void* k_arena;      // [L][NB][Hkv][BS][D]
   const void* v_arena;      // [L][NB][Hkv][D][BS]
   const void* q;            // [n_layers][n_branch][Hq][D]
   float* part_ml;           // [n_layers * Hkv][P][2]: running max (log2 units), sum
   float* part_acc;          // [n_layers * Hkv][P][D]
-  const WorkItem* items;    // [n_items]
-  const int32_t* blk;       // block ids, per chunk padded to a whole 32-token step
-  const int32_t* holders;   // branch index of each holder
-  const uint64_t* anc;      // [n_branch] ancestor-or-self bits (verify only)
-  const int32_t* order;     // wide launch: per workgroup item * (n_layers * Hkv) + layer * Hkv + head, or -1
+  // The schedule's arrays sit at byte offsets from one base: the PlanBytes
+  // passed with the launch when meta_inline (a small schedule then travels
+  // with the launch itself and no upload precedes it), else meta_dev in the
+  // workspace.
+  //   items    WorkItem[n_items]
+  //   blk      block ids, per chunk padded to a whole 32-token step
+  //   holders  branch index of each holder
+  //   anc      uint64 [n_branch] ancestor-or-self bits (verify only)
+  //   order    wide launch: per workgroup item * (n_layers * Hkv) + layer * Hkv + head, or -1
+  //   comb_ptr [n_branch + 1], comb_rows: each branch's partial rows (q-head offset 0) in logical order
+  const uint8_t* meta_dev;
+  int32_t meta_inline;
+  int32_t off_items, off_blk, off_holders, off_anc, off_order, off_comb_ptr, off_comb_rows;
   int32_t n_order;          // workgroups in the launch
   // Narrow launch (no order table): code = item * (n_layers * Hkv) + layer *
   // Hkv + head. Workgroups [0, n_long) take code = blockIdx; after them each
@@ -65,8 +79,6 @@ struct AttnParams {
   // rows merges its branch's other partial states (comb_ptr / comb_rows, as
   // the combine reads them) and writes the output row instead of a partial.
   int32_t finalize;
-  const int32_t* comb_ptr;  // [n_branch + 1]
-  const int32_t* comb_rows; // partial row of q-head offset 0, in logical order
   float* out;               // [n_layers][n_branch][Hq][D]
   int32_t n_items;
   int32_t n_layers;
@@ -86,11 +98,25 @@ struct AttnParams {
   uint32_t q_flip;
 };
 
+// The inline schedule bytes: the kernels take them as a second argument
+// beside AttnCore, so that copies of the small part never carry them.
+struct PlanBytes {
+  alignas(16) uint8_t b[kInlineMetaBytes];
+};
+
+struct AttnParams : AttnCore {
+  PlanBytes meta;
+};
+
 struct CombineParams {
   const float* part_ml;
   const float* part_acc;
-  const int32_t* comb_ptr;   // [n_branch + 1]
-  const int32_t* comb_rows;  // partial row of q-head group offset 0, in logical order
+  // comb_ptr [n_branch + 1] and comb_rows (partial row of q-head group
+  // offset 0, in logical order) at byte offsets from `lists` when
+  // lists_inline, else from meta_dev
+  const uint8_t* meta_dev;
+  int32_t lists_inline;
+  int32_t off_comb_ptr, off_comb_rows;
   float* out;                // [n_layers][n_branch][Hq][D]
   int32_t n_layers;
   int32_t n_branch;
@@ -98,6 +124,7 @@ struct CombineParams {
   int32_t G;
   int32_t Hq;
   int32_t P;
+  alignas(16) uint8_t lists[kInlineListBytes];
 };
 
 }  // namespace pkv

@@ -225,6 +225,28 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// The schedule's arrays, from the launch's own arguments or from the
+// workspace. Both bases are global memory (kernel arguments live there
+// too), which the casts tell the compiler so that every read of the
+// schedule stays a global (or scalar) load.
+struct PlanArrays {
+  const WorkItem* items;
+  const int32_t* blk;
+  const int32_t* holders;
+  const uint64_t* anc;
+  const int32_t* order;
+  const int32_t* comb_ptr;
+  const int32_t* comb_rows;
+};
+typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;
+__device__ __forceinline__ PlanArrays plan_arrays(const AttnCore& p, const PlanBytes& m) {
+  const gbytes_t b = p.meta_inline ? (gbytes_t)(const uint8_t*)m.b : (gbytes_t)p.meta_dev;
+  return {(const WorkItem*)(b + p.off_items),     (const int32_t*)(b + p.off_blk),
+          (const int32_t*)(b + p.off_holders),    (const uint64_t*)(b + p.off_anc),
+          (const int32_t*)(b + p.off_order),      (const int32_t*)(b + p.off_comb_ptr),
+          (const int32_t*)(b + p.off_comb_rows)};
+}
+
 // Online softmax with a lazy reference: a row's probabilities are taken as
 // 2^(s - m) against a reference m that is moved (and the running sum and
 // accumulators rescaled) only when the row's maximum exceeds it by more
@@ -291,7 +313,8 @@ __device__ __forceinline__ int stage_block_ids(int32_t* dst, const int32_t* blk,
 }
 
 template <int D, int BS, bool LO, bool PF, int RW>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes plan_bytes) {
+  const PlanArrays sp = plan_arrays(p, plan_bytes);
   constexpr int KS = D / 32;  // 32-wide k steps of Q.K
   constexpr int DB = D / 16;  // 16-wide d blocks of P.V
   constexpr int ACC_STRIDE = D + 4;
@@ -336,7 +359,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
   const int li = rem / p.Hkv;
   const int kvh = rem - li * p.Hkv;
   const int layer = p.layer0 + li;
-  const WorkItem it = p.items[item_idx];
+  const WorkItem it = sp.items[item_idx];
 
   // row blocks of 16 rows; a wave owns RW consecutive blocks (a row group)
   const int RB = (it.n_rows + 15) >> 4;
@@ -358,7 +381,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
     const int crow = it.r0 + row;
     const int hold = crow / p.G;
     const int gq = crow - hold * p.G;
-    const int branch = row_ok[r] ? p.holders[it.hold_off + hold] : 0;
+    const int branch = row_ok[r] ? sp.holders[it.hold_off + hold] : 0;
     const int qh = kvh * p.G + gq;
     const uint16_t* qp =
         (const uint16_t*)p.q + (((int64_t)li * p.n_branch + branch) * p.Hq + qh) * D + 8 * g;
@@ -368,13 +391,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
       if (row_ok[r]) raw = ld16(qp + 32 * ks);
       qv[r][ks] = as_bf16x8(raw);
     }
-    anc[r] = (tree && row_ok[r]) ? p.anc[branch] : ~0ull;
+    anc[r] = (tree && row_ok[r]) ? sp.anc[branch] : ~0ull;
   }
 
   const uint16_t* K = (const uint16_t*)p.k_arena;
   const uint16_t* V = (const uint16_t*)p.v_arena;
   const int64_t layer_tiles = (int64_t)layer * p.num_blocks * p.Hkv;
-  const int32_t* blk = p.blk + it.blk_off;
+  const int32_t* blk = sp.blk + it.blk_off;
 
   // this lane's token offsets inside a 32-token step: K tile rows and V
   // columns; with 16-token blocks a step spans two blocks (A, B)
@@ -513,9 +536,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
 
   if (active && phase < n_steps) {
     auto ids = [&](int s, int& a, int& b) {
-      const int32_t* src = staged ? blk_s : blk;
-      a = src[(32 * s) / BS];
-      b = src[(32 * s + 16) / BS];
+      // (a branch, not a pointer select: LDS and global reads stay apart)
+      if (staged) {
+        a = blk_s[(32 * s) / BS];
+        b = blk_s[(32 * s + 16) / BS];
+      } else {
+        a = blk[(32 * s) / BS];
+        b = blk[(32 * s + 16) / BS];
+      }
     };
     if (!PF && D <= 128) {
       int bA, bB;
@@ -652,10 +680,10 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
         const int crow = it.r0 + row;
         const int hold = crow / p.G;
         const int gq = crow - hold * p.G;
-        const int branch = p.holders[it.hold_off + hold];
+        const int branch = sp.holders[it.hold_off + hold];
         const int64_t pl = (int64_t)(li * p.Hkv + kvh) * p.P;
         const int own = it.part_row + row;
-        const int e0 = p.comb_ptr[branch], e1 = p.comb_ptr[branch + 1];
+        const int e0 = sp.comb_ptr[branch], e1 = sp.comb_ptr[branch + 1];
         float M = kNegInf, L = 0.f;
         f32x4 o[DB];
 #pragma unroll
@@ -664,7 +692,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
           const int ne = min(8, e1 - e);
           float bm = kNegInf;
           for (int k = 0; k < ne; ++k) {
-            const int rk = p.comb_rows[e + k] + gq;
+            const int rk = sp.comb_rows[e + k] + gq;
             bm = fmaxf(bm, rk == own ? m_run[r] : p.part_ml[2 * (pl + rk)]);
           }
           const float Mn = fmaxf(M, bm);
@@ -674,7 +702,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnParams p) {
 #pragma unroll
           for (int j = 0; j < DB; ++j) o[j] *= a;
           for (int k = 0; k < ne; ++k) {
-            const int rk = p.comb_rows[e + k] + gq;
+            const int rk = sp.comb_rows[e + k] + gq;
             const bool mine = rk == own;
             const float mk = mine ? m_run[r] : p.part_ml[2 * (pl + rk)];
             const float lk = mine ? l_fin[r] : p.part_ml[2 * (pl + rk) + 1];
@@ -724,7 +752,8 @@ template <int D>
 constexpr int wide_loaders() { return D == 256 ? 2 : 1; }
 
 template <int D, int BS, int NC, int RBW>
-__global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kernel(AttnParams p) {
+__global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kernel(AttnCore p, PlanBytes plan_bytes) {
+  const PlanArrays sp = plan_arrays(p, plan_bytes);
   constexpr int KS = D / 32;
   constexpr int DB = D / 16;
   constexpr int NP = wide_loaders<D>();
@@ -741,7 +770,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool loader = wave >= NC;
   const int n = lane & 15, g = lane >> 4;
-  const int code = p.order[blockIdx.x];
+  const int code = sp.order[blockIdx.x];
   if (code < 0) return;
   const int per_item = p.n_layers * p.Hkv;
   const int item_idx = code / per_item;
@@ -749,10 +778,10 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
   const int li = rem / p.Hkv;
   const int kvh = rem - li * p.Hkv;
   const int layer = p.layer0 + li;
-  const WorkItem it = p.items[item_idx];
+  const WorkItem it = sp.items[item_idx];
   const int n_steps = (it.n_tok + 31) >> 5;
   const int last = n_steps - 1;
-  stage_block_ids<BS>(blk_s, p.blk + it.blk_off, n_steps);
+  stage_block_ids<BS>(blk_s, sp.blk + it.blk_off, n_steps);
   __syncthreads();
   const int voff = 8 * g;
 
@@ -851,7 +880,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
     const int crow = it.r0 + row;
     const int hold = crow / p.G;
     const int gq = crow - hold * p.G;
-    const int branch = row_ok[r] ? p.holders[it.hold_off + hold] : 0;
+    const int branch = row_ok[r] ? sp.holders[it.hold_off + hold] : 0;
     const uint16_t* qp = (const uint16_t*)p.q +
                          (((int64_t)li * p.n_branch + branch) * p.Hq + kvh * p.G + gq) * D + 8 * g;
 #pragma unroll
@@ -860,7 +889,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
       if (row_ok[r]) raw = ld16(qp + 32 * ks) ^ p.q_flip;
       qv[r][ks] = as_bf16x8(raw);
     }
-    anc[r] = (tree && row_ok[r]) ? p.anc[branch] : ~0ull;
+    anc[r] = (tree && row_ok[r]) ? sp.anc[branch] : ~0ull;
   }
 
   f32x4 acc[RBW][DB];
@@ -1062,7 +1091,8 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
 // probabilities are broadcast through LDS.
 
 template <typename T, int D, int BS>
-__global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnCore p, PlanBytes plan_bytes) {
+  const PlanArrays sp = plan_arrays(p, plan_bytes);
   constexpr int LPT = 64 / BS;  // lanes per token in the score phase
   constexpr int DPL = D / LPT;  // d per lane in the score phase
   constexpr int DK = D / 64;    // d per lane in the P.V phase
@@ -1082,7 +1112,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   const int li = rem / p.Hkv;
   const int kvh = rem - li * p.Hkv;
   const int layer = p.layer0 + li;
-  const WorkItem it = p.items[item_idx];
+  const WorkItem it = sp.items[item_idx];
   const int nr = it.n_rows;
 
   const T* Q = (const T*)p.q;
@@ -1090,7 +1120,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     const int r = idx / D, d = idx - (idx / D) * D;
     const int crow = it.r0 + r;
     const int hold = crow / p.G, gq = crow - (crow / p.G) * p.G;
-    const int branch = p.holders[it.hold_off + hold];
+    const int branch = sp.holders[it.hold_off + hold];
     qs[r][d] = to_f32<T>(Q[(((int64_t)li * p.n_branch + branch) * p.Hq + kvh * p.G + gq) * D + d]);
   }
   __syncthreads();
@@ -1098,7 +1128,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   const T* K = (const T*)p.k_arena;
   const T* V = (const T*)p.v_arena;
   const int64_t layer_tiles = (int64_t)layer * p.num_blocks * p.Hkv;
-  const int32_t* blk = p.blk + it.blk_off;
+  const int32_t* blk = sp.blk + it.blk_off;
   const int t = lane % BS, part = lane / BS;
 
   float acc[MAXR][DK];
@@ -1248,6 +1278,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 
 template <int D, int WPR>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const gbytes_t lb = p.lists_inline ? (gbytes_t)(const uint8_t*)p.lists : (gbytes_t)p.meta_dev;
+  const int32_t* comb_ptr = (const int32_t*)(lb + p.off_comb_ptr);
+  const int32_t* comb_rows = (const int32_t*)(lb + p.off_comb_rows);
   constexpr int VW = D / 64;
   constexpr int NB = 8;  // partials whose loads are in flight together
   typedef float vec_t __attribute__((ext_vector_type(VW)));
@@ -1264,8 +1297,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int rem = valid ? (int)(orow - li * per_layer) : 0;
   const int b = rem / p.Hq, h = rem - (rem / p.Hq) * p.Hq;
   const int kvh = h / p.G, gq = h - (h / p.G) * p.G;
-  const int e0 = valid ? p.comb_ptr[b] : 0;
-  const int e1 = valid ? p.comb_ptr[b + 1] : 0;
+  const int e0 = valid ? comb_ptr[b] : 0;
+  const int e1 = valid ? comb_ptr[b + 1] : 0;
   const int64_t plane = (int64_t)(li * p.Hkv + kvh) * p.P + gq;
   const int sub = WPR == 1 ? 0 : wave;
 
@@ -1285,7 +1318,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
       li_[k] = 0.f;
       ai[k] = vec_t{};
       if (ek < e1) {
-        const int64_t row = plane + p.comb_rows[ek];
+        const int64_t row = plane + comb_rows[ek];
         mi[k] = p.part_ml[2 * row];
         li_[k] = p.part_ml[2 * row + 1];
         ai[k] = __builtin_nontemporal_load((const vec_t*)(p.part_acc + row * D + lane * VW));
@@ -1389,18 +1422,18 @@ namespace {
 template <int D, bool LO, bool PF, int RW>
 hipError_t launch_mfma_d(int BS, const AttnParams& p, dim3 grid, hipStream_t s, const LaunchEvents& ev) {
   switch (BS) {
-    case 16: return launch(attn_mfma_kernel<D, 16, LO, PF, RW>, grid, dim3(256), s, ev, p);
-    case 32: return launch(attn_mfma_kernel<D, 32, LO, PF, RW>, grid, dim3(256), s, ev, p);
-    default: return launch(attn_mfma_kernel<D, 64, LO, PF, RW>, grid, dim3(256), s, ev, p);
+    case 16: return launch(attn_mfma_kernel<D, 16, LO, PF, RW>, grid, dim3(256), s, ev, (const AttnCore&)p, p.meta);
+    case 32: return launch(attn_mfma_kernel<D, 32, LO, PF, RW>, grid, dim3(256), s, ev, (const AttnCore&)p, p.meta);
+    default: return launch(attn_mfma_kernel<D, 64, LO, PF, RW>, grid, dim3(256), s, ev, (const AttnCore&)p, p.meta);
   }
 }
 
 template <typename T, int D>
 hipError_t launch_valu_d(int BS, const AttnParams& p, dim3 grid, hipStream_t s, const LaunchEvents& ev) {
   switch (BS) {
-    case 16: return launch(attn_valu_kernel<T, D, 16>, grid, dim3(256), s, ev, p);
-    case 32: return launch(attn_valu_kernel<T, D, 32>, grid, dim3(256), s, ev, p);
-    default: return launch(attn_valu_kernel<T, D, 64>, grid, dim3(256), s, ev, p);
+    case 16: return launch(attn_valu_kernel<T, D, 16>, grid, dim3(256), s, ev, (const AttnCore&)p, p.meta);
+    case 32: return launch(attn_valu_kernel<T, D, 32>, grid, dim3(256), s, ev, (const AttnCore&)p, p.meta);
+    default: return launch(attn_valu_kernel<T, D, 64>, grid, dim3(256), s, ev, (const AttnCore&)p, p.meta);
   }
 }
 
@@ -1437,9 +1470,9 @@ hipError_t launch_attn_wide(int D, int BS, int waves, int row_blocks, const Attn
   const dim3 grid((unsigned)p.n_order);
 #define PKV_WIDE(d, nw, rbw)                                                                    \
   switch (BS) {                                                                                 \
-    case 16: return launch(attn_wide_kernel<d, 16, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, p); \
-    case 32: return launch(attn_wide_kernel<d, 32, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, p); \
-    default: return launch(attn_wide_kernel<d, 64, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, p); \
+    case 16: return launch(attn_wide_kernel<d, 16, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, (const AttnCore&)p, p.meta); \
+    case 32: return launch(attn_wide_kernel<d, 32, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, (const AttnCore&)p, p.meta); \
+    default: return launch(attn_wide_kernel<d, 64, nw, rbw>, grid, dim3((nw + wide_loaders<d>()) * 64), stream, ev, (const AttnCore&)p, p.meta); \
   }
   if (D == 64) {
     if (w == 8) {

@@ -235,25 +235,28 @@ void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
 }
 
 void Schedule::layout(int Hkv, int D) {
+  // the schedule's arrays 16-byte aligned and packed (small schedules travel
+  // in the launch's arguments), the partial states 256-byte aligned after them
+  auto align16 = [](size_t x) { return (x + 15) & ~size_t(15); };
   size_t o = 0;
   off_items = o;
-  o = align256(o + items.size() * sizeof(WorkItem));
+  o = align16(o + items.size() * sizeof(WorkItem));
   off_blk = o;
-  o = align256(o + blk.size() * sizeof(int32_t));
+  o = align16(o + blk.size() * sizeof(int32_t));
   off_holders = o;
-  o = align256(o + holders.size() * sizeof(int32_t));
+  o = align16(o + holders.size() * sizeof(int32_t));
   off_comb_ptr = o;
-  o = align256(o + comb_ptr.size() * sizeof(int32_t));
+  o = align16(o + comb_ptr.size() * sizeof(int32_t));
   off_comb_rows = o;
-  o = align256(o + comb_rows.size() * sizeof(int32_t));
+  o = align16(o + comb_rows.size() * sizeof(int32_t));
   off_anc = o;
-  o = align256(o + anc.size() * sizeof(uint64_t));
+  o = align16(o + anc.size() * sizeof(uint64_t));
   off_order = o;
-  o = align256(o + order.size() * sizeof(int32_t));
+  o = align16(o + order.size() * sizeof(int32_t));
   meta_bytes = o;
   const size_t planes = (size_t)n_layers * Hkv;
-  off_ml = o;
-  o = align256(o + planes * P * 2 * sizeof(float));
+  off_ml = align256(o);
+  o = align256(off_ml + planes * P * 2 * sizeof(float));
   off_acc = o;
   o = align256(o + planes * P * (size_t)D * sizeof(float));
   total_bytes = o;

@@ -33,9 +33,12 @@ class _Shape:
 def test_side_bytes_of_a_decode():
     # beam shape: 32 layers, 8 branches, Hq 32, Hkv 8, D 128, bf16; 64 partial rows per plane
     sh = _Shape(32, 8, 128, "bf16")
-    info = {"partial_rows": 64, "workspace_bytes": 64 * 32 * 8 * (128 + 2) * 4 + 2304}
+    info = {"partial_rows": 64, "workspace_bytes": 64 * 32 * 8 * (128 + 2) * 4 + 1792,
+            "plan_bytes": 1632}
     b = bench.side_bytes(sh, 32, 8, info)
     assert b["q"] == 32 * 8 * 32 * 128 * 2
     assert b["out"] == 32 * 8 * 32 * 128 * 4
     assert b["partials"] == 2 * 64 * 32 * 8 * 130 * 4
-    assert b["plan_upload"] == 2304
+    assert b["plan"] == 1632 and b["plan_in_launch_args"]
+    info["plan_bytes"] = 9000
+    assert not bench.side_bytes(sh, 32, 8, info)["plan_in_launch_args"]

@@ -72,9 +72,10 @@ SMALL_DECODE = [
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
                row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256, fold=64,
-               scale=None):
+               scale=None, inline_plan=1):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    c.set_option("inline_plan", inline_plan)
     c.set_option("fold_tokens", fold)
     c.set_option("concurrent", concurrent)
     c.set_option("short_items", short_items)
@@ -258,6 +259,28 @@ def test_final_rows_with_other_item_sizes(rpi):
     check_close(outs[0], want, f"final rows, rows_per_item {rpi}")
 
 
+@pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[3], SMALL_DECODE[8], SMALL_DECODE[9]],
+                         ids=lambda w: w.name)
+def test_plan_in_launch_arguments(w):
+    """A plan of at most 3072 bytes travels in the kernel launches' own
+    arguments (no upload before them); with inline_plan 0 the same plan is
+    staged and copied into the workspace. The kernels read the same arrays
+    either way: bit-identical outputs, which meet the oracle bar (narrow,
+    wide + combine, and wide + final rows from the narrow launch)."""
+    inp = generate(w)
+    c, h = build_library(pytest.pkv, w, inp)
+    info = c.plan_info([h[s] for s in w.query_sids])
+    c.close()
+    note(f"{w.name}: plan {info['plan_bytes']} B")
+    assert 0 < info["plan_bytes"] <= 3072
+    _, got = run_decode(w, inline_plan=1)
+    _, ref = run_decode(w, inline_plan=0)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), w.name
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"{w.name} plan in the launch arguments")
+
+
 @pytest.mark.parametrize("w", [SMALL_DECODE[8], SMALL_DECODE[9]], ids=lambda w: w.name)
 @pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: f"{s[0]}w{s[1]}b")
 def test_wide_shapes_match_oracle(w, shape):
@@ -363,11 +386,13 @@ def test_random_traces_device_bit_exact(pkv, seed, dtype, bs):
 
 # ------------------------------------------------------------------ verify
 
-def run_verify(w, order=None, chunk_tokens=0, parents=None, wide_shape=None, scale=None):
+def run_verify(w, order=None, chunk_tokens=0, parents=None, wide_shape=None, scale=None,
+               inline_plan=1):
     inp = generate(w)
     if parents is not None:
         inp.parents = parents
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
+    c.set_option("inline_plan", inline_plan)
     if wide_shape:
         c.set_option("wide_waves", wide_shape[0])
         c.set_option("wide_row_blocks", wide_shape[1])
@@ -402,6 +427,18 @@ def test_verify_matches_oracle(w, chunk):
     pool = build_oracle(w, inp)
     want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), w.softmax_scale)
     check_close(got, want, f"verify {w.name} chunk={chunk}")
+
+
+@pytest.mark.parametrize("w", SMALL_VERIFY[:2], ids=lambda w: w.name)
+def test_verify_plan_in_launch_arguments(w):
+    """Verify with its plan in the launch arguments and staged: bit-identical
+    outputs that meet the oracle bar."""
+    inp, got = run_verify(w, inline_plan=1)
+    _, ref = run_verify(w, inline_plan=0)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), w.name
+    pool = build_oracle(w, inp)
+    want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"verify {w.name} plan in the launch arguments")
 
 
 @pytest.mark.parametrize("shape", WIDE_SHAPES, ids=lambda s: f"{s[0]}w{s[1]}b")

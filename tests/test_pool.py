@@ -511,6 +511,31 @@ def test_plan_segments_closed_form(pkv, name, segments):
     assert info["workspace_bytes"] > 0
 
 
+def test_plan_bytes_and_the_inline_limit(pkv):
+    """The plan's arrays are packed at 16-byte alignment: the beam step's plan
+    (9 items, 256 block ids, 16 holders, the combine lists) fits the 3072
+    bytes a launch carries in its arguments, so the headline step needs no
+    plan upload; the MCTS plan (hundreds of items) does not and is staged.
+    The workspace holds the plan, then the partial states."""
+    G = 4
+    for name, inline in (("beam", True), ("mcts", False), ("agent", False)):
+        w = get(name)
+        c, seqs = build_host_tree(pkv, w)
+        info = c.plan_info(seqs)
+        pb = info["plan_bytes"]
+        assert pb % 16 == 0 and pb >= info["n_items"] * 48 + 4 * (len(seqs) + 1), (name, pb)
+        assert (pb <= 3072) == inline, (name, pb)
+        part = info["partial_rows"] * w.shape.L * w.shape.Hkv * (w.shape.D + 2) * 4
+        assert info["workspace_bytes"] >= pb + part, name
+    w = get("beam")
+    c, seqs = build_host_tree(pkv, w)
+    info = c.plan_info(seqs)
+    # 9 items (the root's 32 rows, then 8 private tails of 4 rows) x 48 B,
+    # 128 + 8 x 16 block ids, 8 + 8 holders, 9 + 16 list entries
+    assert info["n_items"] == 9
+    assert info["plan_bytes"] == 432 + 1024 + 64 + 48 + 64
+
+
 def test_plan_folds_short_edges_per_leaf(pkv):
     """With fold_tokens above the MCTS edge length (32 tokens), every leaf
     reads its 6 edges (the 5 shared ones and its own) as one item: chunks =
