@@ -229,8 +229,11 @@ int pkv_decode_workspace_size(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seq
  * sequences share are read from HBM once per call and used for all of
  * them. q: device [n_layers][n_seqs][num_q_heads][head_dim] in kv_dtype;
  * out: device float32, same shape. ws: device workspace of ws_bytes >=
- * pkv_decode_workspace_size(...) bytes (256-byte aligned). Every sequence
- * must be non-empty (else PKV_E_INVALID). */
+ * pkv_decode_workspace_size(...) bytes (256-byte aligned); it receives the
+ * plan (unless the plan travels in the launch arguments, option
+ * "inline_plan") and the partial states, so it must not be reused before the
+ * launches on `stream` end. Every sequence must be non-empty (else
+ * PKV_E_INVALID). */
 int pkv_decode_attn(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t layer0,
                     int32_t n_layers, const void* q, float* out, float scale, void* ws,
                     size_t ws_bytes, void* stream);
