@@ -259,14 +259,15 @@ def test_final_rows_with_other_item_sizes(rpi):
     check_close(outs[0], want, f"final rows, rows_per_item {rpi}")
 
 
-@pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[3], SMALL_DECODE[8], SMALL_DECODE[9]],
-                         ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [SMALL_DECODE[1], SMALL_DECODE[2], SMALL_DECODE[3], SMALL_DECODE[8],
+                               SMALL_DECODE[9]], ids=lambda w: w.name)
 def test_plan_in_launch_arguments(w):
     """A plan of at most 3072 bytes travels in the kernel launches' own
     arguments (no upload before them); with inline_plan 0 the same plan is
     staged and copied into the workspace. The kernels read the same arrays
-    either way: bit-identical outputs, which meet the oracle bar (narrow,
-    wide + combine, and wide + final rows from the narrow launch)."""
+    either way: bit-identical outputs, which meet the oracle bar (fp32 on the
+    VALU kernel, narrow, wide + combine, and wide + final rows from the
+    narrow launch)."""
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp)
     info = c.plan_info([h[s] for s in w.query_sids])
