@@ -1,29 +1,32 @@
 #!/usr/bin/env python3
 """Throughput of the copy-on-write paged KV cache on one MI355X.
 
-Default workload (beam search decode step): 8 beams forked from a
-2048-token prompt, each holding 255 private tokens; every step forks each
-beam, appends the beam's next token to the fork (its last block is shared
-and partly filled, so the append copies it on write), runs decode attention
-for all 8 forks over all 32 layers (32 query heads / 8 KV heads, head_dim
-128, block_size 16, bf16 K/V and q), then frees the forks. So one step runs
-every stage of the path: block alloc/free, fork, the append planner with
-copy-on-write, cow_copy, kv_write, the segment planner, paged attention and
-the log-sum-exp combine. The attended sequences are exactly 2048 shared +
-256 private tokens per beam.
+Default run, one JSON line. The headline is decode attention over the MCTS
+tree, the deepest and widest of the workloads: a 4096-token root prompt, a
+binary tree of depth 6 grown by fork + append with 32 tokens of K/V per edge,
+all 64 leaves decoded at once over all 32 layers (32 query heads / 8 KV
+heads, head_dim 128, block_size 16, bf16 K/V and q; root blocks are held by
+64 leaves, depth-k edges by 64/2^k). ``value`` = the unique K/V bytes the
+call must read (distinct blocks x valid slots x 4096 B x 32 layers =
+1,065,353,216 B) divided by the wall time of a call, in GB/s. ``roofline``
+prices the call's two attention launches (the wide-row launch over the
+shared root and the narrow launch over each leaf's path, which also writes
+the outputs) over their summed average durations, measured with HIP events
+on the launch stream, and lists each launch's own fraction.
+``cpu_baseline`` times the CPU oracle on a sample of layers of the same
+inputs, and ``parity`` compares one whole layer of the timed output with
+the oracle (the run exits with status 3 if any check fails).
 
-Prints one JSON line. ``value`` = unique K/V bytes the step's attention must
-read (distinct blocks x valid slots x 4096 B x 32 layers = 512 MiB) divided
-by the wall time of a step, in GB/s. ``roofline`` prices the attention
-kernel alone: the same bytes over its average duration, measured with HIP
-events on the launch stream. ``cpu_baseline`` times the CPU oracle on a
-sample of layers of the same inputs.
+Nested under ``configs``, measured in the same run: the beam search decode
+step (fork every beam, append one token with a copy-on-write of the shared
+15/16-full tail, attention over 32 layers, free), agent decode (4 requests
+sharing 13,312 tokens + 32,768 private each, head_dim 256) and the
+draft-tree verify (4 requests x 32,768 context + 48-node tree) with its
+commit leg; each with its own roofline and parity check. ``ceiling`` is a
+plain device read and copy of 2 GiB, for scale.
 
-Other workloads (``--workload mcts|agent|verify|prompt_cache``) time the
-attention call alone on those trees; they are measurements, not the
-headline line. ``verify`` also times draft-tree commits; ``prompt_cache``
-builds the agent tree by resuming from the prompt cache and reports the
-cache's host latency and the prompt tokens it saves.
+``--workload beam|mcts|agent|verify|prompt_cache`` runs one workload alone
+(for profiler runs and counters).
 """
 
 from __future__ import annotations
@@ -199,6 +202,82 @@ def blas_threads() -> int:
     return os.cpu_count() or 1
 
 
+# ------------------------------------------------------------ oracle legs
+
+MAX_ABS, REL_L2 = 2e-3, 1e-2   # the parity bar of the test suite
+
+
+def oracle_pool(w, inp):
+    """The oracle's pool run through the workload's trace (test
+    infrastructure: used here for the cpu_baseline and parity legs only,
+    outside the timed regions)."""
+    from oracle.pool import OraclePool, run_trace
+    kv = {i: (k, v) for i, _s, k, v in inp.appends}
+    pool = OraclePool(w.num_blocks_bound() + 8, w.shape.BS)
+    run_trace(pool, w.ops, lambda i: (kv[i][0].f32(), kv[i][1].f32()))
+    return pool
+
+
+def compare(got, want) -> dict:
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    ma = float(np.max(np.abs(got - want)))
+    rl = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30))
+    ok = bool(np.all(np.isfinite(got)) and ma <= MAX_ABS and rl <= REL_L2)
+    return {"max_abs": float(f"{ma:.3e}"), "rel_l2": float(f"{rl:.3e}"), "ok": ok}
+
+
+def parity_decode(pool, w, inp, got, layer) -> dict:
+    """One whole layer of a decode output (every branch and query head)
+    against the oracle's float64 result."""
+    import oracle
+    want = oracle.decode(pool, list(w.query_sids), inp.q.f32(), w.softmax_scale, layers=[layer])[0]
+    res = compare(got[layer], want)
+    res.update(layer=layer, rows=int(want.shape[0] * want.shape[1]))
+    return res
+
+
+def parity_verify(pool, w, inp, got, req, nodes) -> dict:
+    """Some tree nodes of one verify request (every query head) against the
+    oracle: node i sees the request's context and its own root path."""
+    import oracle
+    K, V = pool.kv(w.query_sids[req], layer=0)
+    ctx = K.shape[0] - w.n_nodes
+    qf = inp.q.f32()
+    G = w.shape.G
+    gs, ws = [], []
+    for i in nodes:
+        idx = np.concatenate([np.arange(ctx), ctx + np.asarray(oracle.ancestors(inp.parents[req], i))])
+        for g in range(w.shape.Hkv):
+            ws.append(oracle.attention._softmax_attend(qf[req, i, g * G:(g + 1) * G], K[idx, g],
+                                                        V[idx, g], w.softmax_scale))
+            gs.append(got[req, i, g * G:(g + 1) * G])
+    res = compare(np.concatenate(gs), np.concatenate(ws))
+    res.update(request=req, nodes=list(map(int, nodes)), rows=len(nodes) * w.shape.Hq)
+    return res
+
+
+def cpu_baseline_decode(pool, w, q, uniq_bytes_per_layer: int, budget_s: float) -> dict:
+    """The oracle (float64 numpy) timed on the same inputs (q: float32
+    [L][B][Hq][D]): whole layers of the decode (every branch and head), one
+    after another, until the time budget is used (at least one layer)."""
+    import oracle
+    sids = list(w.query_sids)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.decode(pool, sids, q, w.softmax_scale, layers=[done % w.shape.L])
+        done += 1
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or dt / done * (done + 1) > 2 * budget_s:
+            break
+    return {"value": round(uniq_bytes_per_layer * done / dt / 1e9, 4), "unit": "GB/s",
+            "cores": blas_threads(), "kind": "oracle", "cpu": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{done} whole layer(s) of the decode ({len(sids)} branches x {w.shape.Hq} "
+                      f"heads each), same inputs, float64 numpy, {dt:.1f} s",
+            "branch_queries_per_s": round(len(sids) * done / dt, 1)}
+
+
 # ------------------------------------------------------------------ beam
 
 def setup_beam(pkv, torch):
@@ -236,28 +315,6 @@ def beam_step(c, beams, step_k, step_v, q, out, scale, keep=False):
         return kids
     c.free_many(kids)
     return None
-
-
-def cpu_baseline_beam(w, inp, budget_s: float):
-    """The oracle (float64 numpy) on the same inputs, a sample of layers."""
-    import oracle
-    from oracle.pool import OraclePool, run_trace
-    kv = {i: (k, v) for i, _s, k, v in inp.appends}
-    pool = OraclePool(w.num_blocks_bound() + 8, w.shape.BS)
-    run_trace(pool, w.ops, lambda i: (kv[i][0].f32(), kv[i][1].f32()))
-    q = inp.q.f32()
-    sids = list(w.query_sids)
-    # whole passes over all layers until the time budget is used (at least one)
-    layers = list(range(w.shape.L))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.decode(pool, sids, q, w.softmax_scale, layers=layers)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= budget_s or dt / reps * (reps + 1) > 2 * budget_s:
-            break
-    return reps, dt
 
 
 def plan_host_us(c, seqs, n_layers) -> float:
@@ -322,7 +379,7 @@ def per_layer_launches(c, seqs, q, out, scale, n_layers, torch, reps=5) -> dict:
             "combine_ms": round(dev["combine"], 4), "wall_ms": round(wall * 1e3, 4)}
 
 
-def run_beam(args, pkv, torch):
+def run_beam(args, pkv, torch, cpu_baseline=True):
     w, inp, c, beams, step_k, step_v, q, out = setup_beam(pkv, torch)
     sh = w.shape
     scale = w.softmax_scale
@@ -342,6 +399,7 @@ def run_beam(args, pkv, torch):
     t_host = time.perf_counter() - t0
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    got = out.cpu().numpy()     # the last timed step's output
     # kernel durations: the same K steps again with start/end events on every kernel
     for kname in ("attention", "combine", "append"):
         c.timing_read(kname)
@@ -362,16 +420,14 @@ def run_beam(args, pkv, torch):
     c.set_option("timing", 0)
     for kname in ("combine", "append"):
         c.timing_read(kname)
-    # secondary figures on a step's tree kept alive: single-layer launches
-    # and the host planning time
     layered = plan_us = forks = None
-    if not args.no_secondary:
-        kids = beam_step(c, beams, step_k, step_v, q, out, scale, keep=True)
-        torch.cuda.synchronize()
+    kids = beam_step(c, beams, step_k, step_v, q, out, scale, keep=True)
+    torch.cuda.synchronize()
+    if args.secondary:
         layered = per_layer_launches(c, kids, q, out, scale, sh.L, torch)
-        plan_us = plan_host_us(c, kids, sh.L)
-        forks = fork_ns(c, kids[0])
-        c.free_many(kids)
+    plan_us = plan_host_us(c, kids, sh.L)
+    forks = fork_ns(c, kids[0])
+    c.free_many(kids)
     if args.calibrate_copy:
         calibrate_copy(torch)
     ms_step = dt / args.steps * 1e3
@@ -380,6 +436,8 @@ def run_beam(args, pkv, torch):
     attn_avg_s = attn_ms / max(attn_n, 1) / 1e3
     achieved = uniq_bytes / attn_avg_s / 1e9
     traffic = measured_traffic("beam", "attn_mfma_kernel")
+    cow_bytes = 8 * 2 * sh.L * sh.Hkv * 15 * sh.D * 2
+    append_ms = ktimes["append"][0] / max(ktimes["append"][1], 1)
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -401,10 +459,8 @@ def run_beam(args, pkv, torch):
         "fork": forks,
         # the step's copy-on-write: 8 partly filled tails (15 of 16 slots) copied
         # for every layer and KV head, K and V (bytes read = bytes written)
-        "cow": {"ops": 8, "bytes_read": 8 * 2 * sh.L * sh.Hkv * 15 * sh.D * 2,
-                "append_ms": round(ktimes["append"][0] / max(ktimes["append"][1], 1), 5),
-                "GB_s": round(2 * 8 * 2 * sh.L * sh.Hkv * 15 * sh.D * 2
-                              / (ktimes["append"][0] / max(ktimes["append"][1], 1) / 1e3) / 1e9, 1)},
+        "cow": {"ops": 8, "bytes_read": cow_bytes, "append_ms": round(append_ms, 5),
+                "GB_s": round(2 * cow_bytes / (append_ms / 1e3) / 1e9, 1)},
         "plan": info,
         "other_bytes_per_step": side_bytes(sh, sh.L, 8, info),
         "roofline": {"bound": "hbm", "kernel": "attn_mfma_kernel", "achieved": round(achieved, 1),
@@ -412,15 +468,11 @@ def run_beam(args, pkv, torch):
                      "traffic": traffic},
     }
     c.close()
-    if not args.no_cpu_baseline:
-        reps, t = cpu_baseline_beam(w, inp, args.cpu_budget)
-        res["cpu_baseline"] = {
-            "value": round(uniq_bytes * reps / t / 1e9, 4), "unit": "GB/s",
-            "cores": blas_threads(), "kind": "oracle", "cpu": cpu_model(),
-            "host_cpus": os.cpu_count(),
-            "sample": f"{reps} full oracle decode pass(es) of the 8 beams x 32 layers "
-                      f"({t:.1f} s), same inputs, float64 numpy",
-            "branch_queries_per_s": round(8 * sh.L * reps / t, 1)}
+    pool = oracle_pool(w, inp)
+    res["parity"] = parity_decode(pool, w, inp, got, layer=sh.L - 1)
+    if cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(pool, w, inp.q.f32(), uniq_bytes // sh.L,
+                                                  args.cpu_budget)
     return res
 
 
@@ -440,16 +492,41 @@ def calibrate_copy(torch):
     del a, b, flush
 
 
+def ceiling(torch, reps=10) -> dict:
+    """What plain device streaming reaches on this GPU, for scale beside the
+    8 TB/s peak: a 2 GiB bf16 reduction (reads 2 GiB) and a 2 GiB copy
+    (reads and writes 2 GiB), torch's own kernels, HIP events, best of reps.
+    Buffers far larger than the 256 MB last-level cache."""
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    s = torch.empty((), dtype=torch.float32, device="cuda")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        t = float("inf")
+        for _ in range(reps):
+            ev0.record()
+            fn()
+            ev1.record()
+            ev1.synchronize()
+            t = min(t, ev0.elapsed_time(ev1) / 1e3)
+        return t
+
+    t_read = best(lambda: torch.sum(a, dtype=torch.float32, out=s))
+    t_copy = best(lambda: b.copy_(a))
+    del a, b
+    return {"read_GB_s": round(2 * n / t_read / 1e9, 1), "copy_GB_s": round(4 * n / t_copy / 1e9, 1),
+            "bytes": 2 * n, "how": "torch.sum over 2 GiB bf16 (read) and a 2 GiB copy (read + write), "
+                                   "best of 10, HIP events"}
+
+
 # --------------------------------------------------------- other trees
 
-def run_tree(args, pkv, torch):
-    from workloads import generate, get
-    w = get(args.workload)
+def build_tree(pkv, w, inp, extra_blocks=0):
     sh = w.shape
-    inp = generate(w)
-    # verify: room for the contexts to grow by the committed paths
-    extra = len(w.query_sids) * (COMMIT_STEPS * w.n_nodes // sh.BS + 2) if w.kind == "verify" else 0
-    c = pkv.PagedKVCache(w.num_blocks_bound() + 8 + extra, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D,
+    c = pkv.PagedKVCache(w.num_blocks_bound() + 8 + extra_blocks, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D,
                          dtype=sh.dtype)
     kv = {i: (k, v) for i, _s, k, v in inp.appends}
     h = {}
@@ -462,28 +539,55 @@ def run_tree(args, pkv, torch):
             c.append([h[op.sid]], [op.n], to_dev(kv[i][0]), to_dev(kv[i][1]))
         else:
             c.free(h.pop(op.sid))
+    return c, h
+
+
+def run_tree(args, pkv, torch, name, cpu_baseline=False):
+    from workloads import generate, get
+    w = get(name)
+    sh = w.shape
+    inp = generate(w)
+    # verify: room for the contexts to grow by the committed paths
+    extra = len(w.query_sids) * (COMMIT_STEPS * w.n_nodes // sh.BS + 2) if w.kind == "verify" else 0
+    c, h = build_tree(pkv, w, inp, extra)
     seqs = [h[s] for s in w.query_sids]
     q = to_dev(inp.q)
-    res = time_attention(args, c, seqs, q, w, torch, f"{w.name}: {w.note}",
-                         inp.parents if w.kind == "verify" else None)
-    if w.kind != "verify" and not args.no_secondary:
+    res, got = time_attention(args, c, seqs, q, w, torch, f"{w.name}: {w.note}",
+                              inp.parents if w.kind == "verify" else None)
+    if w.kind != "verify":
         res["plan_host_us"] = plan_host_us(c, seqs, sh.L)
         res["fork"] = fork_ns(c, seqs[0])
-        if sh.L > 1:
+        if sh.L > 1 and args.secondary:
             out = torch.empty((sh.L, len(seqs), sh.Hq, sh.D), dtype=torch.float32, device="cuda")
             res["per_layer_launches"] = per_layer_launches(c, seqs, q, out, w.softmax_scale, sh.L, torch)
     if w.kind == "verify":
         res["commit"] = commit_leg(
             c, seqs, w, inp, lambda: c.verify(seqs, inp.parents, q, scale=w.softmax_scale), torch)
     c.close()
+    pool = oracle_pool(w, inp)
+    if w.kind == "verify":
+        import oracle
+        # the first request's deepest node, its root and six more
+        depth = [len(oracle.ancestors(inp.parents[0], i)) for i in range(w.n_nodes)]
+        nodes = sorted({0, int(np.argmax(depth)), *np.random.default_rng(5).choice(w.n_nodes, 6,
+                                                                                   replace=False)})
+        res["parity"] = parity_verify(pool, w, inp, got, 0, nodes)
+    else:
+        res["parity"] = parity_decode(pool, w, inp, got, layer=0)
+    if cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(pool, w, inp.q.f32(),
+                                                  res["unique_kv_bytes_per_step"] // sh.L,
+                                                  args.cpu_budget)
     return res
 
 
 def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
     """Times decode (or, with parents, verify) over seqs: wall time per call
-    and each kernel's device time from HIP events."""
+    and each kernel's device time from HIP events. Returns the record and
+    the output of the last timed call (host copy)."""
     sh = w.shape
-    uniq_bytes = unique_tokens(c, seqs) * sh.token_kv_bytes * sh.L
+    uniq_tok = unique_tokens(c, seqs)
+    uniq_bytes = uniq_tok * sh.token_kv_bytes * sh.L
     if parents is not None:
         out = torch.empty((len(seqs), w.n_nodes, sh.Hq, sh.D), dtype=torch.float32, device="cuda")
         fn = lambda: c.verify(seqs, parents, q, scale=w.softmax_scale, out=out)  # noqa: E731
@@ -498,6 +602,7 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
         fn()
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
+    got = out.cpu().numpy()
     names = ("attention", "attention_wide", "combine")
     for k in names:
         c.timing_read(k)
@@ -518,19 +623,38 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
     if args.calibrate_copy:
         calibrate_copy(torch)
     # the attention bytes are split between the narrow and the wide launch:
-    # price the pair, over their summed durations
-    parts = [n for k, n in (("attention", "attn_mfma_kernel"), ("attention_wide", "attn_wide_kernel"))
+    # price the pair, over their summed durations, and each launch over its
+    # own share of the unique tokens
+    parts = [n for k, n in (("attention_wide", "attn_wide_kernel"), ("attention", "attn_mfma_kernel"))
              if kt[k] > 0]
     kernel = "+".join(parts)
     attn_s = (kt["attention"] + kt["attention_wide"]) / 1e3
     achieved = uniq_bytes / attn_s / 1e9
     info = c.plan_info(seqs) if parents is None else None
-    return {
+    launches = {}
+    if info is not None:
+        wide_bytes = info["wide_tokens"] * sh.token_kv_bytes * sh.L
+        for k, n, b in (("attention_wide", "attn_wide_kernel", wide_bytes),
+                        ("attention", "attn_mfma_kernel", uniq_bytes - wide_bytes)):
+            if kt[k] > 0:
+                gbs = b / (kt[k] / 1e3) / 1e9
+                launches[n] = {"unique_bytes": int(b), "ms": round(kt[k], 5), "GB_s": round(gbs, 1),
+                               "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if kt["attention_wide"] > 0:
+            # matrix-core rate of the wide launch, 4*D flop per (query row, token)
+            rows = sum(1 for _ in seqs) * sh.G  # every branch's rows read the wide chunks
+            flop = 4 * sh.D * rows * info["wide_tokens"] * sh.Hkv * sh.L
+            tf = flop / (kt["attention_wide"] / 1e3) / 1e12
+            launches["attn_wide_kernel"]["mfma_TFLOP_s"] = round(tf, 1)
+            launches["attn_wide_kernel"]["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+    rec = {
         "metric": METRIC, "value": round(uniq_bytes / dt / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": workload, "parallelism": "single GPU"},
+        "config": {"workload": workload, "q_heads": sh.Hq, "kv_heads": sh.Hkv, "head_dim": sh.D,
+                   "block_size": sh.BS, "layers": sh.L, "branches": len(seqs),
+                   "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * uniq_bytes / dt / 1e9 / HBM_PEAK_GBS, 2),
         "branch_queries_per_s": round(n_queries / dt, 1),
         "unique_kv_bytes_per_step": uniq_bytes,
@@ -540,9 +664,10 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
         "other_bytes_per_step": side_bytes(sh, sh.L, len(seqs), info) if info else None,
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name, kernel)},
+                     "traffic": measured_traffic(w.name, kernel), "launches": launches or None},
         "mfma": mfma_rate(c, seqs, w, parents, attn_s) if parents is not None else None,
     }
+    return rec, got
 
 
 def mfma_rate(c, seqs, w, parents, attn_s):
@@ -591,9 +716,9 @@ def run_prompt_cache(args, pkv, torch):
     torch.cuda.synchronize()
     total = sum(len(p) for p in prompts)
     q = torch.randn((sh.L, n_agents, sh.Hq, sh.D), device="cuda").to(torch.bfloat16)
-    res = time_attention(args, c, seqs, q, w, torch,
-                         f"agents resumed from the prompt cache: {n_agents} x ({n_sys} cached "
-                         f"system-prompt tokens + {n_priv} own tokens), block_size {sh.BS}")
+    res, _ = time_attention(args, c, seqs, q, w, torch,
+                            f"agents resumed from the prompt cache: {n_agents} x ({n_sys} cached "
+                            f"system-prompt tokens + {n_priv} own tokens), block_size {sh.BS}")
     entries, _ = c.cache_info()
     res["prompt_cache"] = {
         "prompt_tokens_computed": computed, "prompt_tokens_total": total,
@@ -651,18 +776,56 @@ def commit_leg(c, seqs, w, inp, verify, torch):
             "gather_ms": round(gather / COMMIT_STEPS, 5), "append_ms": round(append / COMMIT_STEPS, 5)}
 
 
+NESTED_KEYS = ("value", "unit", "ms_per_step", "pct_of_hbm_peak", "branch_queries_per_s",
+               "unique_kv_bytes_per_step", "kernel_ms", "attention_ms_p10_p50_p90", "roofline",
+               "mfma", "parity", "cow", "commit", "fork", "plan_host_us", "host_ms_per_step",
+               "per_layer_launches")
+
+
+def nested(rec) -> dict:
+    out = {"workload": rec["config"]["workload"]}
+    out.update({k: rec[k] for k in NESTED_KEYS if rec.get(k) is not None})
+    return out
+
+
+def run_all(args, pkv, torch):
+    """The headline (MCTS decode) with the other configs nested in the same
+    record; every leg checks one layer (or some tree nodes) of its timed
+    output against the oracle."""
+    def note(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    note("bench: mcts (headline)")
+    head = run_tree(args, pkv, torch, "mcts", cpu_baseline=not args.no_cpu_baseline)
+    head["config"]["workload"] = (
+        "MCTS tree decode: 4096-token root, binary tree of depth 6 (32 tokens per edge), all 64 "
+        "leaves decoded at once over 32 layers; 32 q heads / 8 KV heads, head_dim 128, block_size "
+        "16, bf16")
+    configs = {}
+    for name in ("beam_step", "agent", "verify"):
+        note(f"bench: {name}")
+        rec = run_beam(args, pkv, torch, cpu_baseline=False) if name == "beam_step" \
+            else run_tree(args, pkv, torch, name)
+        configs[name] = nested(rec)
+        torch.cuda.empty_cache()
+    head["configs"] = configs
+    note("bench: ceiling")
+    head["ceiling"] = ceiling(torch)
+    return head
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="beam",
-                    choices=["beam", "mcts", "agent", "verify", "prompt_cache"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "beam", "mcts", "agent", "verify", "prompt_cache"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
-    ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the secondary figures (single-layer launches, host planning); "
-                         "for profiler runs, whose per-kernel averages they would mix")
+    ap.add_argument("--secondary", action="store_true",
+                    help="also time the same decode as single-layer launches (its launches "
+                         "would mix into a profiler's per-kernel averages)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -683,13 +846,19 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
-    if args.workload == "beam":
-        res = run_beam(args, pkv, torch)
+    if args.workload == "all":
+        res = run_all(args, pkv, torch)
+    elif args.workload == "beam":
+        res = run_beam(args, pkv, torch, cpu_baseline=not args.no_cpu_baseline)
     elif args.workload == "prompt_cache":
         res = run_prompt_cache(args, pkv, torch)
     else:
-        res = run_tree(args, pkv, torch)
+        res = run_tree(args, pkv, torch, args.workload, cpu_baseline=not args.no_cpu_baseline)
     print(json.dumps(res), flush=True)
+    checks = [res.get("parity")] + [r.get("parity") for r in res.get("configs", {}).values()]
+    if any(c is not None and not c["ok"] for c in checks):
+        print("bench.py: a timed output does not match the oracle", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

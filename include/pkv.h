@@ -103,6 +103,10 @@ typedef struct {
   int32_t live_seqs;
   int32_t reserved;
   int64_t total_refs; /* sum of all block reference counts */
+  /* Block ids and chunk references copied into private table parts since
+   * the pool was created: a fork copies none; the first change to a shared
+   * table copies its list of chunks and at most one chunk of 64 ids. */
+  int64_t table_ids_copied;
 } pkv_stats;
 
 /* ---------------------------------------------------------------- pool */
@@ -208,6 +212,8 @@ typedef struct {
   int64_t plan_bytes;     /* the plan's arrays: carried in the kernel launches'
                              arguments when at most 3072 bytes (option
                              "inline_plan"), else copied into the workspace */
+  int64_t wide_tokens;    /* of unique_tokens, those in chunks served by the
+                             wide-row launch (the rest: the narrow launch) */
 } pkv_plan_info;
 
 /* Plans decode attention for these sequences (as pkv_decode_workspace_size

@@ -11,7 +11,10 @@ import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+# PKV_LIBRARY names another build of the same library (the sanitizer build
+# of the host runtime, ``build.py --sanitize``); by default the in-tree one.
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 PKV_OK = 0
 PKV_E_INVALID = -1
@@ -46,13 +49,14 @@ class PkvPoolDesc(ctypes.Structure):
 
 class PkvStats(ctypes.Structure):
     _fields_ = [("num_blocks", c_int32), ("free_blocks", c_int32), ("live_seqs", c_int32),
-                ("reserved", c_int32), ("total_refs", c_int64)]
+                ("reserved", c_int32), ("total_refs", c_int64),
+                ("table_ids_copied", c_int64)]
 
 
 class PkvPlanInfo(ctypes.Structure):
     _fields_ = [("n_segments", c_int32), ("n_chunks", c_int32), ("n_items", c_int32),
                 ("partial_rows", c_int32), ("unique_tokens", c_int64), ("workspace_bytes", c_int64),
-                ("plan_bytes", c_int64)]
+                ("plan_bytes", c_int64), ("wide_tokens", c_int64)]
 
 
 class PkvError(RuntimeError):

@@ -178,7 +178,7 @@ def pkv_pool_stats(pool) -> dict:
     st = PkvStats()
     check(lib.pkv_pool_stats(pool, byref(st)))
     return {"num_blocks": st.num_blocks, "free_blocks": st.free_blocks, "live_seqs": st.live_seqs,
-            "total_refs": st.total_refs}
+            "total_refs": st.total_refs, "table_ids_copied": st.table_ids_copied}
 
 
 def pkv_pool_set_option(pool, key: str, value: int) -> None:

@@ -1,6 +1,7 @@
 """Builds libpkv.so (HIP for gfx950) in the package directory.
 
     python paged_kv_cache_amd/build.py [-i] [-v]
+    python paged_kv_cache_amd/build.py --sanitize     (host runtime under ASan/UBSan)
 
 (run as a script: importing the package loads the library this builds)
 
@@ -19,6 +20,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -96,5 +98,65 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
     return LIB
 
 
+SAN_DIR = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_DIR, "libpkv_san.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """A debug build of the host runtime for CPU-only checking: the C++
+    sources (pool, planner, C ABI) compiled by g++ with AddressSanitizer and
+    UndefinedBehaviorSanitizer and with PKV_CHECKS (the planner aborts if a
+    write would land in a block that has another holder), linked with the
+    ordinary device object of kernels.hip (no sanitizer in device code) into
+    ``_build/san/libpkv_san.so``. Load it with PKV_LIBRARY pointing at it and
+    the sanitizer runtime preloaded (see README)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    # objects in a directory of this process's own, the library renamed into
+    # place: concurrent builds (parallel test workers) do not mix their files
+    work = tempfile.mkdtemp(dir=SAN_DIR)
+    objs = []
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for s in sources():
+        src = os.path.join(CSRC, s)
+        if s.endswith(".hip"):
+            # the device code as in the ordinary build (reused if up to date)
+            obj = os.path.join(BUILD, s + ".o")
+            if _stale(src, obj):
+                r = subprocess.run(compile_cmd(src, obj), capture_output=True, text=True)
+                if r.returncode != 0:
+                    raise RuntimeError(f"{s}: " + r.stdout + r.stderr)
+            objs.append(obj)
+            continue
+        obj = os.path.join(work, s + ".o")
+        cmd = ["g++", "-std=c++17", "-g", "-O1", "-fno-omit-frame-pointer", "-fPIC",
+               "-D__HIP_PLATFORM_AMD__", "-DPKV_CHECKS", "-I" + os.path.join(rocm, "include"),
+               "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, *SAN_FLAGS, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0 or (verbose and (r.stdout or r.stderr)):
+            print(f"--- {s}\n{r.stdout}{r.stderr}", file=sys.stderr)
+        if r.returncode != 0:
+            raise RuntimeError(f"sanitizer build of {s} failed")
+        objs.append(obj)
+    tmp = os.path.join(work, "libpkv_san.so")
+    link = ["g++", "-shared", *SAN_FLAGS, "-o", tmp, *objs,
+            "-L" + os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(link, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("sanitizer link failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, SAN_LIB)
+    shutil.rmtree(work, ignore_errors=True)
+    return SAN_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of g++'s AddressSanitizer runtime (to preload into Python)."""
+    r = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, incremental="-i" in sys.argv))
+    if "--sanitize" in sys.argv:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv, incremental="-i" in sys.argv))

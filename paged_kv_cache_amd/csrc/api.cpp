@@ -285,6 +285,19 @@ int enqueue_append(pkv_pool* p, const pkv_cow_op* ops, int32_t n_ops, const int6
       wtok.push_back(t);
     }
   }
+  // A write normally never touches a copy's source (the source is shared, so
+  // nobody writes it in place). After a truncate it can: two holders may see
+  // different valid counts in one block, and once the longer holder's copy
+  // is planned the shorter one holds the block alone and writes in place at
+  // an offset the copy still reads. Then the copies run in a launch of
+  // their own, before the writes, on the same stream.
+  bool ordered = false;
+  for (int32_t o = 0; o < n_ops && !ordered; ++o)
+    for (size_t i = 0; i < wslot.size(); ++i)
+      if (wslot[i] / bs == ops[o].src && wslot[i] % bs < ops[o].n_valid) {
+        ordered = true;
+        break;
+      }
   AppendParams a{};
   a.k_new = k_new;
   a.v_new = v_new;
@@ -323,6 +336,16 @@ int enqueue_append(pkv_pool* p, const pkv_cow_op* ops, int32_t n_ops, const int6
     a.wtok = (const int32_t*)(base + o_tok);
     a.ops = (const int32_t*)(base + o_ops);
   }
+  if (ordered) {
+    AppendParams copies = a;
+    copies.n_write = 0;
+    int rc = p->timed(
+        T_APPEND,
+        [&](const LaunchEvents& ev) { return launch_append(d.kv_dtype, copies, stream, ev); },
+        "append launch");
+    if (rc) return rc;
+    a.n_ops = 0;
+  }
   return p->timed(
       T_APPEND, [&](const LaunchEvents& ev) { return launch_append(d.kv_dtype, a, stream, ev); },
       "append launch");
@@ -358,6 +381,8 @@ SchedOptions planner_options(const pkv_pool* p, bool mfma) {
 
 // Builds (or reuses) the decode schedule for these arguments.
 int decode_schedule(pkv_pool* p, const pkv_seq* seqs, int32_t n, int32_t layer0, int32_t n_layers) {
+  // (checked before the cache comparison reads the caller's array)
+  if (n <= 0 || !seqs) return fail(PKV_E_INVALID, "decode: empty batch or null sequence array");
   const bool mfma = use_mfma(p);
   if (p->cache_valid && p->cache_kind == 0 && p->cache_mut == p->pool.mutation() &&
       p->cache_layers == n_layers && p->cache_layer0 == layer0 && p->cache_mfma == mfma &&
@@ -380,6 +405,9 @@ int decode_schedule(pkv_pool* p, const pkv_seq* seqs, int32_t n, int32_t layer0,
 
 int verify_schedule(pkv_pool* p, const pkv_seq* reqs, int32_t n_req, const int32_t* parents,
                     int32_t n_nodes) {
+  // (checked before the cache comparison reads the caller's arrays)
+  if (n_req <= 0 || !reqs || !parents)
+    return fail(PKV_E_INVALID, "verify: empty batch or null request or parent array");
   const size_t np = (size_t)n_req * (size_t)(n_nodes > 0 ? n_nodes : 0);
   if (p->cache_valid && p->cache_kind == 1 && p->cache_mut == p->pool.mutation() &&
       p->cache_nodes == n_nodes && (int32_t)p->cache_seqs.size() == n_req &&
@@ -949,6 +977,7 @@ int pkv_decode_plan_info(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, in
   info->n_items = (int32_t)S.items.size();
   info->partial_rows = S.P;
   info->unique_tokens = S.unique_tokens;
+  info->wide_tokens = S.wide_tokens;
   info->workspace_bytes = (int64_t)S.total_bytes;
   info->plan_bytes = (int64_t)S.meta_bytes;
   return PKV_OK;

@@ -99,14 +99,17 @@ __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) {
 // that land in the block (slots n_valid .. n_valid + m - 1); slots above
 // that are left unspecified. V rows ([BS] per (head, d)) are copied whole
 // with 16-byte vectors and patched in registers. No other workgroup writes
-// the destination block, and a copy's source is shared, so no write
-// touches it: copies and writes need no ordering. The remaining workgroups
-// write one (layer, token) of the write list each, all KV heads. Copies are
-// written with non-temporal stores: a decode usually follows, and with the
-// copied tiles left in the caches the attention launch after the append
-// ran ~2% slower (beam step: 97.9 -> 95.7 us with streaming stores). Their
-// sources are read with non-temporal loads too (read once: append 9.65 ->
-// 9.5 us).
+// the destination block. A copy's source is shared, so in general no write
+// touches it; the one exception (after a truncate, a holder that sees fewer
+// valid slots writes in place once the other holder's copy is planned) is
+// split by the host into a copies-only launch followed by a writes-only
+// launch, so within one launch copies and writes need no ordering. The
+// remaining workgroups write one (layer, token) of the write list each, all
+// KV heads. Copies are written with non-temporal stores: a decode usually
+// follows, and with the copied tiles left in the caches the attention launch
+// after the append ran ~2% slower (beam step: 97.9 -> 95.7 us with streaming
+// stores). Their sources are read with non-temporal loads too (read once:
+// append 9.65 -> 9.5 us).
 
 template <typename T, int BS>
 __device__ __forceinline__ void append_copy(const AppendParams& p, int o, int l, int h) {

@@ -3,6 +3,8 @@
 #include "pool.hpp"
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <unordered_map>
 
 namespace pkv {
@@ -196,6 +198,7 @@ void Pool::own_list(Seq& s) {
   const int32_t l = new_list();  // (may reallocate lists_)
   lists_[l].chunks = lists_[old].chunks;
   for (int32_t c : lists_[l].chunks) ++chunks_[c].ref;
+  ids_copied_ += (int64_t)lists_[l].chunks.size();
   --lists_[old].ref;  // still held by the sequences that shared it
   s.list = l;
 }
@@ -212,6 +215,7 @@ void Pool::own_last_chunk(Seq& s) {
     k.ids[i] = o.ids[i];
     ++ref_[o.ids[i]];
   }
+  ids_copied_ += o.n;
   --chunks_[old].ref;  // still held by the lists that shared it
   lists_[s.list].chunks.back() = c;
 }
@@ -468,6 +472,9 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
         const TChunk& k = chunks_[lists_[s.list].chunks.back()];
         cur = k.ids[k.n - 1];
       }
+#ifdef PKV_CHECKS
+      check_exclusive(s, cur);
+#endif
       if (slots) slots->push_back((int64_t)cur * bs + pos % bs);
       ++s.len;
     }
@@ -476,6 +483,22 @@ int Pool::append_plan_batch(const pkv_seq* seqs, const int32_t* counts, int32_t 
   if (need || n) ++mutation_;
   return PKV_OK;
 }
+
+#ifdef PKV_CHECKS
+// Debug builds (build.py --sanitize): a block about to be written must have
+// exactly one holder ([D2]: a block being written is never aliased): its
+// count is 1 and the table list and chunk through which the writer holds it
+// are the writer's alone. Aborts otherwise.
+void Pool::check_exclusive(const Seq& s, int32_t b) const {
+  const TList& l = lists_[s.list];
+  const TChunk& k = chunks_[l.chunks.back()];
+  if (ref_[b] != 1 || l.ref != 1 || k.ref != 1 || k.n == 0 || k.ids[k.n - 1] != b) {
+    std::fprintf(stderr, "pkv: write into shared block %d (count %d, list %d, chunk %d)\n", b,
+                 ref_[b], l.ref, k.ref);
+    std::abort();
+  }
+}
+#endif
 
 // ------------------------------------------------------------ prompt cache
 
@@ -694,6 +717,7 @@ int Pool::stats(pkv_stats* st) const {
   int64_t refs = 0;
   for (int32_t r : all) refs += r;
   st->total_refs = refs;
+  st->table_ids_copied = ids_copied_;
   return PKV_OK;
 }
 

@@ -158,6 +158,9 @@ class Pool {
   void set_last_id(Seq& s, int32_t b); // replaces the last block id (no count change)
   void cut_table(Seq& s, int32_t keep);  // keeps the first `keep` block ids
   void effective_refs(std::vector<int32_t>& out) const;
+#ifdef PKV_CHECKS
+  void check_exclusive(const Seq& s, int32_t b) const;
+#endif
 
   int32_t find_entry(int32_t parent, const int32_t* toks, uint64_t h) const;
   bool evict_one(uint64_t spare_stamp);  // false: nothing evictable
@@ -176,6 +179,7 @@ class Pool {
   std::vector<int32_t> free_lists_;
   int32_t live_ = 0;
   uint64_t mutation_ = 0;  // bumped by every table change
+  int64_t ids_copied_ = 0;  // block ids and chunk references copied (own_list, own_last_chunk)
 
   std::vector<CacheEntry> ents_;
   std::vector<int32_t> ent_tok_;  // block_size token ids per entry slot

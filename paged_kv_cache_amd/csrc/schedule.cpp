@@ -122,6 +122,7 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
     w.hold_off = s.hold_off;
     w.mask_from = s.mask_from;
     if (opt.wide && rows > rpi) {
+      S->wide_tokens += c.n_tok;
       // wide items of one chunk (siblings) read it through the shared L2
       // (rows split evenly in whole blocks, or with wide_fill every item
       // but the last full)
@@ -309,7 +310,11 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   S->n_layers = n_layers;
   X->ensure(d.num_blocks);
   const uint32_t ep = X->epoch;
-  // pass 1: holder counts, logical position and valid slots of every block
+  // pass 1: holder counts, logical position and valid slots of every block.
+  // Holders of a block hold it at the same position (a fork copies a table
+  // prefix), but after a truncate they may see different valid counts in
+  // it (a kept, partly filled block that a sibling has filled further); such
+  // a block is marked (valid -1) and each holder reads it on its own.
   std::vector<int32_t> distinct;
   for (int32_t i = 0; i < n; ++i) {
     const Seq& s = *sv[i];
@@ -324,8 +329,10 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
         X->valid[b] = v;
         X->seg[b] = -1;
         distinct.push_back(b);
-      } else if (X->pos[b] != j || X->valid[b] != v) {
-        return fail(PKV_E_INVALID, "decode: a shared block differs between its holders");
+      } else if (X->pos[b] != j) {
+        return fail(PKV_E_INVALID, "decode: a shared block sits at two logical positions");
+      } else if (X->valid[b] != v) {
+        X->valid[b] = -1;
       }
       ++X->cnt[b];
     }
@@ -343,51 +350,49 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
     for (int32_t i = 0; i < n; ++i)
       for (int32_t b : pool.blocks(*sv[i])) hold_all[X->off[b] + X->fill[b]++] = i;
   }
-  auto same_holders = [&](int32_t a, int32_t b) {
-    return X->cnt[a] == X->cnt[b] &&
-           std::equal(hold_all.begin() + X->off[a], hold_all.begin() + X->off[a] + X->cnt[a],
-                      hold_all.begin() + X->off[b]);
-  };
-  // segments: maximal runs with one holder set, found by the first holder
+  // segments: maximal runs with one holder set, found by the first holder;
+  // a block read per holder (valid -1) has the holder set {i} for holder i.
+  // Each branch's segments are listed in logical order as they are found.
   std::vector<Segment> segs;
+  std::vector<std::vector<int32_t>> path((size_t)n);
   for (int32_t i = 0; i < n; ++i) {
-    const std::vector<int32_t>& sb = pool.blocks(*sv[i]);
-    int32_t cur = -1, prev = -1;
+    const Seq& s = *sv[i];
+    const std::vector<int32_t>& sb = pool.blocks(s);
+    int32_t cur = -1;
     for (int32_t j = 0; j < (int32_t)sb.size(); ++j) {
       const int32_t b = sb[j];
-      if (X->seg[b] >= 0) {
+      const bool own = X->valid[b] < 0;
+      int32_t sgi;
+      if (!own && X->seg[b] >= 0) {
         cur = -1;
-        prev = b;
-        continue;
-      }
-      if (cur >= 0 && same_holders(b, prev)) {
-        segs[cur].blocks.push_back(b);
-        segs[cur].n_tok += X->valid[b];
+        sgi = X->seg[b];
       } else {
-        Segment sg;
-        sg.blocks.push_back(b);
-        sg.t0 = j * bs;
-        sg.n_tok = X->valid[b];
-        sg.hold_off = (int32_t)S->holders.size();
-        sg.n_hold = X->cnt[b];
-        S->holders.insert(S->holders.end(), hold_all.begin() + X->off[b],
-                          hold_all.begin() + X->off[b] + X->cnt[b]);
-        segs.push_back(std::move(sg));
-        cur = (int32_t)segs.size() - 1;
+        const int32_t* key = own ? &i : hold_all.data() + X->off[b];
+        const int32_t nkey = own ? 1 : X->cnt[b];
+        const int32_t v = own ? std::min(bs, s.len - j * bs) : X->valid[b];
+        if (cur >= 0 && segs[cur].n_hold == nkey &&
+            std::equal(key, key + nkey, S->holders.begin() + segs[cur].hold_off)) {
+          segs[cur].blocks.push_back(b);
+          segs[cur].n_tok += v;
+        } else {
+          Segment sg;
+          sg.blocks.push_back(b);
+          sg.t0 = j * bs;
+          sg.n_tok = v;
+          sg.hold_off = (int32_t)S->holders.size();
+          sg.n_hold = nkey;
+          S->holders.insert(S->holders.end(), key, key + nkey);
+          segs.push_back(std::move(sg));
+          cur = (int32_t)segs.size() - 1;
+        }
+        if (!own) X->seg[b] = cur;
+        sgi = cur;
       }
-      X->seg[b] = cur;
-      prev = b;
+      if (path[i].empty() || path[i].back() != sgi) path[i].push_back(sgi);
     }
   }
   S->n_segments = (int32_t)segs.size();
   for (const Segment& sg : segs) S->unique_tokens += sg.n_tok;
-  // each branch's segments in logical order
-  std::vector<std::vector<int32_t>> path((size_t)n);
-  for (int32_t i = 0; i < n; ++i) {
-    int32_t last = -1;
-    for (int32_t b : pool.blocks(*sv[i]))
-      if (X->seg[b] != last) path[i].push_back(last = X->seg[b]);
-  }
   // Short shared segments are folded into per-branch segments: a shared
   // segment writes one partial state per row it serves, and when it holds
   // few tokens (an MCTS edge: 32 tokens for up to 128 rows per KV head)

@@ -60,6 +60,7 @@ struct Schedule {
   int32_t n_segments = 0;
   int32_t n_chunks = 0;
   int64_t unique_tokens = 0;  // distinct (block, slot) token positions read per plane
+  int64_t wide_tokens = 0;    // of those, the ones in chunks served by wide items
 
   // byte offsets inside the workspace
   size_t off_items = 0, off_blk = 0, off_holders = 0, off_comb_ptr = 0, off_comb_rows = 0,

@@ -42,3 +42,47 @@ def test_side_bytes_of_a_decode():
     assert b["plan"] == 1632 and b["plan_in_launch_args"]
     info["plan_bytes"] = 9000
     assert not bench.side_bytes(sh, 32, 8, info)["plan_in_launch_args"]
+
+
+def test_compare_applies_the_parity_bar():
+    import numpy as np
+    want = np.linspace(-1, 1, 64).reshape(4, 16)
+    assert bench.compare(want + 1e-4, want)["ok"]
+    assert not bench.compare(want + 3e-3, want)["ok"]          # max-abs above 2e-3
+    small = want * 1e-3
+    assert not bench.compare(small * 1.05, small)["ok"]        # relative L2 above 1e-2
+    bad = want.copy()
+    bad[0, 0] = np.nan
+    assert not bench.compare(bad, want)["ok"]
+
+
+def test_parity_legs_on_the_tiny_trees():
+    """The bench's parity legs, fed the oracle's own output (passes) and the
+    same output with one row moved by 4e-3 (fails)."""
+    import numpy as np
+    import oracle
+    from workloads import generate, get, scaled
+    w = get("tiny_b")
+    inp = generate(w)
+    pool = bench.oracle_pool(w, inp)
+    want = oracle.decode(pool, list(w.query_sids), inp.q.f32(), w.softmax_scale)
+    assert bench.parity_decode(pool, w, inp, want, 0)["ok"]
+    off = want.copy()
+    off[0, 1, 2] += 4e-3
+    assert not bench.parity_decode(pool, w, inp, off, 0)["ok"]
+    v = scaled("verify", "verify_tiny", n_req=2, ctx_len=40, n_nodes=9, max_depth=4,
+               shape=get("tiny_a").shape)
+    vin = generate(v)
+    vpool = bench.oracle_pool(v, vin)
+    vwant = oracle.verify(vpool, list(v.query_sids), vin.parents, vin.q.f32(), v.softmax_scale)
+    assert bench.parity_verify(vpool, v, vin, vwant, 1, [0, 3, 8])["ok"]
+    vwant[1, 3, 0, 0] += 4e-3
+    assert not bench.parity_verify(vpool, v, vin, vwant, 1, [0, 3, 8])["ok"]
+
+
+def test_nested_records_keep_the_measured_fields():
+    rec = {"config": {"workload": "x"}, "value": 1.0, "unit": "GB/s", "roofline": {"frac": 0.5},
+           "parity": {"ok": True}, "metric": "m", "n_gpus": 1, "commit": None}
+    out = bench.nested(rec)
+    assert out == {"workload": "x", "value": 1.0, "unit": "GB/s", "roofline": {"frac": 0.5},
+                   "parity": {"ok": True}}

@@ -219,28 +219,30 @@ def test_long_tables_across_chunks_bit_exact(pkv, seed):
 
 
 def test_fork_cost_does_not_grow_with_the_table(pkv):
-    """A fork shares the parent's table: forking a 16,384-block sequence
-    costs about what forking a 16-block one does (both are dominated by
-    the call itself), where copying the table would cost a thousand times
-    more work."""
-    import time
+    """A fork shares the parent's table: forking (and freeing) a 16,384-block
+    sequence copies no block id, however long the table, where a table copy
+    would write 16,384 of them. The first append to a fork copies only the
+    parts it changes: the list of chunk references (one per 64 ids) and the
+    last chunk. Counted by the pool (table_ids_copied), not timed."""
     c = host_cache(pkv, 20000, 1)
     small, big = c.create(), c.create()
     c.plan(small, 16)
     c.plan(big, 16384)
-
-    def cost(seq, reps=3000):
-        best = float("inf")
-        for _ in range(3):
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                c.free(c.fork(seq))
-            best = min(best, time.perf_counter() - t0)
-        return best / reps
-
-    assert cost(big) < 4 * cost(small)
+    for seq, n in ((small, 16), (big, 16384)):
+        before = c.stats()["table_ids_copied"]
+        kids = [c.fork(seq) for _ in range(100)]
+        for k in kids:
+            assert c.table(k) == c.table(seq)
+        assert all(c.refcount(b) == 101 for b in c.table(seq)[:5])
+        c.free_many(kids)
+        assert c.stats()["table_ids_copied"] == before, n
+    # the first append to a fork of the 16,384-block table (block size 1, so
+    # the tail is full and only the list is copied): 256 chunk references
     k = c.fork(big)
-    assert c.table(k) == c.table(big) and c.refcount(c.table(big)[0]) == 2
+    before = c.stats()["table_ids_copied"]
+    c.plan(k, 1)
+    assert c.stats()["table_ids_copied"] - before == 16384 // 64
+    assert c.table(k)[:-1] == c.table(big) and c.refcount(c.table(big)[0]) == 2
 
 
 def test_truncate_rejects_bad_lengths(pkv):
@@ -418,15 +420,24 @@ def test_batch_append_equals_sequential(pkv):
             assert a.table(x) == b.table(y)
 
 
+def visible_stats(c):
+    """The pool's state as callers see it (without the work counter
+    table_ids_copied, which a refused call may advance: it copies private
+    table parts before it counts blocks, invisibly)."""
+    st = dict(c.stats())
+    st.pop("table_ids_copied")
+    return st
+
+
 def test_oom_is_atomic_and_reported(pkv):
     c = host_cache(pkv, 3, 4)
     s = c.create()
     c.plan(s, 6)
     k = c.fork(s)
-    before = (c.table(s), c.table(k), [c.refcount(b) for b in range(3)], c.stats())
+    before = (c.table(s), c.table(k), [c.refcount(b) for b in range(3)], visible_stats(c))
     with pytest.raises(pkv.OOM):
         c.plan(k, 4)            # needs a copy + a fresh block, one is free
-    assert (c.table(s), c.table(k), [c.refcount(b) for b in range(3)], c.stats()) == before
+    assert (c.table(s), c.table(k), [c.refcount(b) for b in range(3)], visible_stats(c)) == before
     c.plan(k, 2)
     assert c.table(k) == [0, 2] and c.refcount(1) == 1
 
@@ -621,3 +632,55 @@ def test_chunk_defaults_follow_head_size(pkv, name, min_chunk, per_row):
     c.set_option("min_chunk_tokens", 0)
     c.set_option("tokens_per_row", 0)
     assert c.plan_info(seqs) == auto
+
+
+def test_plan_truncated_fork_beside_its_sibling(pkv):
+    """After a truncate two holders can see different valid counts in one
+    block (A holds 40 tokens, its fork B was cut to 36: block 2 holds 8 of
+    A's tokens and 4 of B's). Decode plans such a batch: the shared blocks
+    0-1 form one segment read once for both; block 2 is read by each holder
+    on its own, up to its own length."""
+    c = host_cache(pkv, 16, 16)
+    a = c.create()
+    c.plan(a, 40)
+    b = c.fork(a)
+    c.truncate(b, 36)
+    assert c.table(b) == c.table(a) == [0, 1, 2]
+    c.set_option("fold_tokens", 0)
+    info = c.plan_info([a, b])
+    # segments: blocks 0-1 for {A, B}; block 2 for {A} (8 tokens) and for {B} (4)
+    assert info["n_segments"] == 3
+    assert info["unique_tokens"] == 32 + 8 + 4
+    info2 = c.plan_info([b, a])
+    assert info2["n_segments"] == 3 and info2["unique_tokens"] == 44
+    # a third holder agreeing with A: still one read per holder of block 2
+    d = c.fork(a)
+    assert c.plan_info([a, b, d])["unique_tokens"] == 32 + 8 + 4 + 8
+    # A grows past block 2 (copying it on write, B keeps the original)
+    c.free(d)
+    c.plan(a, 20)
+    assert c.table(a)[:2] == [0, 1] and c.table(a)[2] != 2 and c.table(b) == [0, 1, 2]
+    assert c.plan_info([a, b])["n_segments"] == 3
+
+
+def test_null_arrays_after_a_cached_plan(pkv):
+    """A call with a null sequence (or parent) array is refused with
+    PKV_E_INVALID, also right after a successful call of the same size whose
+    plan is cached (the cache comparison must not read through the null)."""
+    import ctypes
+    from paged_kv_cache_amd import _lib
+    c = host_cache(pkv, 16, 16)
+    a = c.create()
+    c.plan(a, 20)
+    b = c.fork(a)
+    c.plan_info([a, b])
+    size = ctypes.c_size_t(0)
+    assert _lib.lib.pkv_decode_workspace_size(c.handle, None, 2, 1, ctypes.byref(size)) == \
+        pkv.PKV_E_INVALID
+    info = _lib.PkvPlanInfo()
+    assert _lib.lib.pkv_decode_plan_info(c.handle, None, 2, 1, ctypes.byref(info)) == \
+        pkv.PKV_E_INVALID
+    assert _lib.lib.pkv_decode_attn(c.handle, None, 2, 0, 1, None, None, ctypes.c_float(1.0),
+                                    None, 0, None) == pkv.PKV_E_INVALID
+    assert _lib.lib.pkv_tree_verify_attn(c.handle, None, 1, None, 4, 0, None, None,
+                                         ctypes.c_float(1.0), None, 0, None) == pkv.PKV_E_INVALID
