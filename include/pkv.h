@@ -244,6 +244,29 @@ int pkv_decode_attn(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t
                     int32_t n_layers, const void* q, float* out, float scale, void* ws,
                     size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * pkv_decode_attn with the workspace taken from a static device array of
+ * the library instead of a caller's buffer. Same arguments, semantics and
+ * outputs as pkv_decode_attn (bit-identical: same plan, same kernels),
+ * minus ws / ws_bytes. It calls no hipMalloc, hipFree, host-pinned
+ * allocation or other allocating device routine: a plan too large for the
+ * launch arguments is written into the array by small copy kernels whose
+ * arguments carry it; the "concurrent" option's second stream and the
+ * "timing" events are not used. The array holds PKV_NOALLOC_WORKSPACE_BYTES
+ * (128 MiB, enough for a 32-layer decode of 64 MCTS leaves) per GPU, from the library's load until the process ends; its
+ * address is looked up on the first call on each device (the device
+ * current at the call; the arenas, q, out and stream must belong to it). A
+ * call needing more than that (pkv_decode_workspace_size) fails with
+ * PKV_E_WORKSPACE before any device work. All calls on one GPU share the
+ * array: calls whose launches overlap in time (other streams, other pools,
+ * other threads) race on it; calls on one stream follow each other safely.
+ * Nothing in the array has to start at zero. */
+#define PKV_NOALLOC_WORKSPACE_BYTES (128u << 20)
+int pkv_decode_attn_noalloc(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t layer0,
+                            int32_t n_layers, const void* q, float* out, float scale,
+                            void* stream);
+
 /* Workspace bytes pkv_tree_verify_attn needs. */
 int pkv_verify_workspace_size(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
                               int32_t n_nodes, size_t* bytes);

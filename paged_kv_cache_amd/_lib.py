@@ -97,6 +97,8 @@ _PROTOS = {
     "pkv_decode_workspace_size": [c_void_p, POINTER(PkvSeq), c_int32, c_int32, POINTER(c_size_t)],
     "pkv_decode_attn": [c_void_p, POINTER(PkvSeq), c_int32, c_int32, c_int32, c_void_p, c_void_p,
                         c_float, c_void_p, c_size_t, c_void_p],
+    "pkv_decode_attn_noalloc": [c_void_p, POINTER(PkvSeq), c_int32, c_int32, c_int32, c_void_p,
+                                c_void_p, c_float, c_void_p],
     "pkv_verify_workspace_size": [c_void_p, POINTER(PkvSeq), c_int32, c_int32, POINTER(c_size_t)],
     "pkv_tree_verify_attn": [c_void_p, POINTER(PkvSeq), c_int32, POINTER(c_int32), c_int32, c_int32,
                              c_void_p, c_void_p, c_float, c_void_p, c_size_t, c_void_p],

@@ -211,6 +211,12 @@ def pkv_decode_attn(pool, seqs: Sequence[PkvSeq], layer0: int, n_layers: int, q,
                               _stream(stream)))
 
 
+def pkv_decode_attn_noalloc(pool, seqs: Sequence[PkvSeq], layer0: int, n_layers: int, q, out,
+                            scale: float, stream=None) -> None:
+    check(lib.pkv_decode_attn_noalloc(pool, _seq_array(seqs), len(seqs), layer0, n_layers,
+                                      _dev_ptr(q), _dev_ptr(out), float(scale), _stream(stream)))
+
+
 def pkv_verify_workspace_size(pool, reqs: Sequence[PkvSeq], n_nodes: int) -> int:
     out = c_size_t()
     check(lib.pkv_verify_workspace_size(pool, _seq_array(reqs), len(reqs), n_nodes, byref(out)))

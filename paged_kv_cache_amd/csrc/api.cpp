@@ -17,6 +17,9 @@
 
 using namespace pkv;
 
+static_assert(kScratchBytes == (size_t)PKV_NOALLOC_WORKSPACE_BYTES,
+              "the header states the static scratch's size");
+
 namespace {
 
 constexpr int kRing = 8;
@@ -105,6 +108,7 @@ struct pkv_pool {
   int ring_next = 0;
   void* dmeta = nullptr;  // device copy of per-call metadata (slots, copy ops)
   size_t dmeta_cap = 0;
+  std::vector<uint8_t> meta_host;  // a packed plan on its way to the static scratch
   PlannerScratch scratch;
   SchedOptions opt;
   int path = 0;  // 0 auto, 1 VALU, 2 matrix cores
@@ -429,8 +433,12 @@ int verify_schedule(pkv_pool* p, const pkv_seq* reqs, int32_t n_req, const int32
 }
 
 // Uploads the schedule into the workspace and launches attention + combine.
+// no_alloc (pkv_decode_attn_noalloc): ws is the static scratch array; a
+// schedule too large for the launch arguments is written into it through
+// copy-kernel arguments (no pinned staging), the wide launch stays on the
+// caller's stream and no timing events are created or recorded.
 int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* out, float scale,
-                  void* ws, size_t ws_bytes, hipStream_t stream) {
+                  void* ws, size_t ws_bytes, hipStream_t stream, bool no_alloc = false) {
   const pkv_pool_desc& d = p->pool.desc();
   const Schedule& S = p->sched;
   if (!ws || ws_bytes < S.total_bytes)
@@ -449,6 +457,11 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   AttnParams a;
   if (inl) {
     S.pack_meta(a.meta.b);
+  } else if (no_alloc) {
+    p->meta_host.resize(S.meta_bytes);
+    S.pack_meta(p->meta_host.data());
+    hipError_t e = launch_arg_copy(w, p->meta_host.data(), S.meta_bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "plan copy launch");
   } else {
     rc = p->upload(w, S.meta_bytes, stream, [&](uint8_t* h) { S.pack_meta(h); });
     if (rc) return rc;
@@ -492,7 +505,15 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   // from and joined back into the caller's stream: the two read disjoint
   // chunks and write disjoint partial rows, and together they keep more
   // loads in flight than either alone.
-  const bool fork = a.n_order > 0 && S.n_order_wide > 0 && p->concurrent;
+  const bool fork = a.n_order > 0 && S.n_order_wide > 0 && p->concurrent && !no_alloc;
+  // (timing events are created on first use: not in the no-allocation form)
+  const bool timing = p->timing;
+  if (no_alloc) p->timing = false;
+  struct Restore {
+    pkv_pool* p;
+    bool t;
+    ~Restore() { p->timing = t; }
+  } restore{p, timing};
   // the narrow launch writes the outputs itself when the plan allows it and
   // the wide launch precedes it on the same stream
   a.finalize = (S.finalize && mfma && !fork && a.n_order > 0) ? 1 : 0;
@@ -1001,6 +1022,33 @@ int pkv_decode_attn(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t
   if (layer0 < 0 || layer0 + n_layers > d.num_layers)
     return fail(PKV_E_INVALID, "decode: layer range outside the pool");
   return run_attention(pool, mfma, layer0, q, out, scale, ws, ws_bytes, (hipStream_t)stream);
+  PKV_GUARD_END
+}
+
+int pkv_decode_attn_noalloc(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, int32_t layer0,
+                            int32_t n_layers, const void* q, float* out, float scale, void* stream) {
+  PKV_GUARD_BEGIN
+  if (!pool_ok(pool)) return fail(PKV_E_INVALID, "null pool");
+  const pkv_pool_desc& d = pool->pool.desc();
+  if (!has_arenas(d)) return fail(PKV_E_INVALID, "pool has no device arenas");
+  if (!q || !out) return fail(PKV_E_INVALID, "decode: null q or out");
+  const bool mfma = use_mfma(pool);
+  if (!attn_supported(mfma, d.kv_dtype, d.head_dim, d.block_size))
+    return fail(PKV_E_UNSUPPORTED, "decode: head_dim must be 64/128/256 and block_size 16/32/64");
+  int rc = decode_schedule(pool, seqs, n_seqs, 0, n_layers);
+  if (rc) return rc;
+  if (layer0 < 0 || layer0 + n_layers > d.num_layers)
+    return fail(PKV_E_INVALID, "decode: layer range outside the pool");
+  if (pool->sched.total_bytes > kScratchBytes)
+    return fail(PKV_E_WORKSPACE, "decode_noalloc: the call needs " +
+                                     std::to_string(pool->sched.total_bytes) +
+                                     " bytes of workspace, more than the static scratch's " +
+                                     std::to_string(kScratchBytes));
+  void* ws = nullptr;
+  hipError_t e = scratch_pointer(&ws);
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  return run_attention(pool, mfma, layer0, q, out, scale, ws, kScratchBytes, (hipStream_t)stream,
+                       true);
   PKV_GUARD_END
 }
 

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -1378,6 +1379,53 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   *(vec_t*)(p.out + orow * D + lane * VW) = acc / L;
 }
 
+// ------------------------------------------------------ static scratch
+//
+// The workspace of pkv_decode_attn_noalloc: plan and partial states of one
+// decode, in memory the library never allocates at call time. Host code
+// uses only the address hipGetSymbolAddress returns for the current device
+// (the array's name in host code is a stand-in, not a device address).
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_pointer(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+struct ArgCopyParams {
+  uint8_t* dst;
+  int32_t n;
+  alignas(16) uint8_t b[kArgCopyBytes];
+};
+
+// One workgroup: thread i copies bytes 4i .. 4i + 3 of the payload.
+__global__ __launch_bounds__(1024) void arg_copy_kernel(ArgCopyParams p) {
+  for (int i = 4 * threadIdx.x; i < p.n; i += 4 * blockDim.x) {
+    if (i + 4 <= p.n && ((uintptr_t)(p.dst + i) & 3) == 0) {
+      uint32_t v;
+      __builtin_memcpy(&v, p.b + i, 4);
+      *(uint32_t*)(p.dst + i) = v;
+    } else {
+      for (int k = i; k < i + 4 && k < p.n; ++k) p.dst[k] = p.b[k];
+    }
+  }
+}
+
 // ------------------------------------------------------------- launchers
 
 namespace {
@@ -1395,6 +1443,20 @@ hipError_t launch(void (*kern)(KArgs...), dim3 grid, dim3 block, hipStream_t str
 }
 
 }  // namespace
+
+hipError_t launch_arg_copy(void* dst, const uint8_t* src, size_t n, hipStream_t stream) {
+  ArgCopyParams a;
+  for (size_t o = 0; o < n; o += kArgCopyBytes) {
+    const size_t m = n - o < (size_t)kArgCopyBytes ? n - o : (size_t)kArgCopyBytes;
+    a.dst = (uint8_t*)dst + o;
+    a.n = (int32_t)m;
+    __builtin_memcpy(a.b, src + o, m);
+    arg_copy_kernel<<<dim3(1), dim3(768), 0, stream>>>(a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_gather(int dtype, const GatherParams& p, hipStream_t stream,
                          const LaunchEvents& ev) {

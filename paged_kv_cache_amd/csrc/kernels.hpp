@@ -107,6 +107,21 @@ hipError_t launch_attn_wide(int D, int BS, int waves, int row_blocks, const Attn
 // block each. The kernel adds its loader waves.
 void attn_wide_shape(int D, int* waves, int* row_blocks);
 
+// ------------------------------------------------------ static scratch
+// Device memory for callers that cannot allocate (pkv_decode_attn_noalloc):
+// a file-scope __device__ array of kScratchBytes in kernels.hip, one copy
+// per GPU, held until the process ends. scratch_pointer returns its device
+// address on the current device, looked up with hipGetSymbolAddress on the
+// first call per device and kept (thread-safe).
+constexpr size_t kScratchBytes = size_t(128) << 20;
+hipError_t scratch_pointer(void** out);
+
+// Writes n bytes from host memory to device memory dst through the launch
+// arguments of a small copy kernel (kArgCopyBytes per launch, in stream
+// order): no pinned staging buffer and no host-to-device copy command.
+constexpr int kArgCopyBytes = 3072;
+hipError_t launch_arg_copy(void* dst, const uint8_t* src, size_t n, hipStream_t stream);
+
 // max_entries: the longest per-branch list of partial states.
 hipError_t launch_combine(int D, int max_entries, const CombineParams& p, hipStream_t stream,
                           const LaunchEvents& ev);
