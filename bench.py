@@ -602,7 +602,7 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
     torch.cuda.synchronize()
     dt = (time.perf_counter() - t0) / args.steps
     got = out.cpu().numpy()
-    names = ("attention", "attention_wide", "combine")
+    names = ("attention", "attention_wide", "attention_tree", "combine")
     for k in names:
         c.timing_read(k)
     c.set_option("timing", 1)
@@ -616,7 +616,8 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
     for _ in range(args.steps):
         fn()
         torch.cuda.synchronize()
-        per_call.append(c.timing_read("attention")[0] + c.timing_read("attention_wide")[0])
+        per_call.append(sum(c.timing_read(k)[0]
+                            for k in ("attention", "attention_wide", "attention_tree")))
     c.set_option("timing", 0)
     c.timing_read("combine")
     if args.calibrate_copy:
@@ -624,14 +625,24 @@ def time_attention(args, c, seqs, q, w, torch, workload: str, parents=None):
     # the attention bytes are split between the narrow and the wide launch:
     # price the pair, over their summed durations, and each launch over its
     # own share of the unique tokens
-    parts = [n for k, n in (("attention_wide", "attn_wide_kernel"), ("attention", "attn_mfma_kernel"))
-             if kt[k] > 0]
+    parts = [n for k, n in (("attention_tree", "attn_tree_kernel"), ("attention_wide", "attn_wide_kernel"),
+                            ("attention", "attn_mfma_kernel")) if kt[k] > 0]
     kernel = "+".join(parts)
-    attn_s = (kt["attention"] + kt["attention_wide"]) / 1e3
+    attn_s = (kt["attention"] + kt["attention_wide"] + kt["attention_tree"]) / 1e3
     achieved = uniq_bytes / attn_s / 1e9
     info = c.plan_info(seqs) if parents is None else None
     launches = {}
-    if info is not None:
+    if info is not None and kt["attention_tree"] > 0:
+        # one launch reads every unique token once; its matrix-core work is
+        # 4*D flop per (query row, token of that row's sequence)
+        gbs = uniq_bytes / (kt["attention_tree"] / 1e3) / 1e9
+        flop = 4 * sh.D * sh.Hq * sh.L * sum(c.length(s) for s in seqs)
+        tf = flop / (kt["attention_tree"] / 1e3) / 1e12
+        launches["attn_tree_kernel"] = {
+            "unique_bytes": int(uniq_bytes), "ms": round(kt["attention_tree"], 5),
+            "GB_s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_TFLOP_s": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    elif info is not None:
         wide_bytes = info["wide_tokens"] * sh.token_kv_bytes * sh.L
         for k, n, b in (("attention_wide", "attn_wide_kernel", wide_bytes),
                         ("attention", "attn_mfma_kernel", uniq_bytes - wide_bytes)):

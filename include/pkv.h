@@ -424,6 +424,18 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       most 16 * waves * row blocks rows
  *   "target_workgroups" 256: chunks are shortened (down to 1024 tokens) while the
  *                       grid has fewer than 3/4 of this many workgroups
+ *   "tree"              1: a decode whose rows all fit one workgroup (branches x
+ *                       query-head group <= 256) at head_dim 64 or 128 (bf16) runs
+ *                       as one launch with one workgroup per (layer, KV head) that
+ *                       reads every chunk of the batch once for all rows holding
+ *                       it and writes the outputs (no partial states, no combine),
+ *                       when some segment has more rows than a narrow item and the
+ *                       (layer, KV head) planes alone fill the chip (at least 3/4
+ *                       of "target_workgroups"); 2: whenever the rows fit; 0: never
+ *   "tree_stages"       4: LDS ring depth of the tree launch (3 or 4)
+ *   "tree_piece_tokens" 512: segments of 64 or more rows are cut into pieces of
+ *                       this many tokens, spread among the narrower segments
+ *                       (32..8192)
  *   "timing"            0: 1 records a pair of HIP events at the start and end
  *                       of every kernel the pool launches (pkv_timing_read)
  * Unknown keys or out-of-range values are PKV_E_INVALID. */
@@ -432,8 +444,8 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value);
 /* Device time of the kernels launched since the last read (with the
  * "timing" option on): kernel is "attention" (items of few rows),
  * "attention_wide" (items of many rows; the two may overlap in time),
- * "attention_span" (from before the first to after the last attention
- * launch of a call, on the caller's stream), "combine", "append" (the
+ * "attention_tree" (the tree launch), "attention_span" (from before the first
+ * to after the last attention launch of a call, on the caller's stream), "combine", "append" (the
  * launch that performs copy-on-write copies and token writes) or
  * "commit_gather" (the read-out of a committed path's K/V). Waits for
  * the last recorded launch, returns the summed milliseconds and the launch

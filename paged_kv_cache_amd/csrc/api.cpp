@@ -82,7 +82,16 @@ struct KernelTimer {
   }
 };
 
-enum { T_ATTN = 0, T_COMBINE = 1, T_APPEND = 2, T_WIDE = 3, T_SPAN = 4, T_GATHER = 5, T_KINDS = 6 };
+enum {
+  T_ATTN = 0,
+  T_COMBINE = 1,
+  T_APPEND = 2,
+  T_WIDE = 3,
+  T_SPAN = 4,
+  T_GATHER = 5,
+  T_TREE = 6,
+  T_KINDS = 7
+};
 
 struct pkv_pool {
   explicit pkv_pool(const pkv_pool_desc& d) : pool(d) {}
@@ -117,6 +126,7 @@ struct pkv_pool {
   int prefetch = 0;    // narrow matrix-core kernel loads one step ahead
   int concurrent = 0;  // narrow and wide launches on two streams
   int inline_plan = 1;  // small schedules travel in the launch arguments (no upload)
+  int tree_stages = 4;  // LDS ring depth of the tree kernel (3 or 4)
 
   // A second stream (default priority) for the wide launch, so that it runs
   // beside the narrow one; created on first use, on the device current then.
@@ -373,6 +383,8 @@ SchedOptions planner_options(const pkv_pool* p, bool mfma) {
     o.max_row_blocks_per_wave = 1;
     o.short_items = false;
   } else {
+    o.tree_ok = p->pool.desc().kv_dtype == PKV_BF16 &&
+                tree_supported(p->pool.desc().head_dim, p->pool.desc().block_size);
     if (attn_max_row_blocks_per_wave(p->pool.desc().head_dim) < 2 || p->prefetch)
       o.max_row_blocks_per_wave = 1;
     // a wide item holds at most what one workgroup of the wide kernel serves
@@ -480,6 +492,8 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.off_order = (int32_t)S.off_order;
   a.off_comb_ptr = (int32_t)S.off_comb_ptr;
   a.off_comb_rows = (int32_t)S.off_comb_rows;
+  a.off_titems = (int32_t)S.off_titems;
+  a.off_tchunks = (int32_t)S.off_tchunks;
   a.n_order = S.n_order_narrow;
   a.n_long = (S.n_narrow - S.n_short) * S.n_layers * d.num_kv_heads;
   a.n_codes = S.n_narrow * S.n_layers * d.num_kv_heads;
@@ -514,6 +528,16 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
     bool t;
     ~Restore() { p->timing = t; }
   } restore{p, timing};
+  if (S.tree) {
+    // one launch: every chunk read once by each plane's workgroup, final rows
+    const int n_wg = (int)S.titems.size() * S.n_layers * d.num_kv_heads;
+    return p->timed(
+        T_TREE,
+        [&](const LaunchEvents& ev) {
+          return launch_attn_tree(d.head_dim, d.block_size, p->tree_stages, a, n_wg, stream, ev);
+        },
+        "tree attention launch");
+  }
   // the narrow launch writes the outputs itself when the plan allows it and
   // the wide launch precedes it on the same stream
   a.finalize = (S.finalize && mfma && !fork && a.n_order > 0) ? 1 : 0;
@@ -1142,6 +1166,15 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "wide_rows") {
     if (value < 16 || value > 256) return fail(PKV_E_INVALID, "wide_rows must be 16..256");
     pool->opt.wide_rows = (int32_t)value;
+  } else if (k == "tree") {
+    if (value < 0 || value > 2) return fail(PKV_E_INVALID, "tree must be 0, 1 or 2");
+    pool->opt.tree = (int32_t)value;
+  } else if (k == "tree_stages") {
+    if (value != 3 && value != 4) return fail(PKV_E_INVALID, "tree_stages must be 3 or 4");
+    pool->tree_stages = (int)value;
+  } else if (k == "tree_piece_tokens") {
+    if (value < 32 || value > 8192) return fail(PKV_E_INVALID, "tree_piece_tokens must be 32..8192");
+    pool->opt.tree_piece_tokens = (int32_t)value;
   } else if (k == "timing") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "timing must be 0 or 1");
     pool->timing = value != 0;
@@ -1173,6 +1206,7 @@ int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_
              : k == "combine" ? T_COMBINE
              : k == "append" ? T_APPEND
              : k == "commit_gather" ? T_GATHER
+             : k == "attention_tree" ? T_TREE
                                : -1;
   if (kind < 0) return fail(PKV_E_INVALID, "unknown kernel " + k);
   return pool->timers[kind].read(total_ms, launches);

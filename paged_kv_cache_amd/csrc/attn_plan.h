@@ -47,6 +47,36 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 48, "WorkItem layout");
 
+// Tree items (decode of a batch whose rows all fit one workgroup): one
+// workgroup per (tree item, layer, KV head) holds up to kTreeRows query rows
+// (row r = holder r / G, q-head offset r % G) and reads every chunk any of
+// them holds, each once, applying it to the rows that hold it; it writes
+// the final output rows (no partial states, no combine).
+constexpr int32_t kTreeRows = 256;
+constexpr int32_t kMaxTreeBlocks = 2048;  // block ids of an item, staged in LDS
+constexpr int32_t kMaxTreeChunks = 256;   // chunk records of an item, staged in LDS
+
+struct TreeItem {
+  int32_t hold_off;   // index in holders[] of the item's first holder
+  int32_t n_rows;     // query rows (1 .. kTreeRows)
+  int32_t chunk_off;  // index of the item's first TreeChunk
+  int32_t n_chunks;
+  int32_t blk_off;    // index in blk[] of the item's first block id
+  int32_t n_blk;      // block ids of all its chunks (<= kMaxTreeBlocks)
+  int32_t n_steps;    // 32-token steps over all its chunks
+  int32_t pad;
+};
+static_assert(sizeof(TreeItem) == 32, "TreeItem layout");
+
+struct TreeChunk {
+  int32_t blk_off;    // first block id, relative to the item's blk_off; padded to whole steps
+  int32_t n_tok;      // valid tokens (> 0)
+  int32_t t0;         // logical position of the first token
+  int32_t n_steps;    // ceil(n_tok / 32)
+  uint64_t rows[4];   // bit r % 64 of rows[r / 64]: item row r reads this chunk
+};
+static_assert(sizeof(TreeChunk) == 48, "TreeChunk layout");
+
 // Device-side pointers to a decode / verify schedule and its partials.
 // Partial states are stored per plane (layer, KV head): P rows each.
 struct AttnCore {
@@ -65,9 +95,11 @@ struct AttnCore {
   //   anc      uint64 [n_branch] ancestor-or-self bits (verify only)
   //   order    wide launch: per workgroup item * (n_layers * Hkv) + layer * Hkv + head, or -1
   //   comb_ptr [n_branch + 1], comb_rows: each branch's partial rows (q-head offset 0) in logical order
+  //   titems   TreeItem[], tchunks TreeChunk[] (tree launch only)
   const uint8_t* meta_dev;
   int32_t meta_inline;
   int32_t off_items, off_blk, off_holders, off_anc, off_order, off_comb_ptr, off_comb_rows;
+  int32_t off_titems, off_tchunks;
   int32_t n_order;          // workgroups in the launch
   // Narrow launch (no order table): code = item * (n_layers * Hkv) + layer *
   // Hkv + head. Workgroups [0, n_long) take code = blockIdx; after them each

@@ -107,6 +107,14 @@ hipError_t launch_attn_wide(int D, int BS, int waves, int row_blocks, const Attn
 // block each. The kernel adds its loader waves.
 void attn_wide_shape(int D, int* waves, int* row_blocks);
 
+// The tree kernel (tree.hip): one workgroup per (tree item, layer, KV head)
+// reads each chunk of the item once for all rows that hold it and writes
+// the final output rows. stages: LDS ring depth (3 or 4). Built for bf16,
+// head_dim 64 / 128 and block_size 16 / 32 / 64.
+bool tree_supported(int D, int BS);
+hipError_t launch_attn_tree(int D, int BS, int stages, const AttnParams& p, int n_wg,
+                            hipStream_t stream, const LaunchEvents& ev);
+
 // ------------------------------------------------------ static scratch
 // Device memory for callers that cannot allocate (pkv_decode_attn_noalloc):
 // a file-scope __device__ array of kScratchBytes in kernels.hip, one copy

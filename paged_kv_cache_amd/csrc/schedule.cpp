@@ -192,6 +192,93 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   return chunks;
 }
 
+// The tree plan: one item holding all n * G rows (row r = branch r / G,
+// q-head offset r % G), every segment one or more chunks read once with the
+// mask of the rows whose branch holds it. Segments of at least 64 rows (the
+// shared root of a wide tree: matrix-core work) are cut into pieces of
+// piece tokens and spread evenly, by tokens, among the other segments (the
+// edges: memory traffic), so that a workgroup alternates between the two.
+// Returns false (S untouched) if the batch does not fit the tree kernel.
+bool plan_tree(const std::vector<Segment>& segs, int32_t n, int32_t bs, int32_t G,
+               int32_t piece, Schedule* S) {
+  const int32_t rows = n * G;
+  if (rows > kTreeRows || rows <= 0) return false;
+  struct Piece {
+    int32_t seg, b0, b1, t0, n_tok;
+  };
+  std::vector<Piece> heavy, light;
+  const int32_t unit = std::max<int32_t>(32, bs);           // whole steps and whole blocks
+  const int32_t pblocks = std::max<int32_t>(1, round_up(std::max(piece, unit), unit) / bs);
+  int64_t h_tok = 0, l_tok = 0;
+  for (size_t k = 0; k < segs.size(); ++k) {
+    const Segment& sg = segs[k];
+    const int32_t nb = (int32_t)sg.blocks.size();
+    const bool big = sg.n_hold * G >= 64;
+    const int32_t step = big ? pblocks : nb;
+    for (int32_t b0 = 0; b0 < nb; b0 += step) {
+      const int32_t b1 = std::min(nb, b0 + step);
+      Piece pc{(int32_t)k, b0, b1, sg.t0 + b0 * bs, std::min(sg.n_tok - b0 * bs, (b1 - b0) * bs)};
+      (big ? heavy : light).push_back(pc);
+      (big ? h_tok : l_tok) += pc.n_tok;
+    }
+  }
+  if ((int64_t)heavy.size() + (int64_t)light.size() > kMaxTreeChunks) return false;
+  // interleave by tokens: take the list that is behind its share
+  std::vector<Piece> order;
+  size_t hi = 0, li = 0;
+  int64_t hd = 0, ld = 0;
+  while (hi < heavy.size() || li < light.size()) {
+    const bool take_h = li >= light.size() ||
+                        (hi < heavy.size() && (double)hd * (double)std::max<int64_t>(l_tok, 1) <=
+                                                  (double)ld * (double)std::max<int64_t>(h_tok, 1));
+    if (take_h) {
+      hd += heavy[hi].n_tok;
+      order.push_back(heavy[hi++]);
+    } else {
+      ld += light[li].n_tok;
+      order.push_back(light[li++]);
+    }
+  }
+  std::vector<int32_t> blk;
+  std::vector<TreeChunk> chunks;
+  int32_t steps = 0;
+  for (const Piece& pc : order) {
+    const Segment& sg = segs[pc.seg];
+    TreeChunk c{};
+    c.blk_off = (int32_t)blk.size();
+    c.n_tok = pc.n_tok;
+    c.t0 = pc.t0;
+    c.n_steps = (pc.n_tok + 31) / 32;
+    for (int32_t b = pc.b0; b < pc.b1; ++b) blk.push_back(sg.blocks[b]);
+    const int32_t need = (32 * c.n_steps + bs - 1) / bs;  // blocks the steps touch
+    while ((int32_t)blk.size() - c.blk_off < need) blk.push_back(sg.blocks[pc.b1 - 1]);
+    for (int32_t h = 0; h < sg.n_hold; ++h) {
+      const int32_t br = S->holders[sg.hold_off + h];
+      for (int32_t g = 0; g < G; ++g) {
+        const int32_t r = br * G + g;
+        c.rows[r >> 6] |= 1ull << (r & 63);
+      }
+    }
+    steps += c.n_steps;
+    chunks.push_back(c);
+  }
+  if ((int64_t)blk.size() > kMaxTreeBlocks) return false;
+  TreeItem it{};
+  it.hold_off = (int32_t)S->holders.size();
+  it.n_rows = rows;
+  it.chunk_off = 0;
+  it.n_chunks = (int32_t)chunks.size();
+  it.blk_off = 0;
+  it.n_blk = (int32_t)blk.size();
+  it.n_steps = steps;
+  for (int32_t i = 0; i < n; ++i) S->holders.push_back(i);
+  S->blk = std::move(blk);
+  S->tchunks = std::move(chunks);
+  S->titems.assign(1, it);
+  S->tree = true;
+  return true;
+}
+
 }  // namespace
 
 void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
@@ -254,6 +341,10 @@ void Schedule::layout(int Hkv, int D) {
   o = align16(o + anc.size() * sizeof(uint64_t));
   off_order = o;
   o = align16(o + order.size() * sizeof(int32_t));
+  off_titems = o;
+  o = align16(o + titems.size() * sizeof(TreeItem));
+  off_tchunks = o;
+  o = align16(o + tchunks.size() * sizeof(TreeChunk));
   meta_bytes = o;
   const size_t planes = (size_t)n_layers * Hkv;
   off_ml = align256(o);
@@ -272,6 +363,9 @@ void Schedule::pack_meta(uint8_t* dst) const {
   std::memcpy(dst + off_comb_rows, comb_rows.data(), comb_rows.size() * sizeof(int32_t));
   if (!anc.empty()) std::memcpy(dst + off_anc, anc.data(), anc.size() * sizeof(uint64_t));
   if (!order.empty()) std::memcpy(dst + off_order, order.data(), order.size() * sizeof(int32_t));
+  if (!titems.empty()) std::memcpy(dst + off_titems, titems.data(), titems.size() * sizeof(TreeItem));
+  if (!tchunks.empty())
+    std::memcpy(dst + off_tchunks, tchunks.data(), tchunks.size() * sizeof(TreeChunk));
 }
 
 void PlannerScratch::ensure(int nb) {
@@ -393,6 +487,25 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   }
   S->n_segments = (int32_t)segs.size();
   for (const Segment& sg : segs) S->unique_tokens += sg.n_tok;
+  // The tree launch: when all rows fit one workgroup, one workgroup per
+  // plane reads every segment once (no partial states, no combine); chosen
+  // automatically when some segment is wide and the planes alone fill the
+  // chip (else the narrow / wide items' split of long segments is needed for
+  // parallelism).
+  if (opt.tree > 0 && opt.tree_ok) {
+    bool wide_seg = false;
+    for (const Segment& sg : segs) wide_seg = wide_seg || sg.n_hold * G > opt.rows_per_item;
+    const int64_t planes = (int64_t)n_layers * d.num_kv_heads;
+    const bool pays = opt.tree == 2 || (wide_seg && 4 * planes >= 3 * (int64_t)opt.target_workgroups);
+    if (pays && plan_tree(segs, n, bs, G, opt.tree_piece_tokens, S)) {
+      for (const Segment& sg : segs)
+        if (sg.n_hold * G > opt.rows_per_item) S->wide_tokens += sg.n_tok;
+      S->n_chunks = (int32_t)S->tchunks.size();
+      S->n_branch = n;
+      S->layout(d.num_kv_heads, d.head_dim);
+      return PKV_OK;
+    }
+  }
   // Short shared segments are folded into per-branch segments: a shared
   // segment writes one partial state per row it serves, and when it holds
   // few tokens (an MCTS edge: 32 tokens for up to 128 rows per KV head)

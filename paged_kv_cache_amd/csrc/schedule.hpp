@@ -34,6 +34,14 @@ struct SchedOptions {
   int32_t short_tokens = kShortTokens;  // longest narrow item (of <= 16 rows) that counts as short
   int32_t fold_tokens = 64;        // shared segments shorter than this are read per branch (0: never)
   bool finalize = true;            // the narrow launch may write final outputs (see Schedule::finalize)
+  // Tree launch (one workgroup per plane holding every row and reading each
+  // chunk once): 0 never, 1 when it applies and pays (all rows fit one
+  // workgroup, some segment has more rows than a narrow item, and the planes
+  // alone fill the chip), 2 whenever it applies (for tests). tree_ok: the
+  // head size and dtype have a tree kernel.
+  int32_t tree = 1;
+  bool tree_ok = false;
+  int32_t tree_piece_tokens = 512;  // the widest segments are cut into pieces of this many tokens
 };
 
 struct Schedule {
@@ -45,6 +53,11 @@ struct Schedule {
   // chunks by wide items: the wide launch runs first, so each narrow row can
   // merge its branch's wide partials itself and write the output (no combine).
   bool finalize = false;
+  // The tree launch serves the whole batch (titems / tchunks); no narrow or
+  // wide items, no partial states, no combine.
+  bool tree = false;
+  std::vector<TreeItem> titems;
+  std::vector<TreeChunk> tchunks;
   int32_t narrow_rw = 1;           // 16-row blocks per wave in the narrow launch
   std::vector<int32_t> order;      // workgroup order of the wide launch
   int32_t n_order_narrow = 0;      // workgroups of the narrow launch (no table)
@@ -64,7 +77,8 @@ struct Schedule {
 
   // byte offsets inside the workspace
   size_t off_items = 0, off_blk = 0, off_holders = 0, off_comb_ptr = 0, off_comb_rows = 0,
-         off_anc = 0, off_order = 0, meta_bytes = 0, off_ml = 0, off_acc = 0, total_bytes = 0;
+         off_anc = 0, off_order = 0, off_titems = 0, off_tchunks = 0, meta_bytes = 0, off_ml = 0,
+         off_acc = 0, total_bytes = 0;
 
   void layout(int Hkv, int D);
   // Fills `order` for n_layers x Hkv planes (items must be final).

@@ -556,6 +556,7 @@ def test_plan_folds_short_edges_per_leaf(pkv):
     w = get("mcts")
     c, seqs = build_host_tree(pkv, w)
     G = w.shape.Hq // w.shape.Hkv
+    c.set_option("tree", 0)          # (the narrow / wide items' plan)
     c.set_option("fold_tokens", 0)
     plain = c.plan_info(seqs)
     c.set_option("fold_tokens", 64)
@@ -568,6 +569,36 @@ def test_plan_folds_short_edges_per_leaf(pkv):
     assert folded["partial_rows"] == root_chunks * 64 * G + 64 * G
     c.set_option("fold_tokens", 16)                    # shorter than the edges: no folding
     assert c.plan_info(seqs) == plain
+
+
+def test_plan_tree_for_mcts(pkv):
+    """The MCTS batch (64 leaves x G = 4 = 256 rows, 256 planes) takes the
+    tree plan by default: one item, the root cut into 8 pieces of 512 tokens
+    and the 126 edges whole (134 chunks), each token slot read once (unique
+    tokens as for the other plan), no partial states; off with tree 0, and
+    not taken when the planes do not fill the chip (a one-layer call) unless
+    forced (tree 2) or when the rows do not fit one workgroup."""
+    w = get("mcts")
+    c, seqs = build_host_tree(pkv, w)
+    tree = c.plan_info(seqs)
+    assert tree["n_chunks"] == 4096 // 512 + 126
+    assert tree["n_items"] == 0 and tree["partial_rows"] == 0
+    assert tree["unique_tokens"] == distinct_tokens(c, seqs) == 4096 + 126 * 32
+    assert tree["workspace_bytes"] == (tree["plan_bytes"] + 255) // 256 * 256   # the plan alone
+    c.set_option("tree_piece_tokens", 1024)
+    assert c.plan_info(seqs)["n_chunks"] == 4 + 126
+    c.set_option("tree_piece_tokens", 512)
+    c.set_option("tree", 0)
+    items = c.plan_info(seqs)
+    assert items["partial_rows"] > 0 and items["unique_tokens"] == tree["unique_tokens"]
+    c.set_option("tree", 1)
+    one_layer = c.plan_info(seqs, n_layers=1)         # 8 planes: the root is split for parallelism
+    assert one_layer["partial_rows"] > 0
+    c.set_option("tree", 2)
+    assert c.plan_info(seqs, n_layers=1)["partial_rows"] == 0
+    # 65 branches x G = 4 = 260 rows: more than one workgroup holds
+    more = c.fork_many(seqs[:1])
+    assert c.plan_info(seqs + more)["partial_rows"] > 0
 
 
 def build_host_tree(pkv, w):
