@@ -427,14 +427,15 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int i = 0; i < 4; ++i) s8[r][4 * tau + i] = sc[r][tau][i];
+      if (NEG) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s8[r][e] = -s8[r][e];
+      }
+      // (after the negation: a masked score stays -inf)
       if (!full) {
         const int valid = ((m64 >> (16 * r + n)) & 1ull) ? ntok - (tb + voff) : 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s8[r][e] = e < valid ? s8[r][e] : kNegInf;
-      }
-      if (NEG) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s8[r][e] = -s8[r][e];
       }
       float m = fmaxf(fmaxf(s8[r][0], s8[r][1]), fmaxf(s8[r][2], s8[r][3]));
       m = fmaxf(m, fmaxf(fmaxf(s8[r][4], s8[r][5]), fmaxf(s8[r][6], s8[r][7])));
