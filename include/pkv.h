@@ -160,14 +160,18 @@ int pkv_seq_free_many(pkv_pool* pool, const pkv_seq* seqs, int32_t n);
 int pkv_seq_append_plan(pkv_pool* pool, pkv_seq seq, int32_t n, int64_t* slots_out,
                         pkv_cow_op* cow_out, int32_t* n_cow);
 
-/* Device: perform copy-on-write copies (host array of n ops) for every
- * layer and KV head, K and V, on the stream. Slots at and above n_valid of
+/* Device: perform copy-on-write copies [D1, D2] (host array of n ops) for
+ * every layer and KV head, K and V, on the stream: the shared, partly
+ * filled block is duplicated so that the appending branch writes a block
+ * no other table points to. Slots at and above n_valid of
  * each destination block hold unspecified values afterwards. block_size
  * must be 16, 32 or 64 for every device call (else PKV_E_UNSUPPORTED). */
 int pkv_cow_copy(pkv_pool* pool, const pkv_cow_op* ops, int32_t n, void* stream);
 
-/* Device: scatter n tokens of new K/V into their slots. slots: host array of
- * n slot ids (block * block_size + offset, each in range). k_new, v_new:
+/* Device: scatter n tokens of new K/V into their slots [D1, D2] (slots from
+ * an append plan: every one lies in a block whose count is one, so no other
+ * table sees the write). slots: host array of n slot ids
+ * (block * block_size + offset, each in range). k_new, v_new:
  * device, [num_layers][n][num_kv_heads][head_dim] in kv_dtype. */
 int pkv_write_kv(pkv_pool* pool, const int64_t* slots, int32_t n, const void* k_new,
                  const void* v_new, void* stream);
@@ -287,7 +291,7 @@ int pkv_tree_verify_attn(pkv_pool* pool, const pkv_seq* reqs, int32_t n_req,
 /* Keeps the first new_len tokens of seq (0 <= new_len <= its length):
  * blocks that then hold none of its tokens lose its reference (and are
  * freed at zero); a kept, partly filled last block keeps its count, so a
- * later append copies it if it is shared ([D-rust]). Host only. */
+ * later append copies it if it is shared [D2]. Host only. */
 int pkv_seq_truncate(pkv_pool* pool, pkv_seq seq, int32_t new_len);
 
 /* Workspace bytes pkv_tree_commit(_batch) needs to keep n_accepted tokens
@@ -424,15 +428,16 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       most 16 * waves * row blocks rows
  *   "target_workgroups" 256: chunks are shortened (down to 1024 tokens) while the
  *                       grid has fewer than 3/4 of this many workgroups
- *   "tree"              1: a decode whose rows all fit one workgroup (branches x
- *                       query-head group <= 256) at head_dim 64 or 128 (bf16) runs
- *                       as one launch with one workgroup per (layer, KV head) that
- *                       reads every chunk of the batch once for all rows holding
- *                       it and writes the outputs (no partial states, no combine),
- *                       when some segment has more rows than a narrow item and the
- *                       (layer, KV head) planes alone fill the chip (at least 3/4
- *                       of "target_workgroups"); 2: whenever the rows fit; 0: never
- *   "tree_stages"       4: LDS ring depth of the tree launch (3 or 4)
+ *   "tree"              0: never; 1: a decode whose rows all fit one workgroup
+ *                       (branches x query-head group <= 256) at head_dim 64 or
+ *                       128 (bf16) runs as one launch with one workgroup per
+ *                       (layer, KV head) that reads every chunk of the batch
+ *                       once for all rows holding it and writes the outputs (no
+ *                       partial states, no combine), when some segment has more
+ *                       rows than a narrow item and the (layer, KV head) planes
+ *                       alone fill the chip (at least 3/4 of
+ *                       "target_workgroups"); 2: whenever the rows fit
+ *   "tree_stages"       5: LDS ring depth of the tree launch (4, 5 or 6)
  *   "tree_piece_tokens" 512: segments of 64 or more rows are cut into pieces of
  *                       this many tokens, spread among the narrower segments
  *                       (32..8192)

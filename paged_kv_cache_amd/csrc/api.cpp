@@ -126,7 +126,7 @@ struct pkv_pool {
   int prefetch = 0;    // narrow matrix-core kernel loads one step ahead
   int concurrent = 0;  // narrow and wide launches on two streams
   int inline_plan = 1;  // small schedules travel in the launch arguments (no upload)
-  int tree_stages = 4;  // LDS ring depth of the tree kernel (3 or 4)
+  int tree_stages = 5;  // LDS ring depth of the tree kernel (4 to 6)
 
   // A second stream (default priority) for the wide launch, so that it runs
   // beside the narrow one; created on first use, on the device current then.
@@ -1170,7 +1170,7 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
     if (value < 0 || value > 2) return fail(PKV_E_INVALID, "tree must be 0, 1 or 2");
     pool->opt.tree = (int32_t)value;
   } else if (k == "tree_stages") {
-    if (value != 3 && value != 4) return fail(PKV_E_INVALID, "tree_stages must be 3 or 4");
+    if (value < 4 || value > 6) return fail(PKV_E_INVALID, "tree_stages must be 4, 5 or 6");
     pool->tree_stages = (int)value;
   } else if (k == "tree_piece_tokens") {
     if (value < 32 || value > 8192) return fail(PKV_E_INVALID, "tree_piece_tokens must be 32..8192");

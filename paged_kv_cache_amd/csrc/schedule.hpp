@@ -37,9 +37,11 @@ struct SchedOptions {
   // Tree launch (one workgroup per plane holding every row and reading each
   // chunk once): 0 never, 1 when it applies and pays (all rows fit one
   // workgroup, some segment has more rows than a narrow item, and the planes
-  // alone fill the chip), 2 whenever it applies (for tests). tree_ok: the
-  // head size and dtype have a tree kernel.
-  int32_t tree = 1;
+  // alone fill the chip), 2 whenever it applies (for tests). Off by
+  // default: on the MCTS batch the tree launch measures slower than the
+  // wide and narrow launches together. tree_ok: the head size and dtype
+  // have a tree kernel.
+  int32_t tree = 0;
   bool tree_ok = false;
   int32_t tree_piece_tokens = 512;  // the widest segments are cut into pieces of this many tokens
 };

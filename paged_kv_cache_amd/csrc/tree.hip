@@ -7,20 +7,22 @@
 // workgroup per plane the two overlap across the chip, no partial state is
 // written and no second launch re-reads the edges per leaf.
 //
-// Shape: 4 waves, one per SIMD, each owning 64 rows (four 16-row blocks), so
-// every K/V operand read from LDS feeds four matrix products. Each wave also
-// moves its quarter of every 32-token step of K/V from global memory into
+// Shape: 8 waves, two per SIMD, each owning 32 rows (two 16-row blocks), so
+// every K/V operand read from LDS feeds two matrix products. Each wave also
+// moves its eighth of every 32-token step of K/V from global memory into
 // LDS (global_load_lds_dwordx4, operand order, as the wide kernel's loaders
 // do), keeping NS - 1 steps in flight in a ring of NS separate LDS arrays.
-// One wave per SIMD leaves each wave up to 512 registers (VGPRs and AGPRs),
-// room for the four blocks' accumulators next to the softmax and operands.
+// Two waves per SIMD leave each up to 256 registers (VGPRs and AGPRs), and
+// let the SIMD issue one wave's softmax while the other's matrix products
+// run: with one wave per SIMD, every vector instruction that waits on a
+// product's result, and every product that waits on the busy matrix unit,
+// stalls the SIMD.
 //
-// Per step and wave (all four blocks active): Q.K^T for the four blocks from
-// one read of the K sections, the four row maxima and one wave vote for the
-// (rare) rescale, then per block the probabilities (bf16 hi + lo, as in the
-// other kernels) and its P.V products from one read of the V sections; the
-// blocks' softmax and products are independent, so the scheduler overlaps
-// one block's vector work with another block's matrix products.
+// Per step and wave (both blocks active): Q.K^T for the two blocks from one
+// read of the K sections, the row maxima, then per block the probabilities
+// (bf16 hi + lo, as in the other kernels) and its P.V products from one
+// read of the V sections, the second block's probabilities placed between
+// the first block's products.
 //
 // Chunks whose row mask leaves some rows out (the edges) skip the row blocks
 // with no row in the mask and give masked rows -inf scores. Odd planes walk
@@ -85,56 +87,136 @@ __device__ __forceinline__ void pv_step(f32x4& acc, const u32x4& v, bf16x8 phi, 
       : "v"(v), "v"(phi), "v"(plo));
 }
 
-// Q.K^T for one 16-row block: the two 16-token score tiles of a 32-token
-// step, S^T[tau] = sum_ks K[tau][ks] Q^T[ks], with the block's queries held
-// in AGPRs (matrix products read their B operand from there), which keeps
-// 64 VGPRs free for the rest. on == 0 skips the block (its scores are left
-// unspecified; every score of such a block is masked afterwards) and waits
-// out the products of the block before, whose scores are read next. The
-// scores are read by vector instructions only after another block's
-// statement or after settle_v(), which waits out the writes.
+// Q.K^T for a wave's two 16-row blocks: per block the two 16-token score
+// tiles of a 32-token step, s[r][tau] = K[tau] Q_r^T (rows of the tile are
+// tokens, columns the block's rows), with the queries held in AGPRs (matrix
+// products read their B operand from there). The four chains (block, tile)
+// are interleaved so that no product waits on the one just before it.
+// on0 / on1 (wave-uniform) skip a block with no row in the step's mask; its
+// scores are left unspecified (every one of them is masked afterwards).
+// The statement always runs (a C++ branch around it would let the compiler
+// copy fresh results at the join, with no wait for the products); the
+// scores are read by vector instructions only a whole step later.
 template <int KS>
-__device__ __forceinline__ void qk_block(f32x4& s0, f32x4& s1, const u32x4 (&k)[2 * KS],
-                                         const bf16x8 (&q)[KS], uint32_t on);
+__device__ __forceinline__ void qk_pair(f32x4 (&s)[2][2], const u32x4 (&k)[2 * KS],
+                                        const bf16x8 (&q0)[KS], const bf16x8 (&q1)[KS],
+                                        uint32_t on0, uint32_t on1);
 template <>
-__device__ __forceinline__ void qk_block<4>(f32x4& s0, f32x4& s1, const u32x4 (&k)[8],
-                                            const bf16x8 (&q)[4], uint32_t on) {
-  asm("s_cmp_eq_u32 %14, 0\n\t"
-      "s_cbranch_scc0 2f\n\t"
-      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-      "s_branch 1f\n"
-      "2:\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %2, %10, 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %6, %10, 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %3, %11, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %7, %11, %1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %12, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %8, %12, %1\n\t"
+__device__ __forceinline__ void qk_pair<4>(f32x4 (&s)[2][2], const u32x4 (&k)[8],
+                                           const bf16x8 (&q0)[4], const bf16x8 (&q1)[4],
+                                           uint32_t on0, uint32_t on1) {
+  asm("s_cmp_eq_u32 %20, 0\n\t"
+      "s_cbranch_scc1 3f\n\t"
+      "s_cmp_eq_u32 %21, 0\n\t"
+      "s_cbranch_scc1 2f\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %12, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %8, %12, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %8, %16, 0\n\t"
       "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1\n"
-      "1:"
-      : "=&v"(s0), "=&v"(s1)
+      "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %17, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %9, %17, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %14, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %10, %14, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %6, %18, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %10, %18, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %7, %15, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %11, %15, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %7, %19, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %11, %19, %3\n\t"
+      "s_branch 4f\n"
+      "2:\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %12, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %8, %12, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %13, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %9, %13, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %6, %14, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %10, %14, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %7, %15, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %11, %15, %1\n\t"
+      "s_branch 4f\n"
+      "3:\n\t"
+      "s_cmp_eq_u32 %21, 0\n\t"
+      "s_cbranch_scc1 4f\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %8, %16, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %17, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %9, %17, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %6, %18, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %10, %18, %3\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %7, %19, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %11, %19, %3\n"
+      "4:"
+      : "=&v"(s[0][0]), "=&v"(s[0][1]), "=&v"(s[1][0]), "=&v"(s[1][1])
       : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "v"(k[4]), "v"(k[5]), "v"(k[6]), "v"(k[7]),
-        "a"(q[0]), "a"(q[1]), "a"(q[2]), "a"(q[3]), "s"(__builtin_amdgcn_readfirstlane(on))
+        "a"(q0[0]), "a"(q0[1]), "a"(q0[2]), "a"(q0[3]), "a"(q1[0]), "a"(q1[1]), "a"(q1[2]),
+        "a"(q1[3]), "s"(__builtin_amdgcn_readfirstlane(on0)),
+        "s"(__builtin_amdgcn_readfirstlane(on1))
       : "scc");
 }
 template <>
-__device__ __forceinline__ void qk_block<2>(f32x4& s0, f32x4& s1, const u32x4 (&k)[4],
-                                            const bf16x8 (&q)[2], uint32_t on) {
-  asm("s_cmp_eq_u32 %8, 0\n\t"
-      "s_cbranch_scc0 2f\n\t"
-      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-      "s_branch 1f\n"
+__device__ __forceinline__ void qk_pair<2>(f32x4 (&s)[2][2], const u32x4 (&k)[4],
+                                           const bf16x8 (&q0)[2], const bf16x8 (&q1)[2],
+                                           uint32_t on0, uint32_t on1) {
+  asm("s_cmp_eq_u32 %12, 0\n\t"
+      "s_cbranch_scc1 3f\n\t"
+      "s_cmp_eq_u32 %13, 0\n\t"
+      "s_cbranch_scc1 2f\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %8, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %8, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %10, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %6, %10, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %9, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %7, %9, %1\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %11, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %7, %11, %3\n\t"
+      "s_branch 4f\n"
       "2:\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %2, %6, 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %6, 0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %3, %7, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %5, %7, %1\n"
-      "1:"
-      : "=&v"(s0), "=&v"(s1)
-      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "a"(q[0]), "a"(q[1]), "s"(__builtin_amdgcn_readfirstlane(on))
+      "v_mfma_f32_16x16x32_bf16 %0, %4, %8, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %6, %8, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %0, %5, %9, %0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %1, %7, %9, %1\n\t"
+      "s_branch 4f\n"
+      "3:\n\t"
+      "s_cmp_eq_u32 %13, 0\n\t"
+      "s_cbranch_scc1 4f\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %4, %10, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %6, %10, 0\n\t"
+      "v_mfma_f32_16x16x32_bf16 %2, %5, %11, %2\n\t"
+      "v_mfma_f32_16x16x32_bf16 %3, %7, %11, %3\n"
+      "4:"
+      : "=&v"(s[0][0]), "=&v"(s[0][1]), "=&v"(s[1][0]), "=&v"(s[1][1])
+      : "v"(k[0]), "v"(k[1]), "v"(k[2]), "v"(k[3]), "a"(q0[0]), "a"(q0[1]), "a"(q1[0]),
+        "a"(q1[1]), "s"(__builtin_amdgcn_readfirstlane(on0)),
+        "s"(__builtin_amdgcn_readfirstlane(on1))
       : "scc");
 }
+
+// Maxima as written (v_max_f32, v_max3_f32): the scores come out of asm
+// statements, and fmaxf on values the compiler cannot prove canonical
+// quiets each input first (two more instructions per maximum).
+__device__ __forceinline__ float rmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float rmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// the maximum over the four lanes of a row (l, l ^ 16, l ^ 32, l ^ 48)
+__device__ __forceinline__ float rmax_rows(float x) {
+  float a = x, b = x;
+  swap16(a, b);
+  x = rmax(a, b);
+  a = x;
+  b = x;
+  swap32(a, b);
+  return rmax(a, b);
+}
+
 // A block's queries (KS 16-byte pieces per lane, 64 bytes apart) loaded
 // straight into AGPRs, the load waited for in the same statement: defined
 // in AGPRs, they stay there (loaded into VGPRs, the compiler would copy them
@@ -167,13 +249,13 @@ __device__ __forceinline__ void load_q<2>(bf16x8 (&q)[2], const void* src) {
 // An accumulator set to zero by a matrix product (0 x 0 + 0), so that it
 // is defined in AGPRs: zeroed by ordinary code it would be defined in VGPRs,
 // and the compiler would carry it there, copying it into AGPRs and back
-// around every product.
+// around every product. Volatile: the statements of all accumulators have
+// the same input, and merged into one, the compiler would copy its result
+// into the others with no wait for the product (it does not know the
+// statement holds one). The caller settles the accumulators before any
+// other code reads them.
 __device__ __forceinline__ void zero_acc(f32x4& acc, const u32x4& z) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
-}
-
-__device__ __forceinline__ void settle_v(f32x4& s0, f32x4& s1) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
 }
 
 // pv_step for a block that may have no row in the chunk's mask (on == 0:
@@ -192,23 +274,6 @@ __device__ __forceinline__ void pv_step_if(f32x4& acc, const u32x4& v, bf16x8 ph
       : "+a"(acc)
       : "v"(v), "v"(phi), "v"(plo), "s"(__builtin_amdgcn_readfirstlane(on))
       : "scc");
-}
-
-// acc *= alpha (per lane) in place, in the accumulator's own AGPRs; the
-// products still writing it are waited out first (an XDL result is read by
-// other instructions some 19 wait states after issue at the longest).
-__device__ __forceinline__ void scale_acc(f32x4& acc, float alpha) {
-  float e0 = acc[0], e1 = acc[1], e2 = acc[2], e3 = acc[3];
-  float t;
-  asm volatile(
-      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
-      "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
-      "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
-      "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
-      "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4"
-      : "+a"(e0), "+a"(e1), "+a"(e2), "+a"(e3), "=&v"(t)
-      : "v"(alpha));
-  acc = f32x4{e0, e1, e2, e3};
 }
 
 // The probabilities of one row block's eight scores per lane (as probs8:
@@ -276,24 +341,34 @@ __device__ __forceinline__ void settle(f32x4 (&acc)[DB]) {
                  : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
 }
 
-// NEG: the softmax scale is negative; the scores are negated as they are
-// masked (the scale's magnitude is folded into the exponent as elsewhere).
+// NEG: the softmax scale is negative; the scores are negated before they
+// are masked (the scale's magnitude is folded into the exponent as
+// elsewhere).
+//
+// The walk is software-pipelined by one step: step t + 1 is made visible
+// (its loads waited for, then a barrier) before step t is finished, so that
+// each wave issues step t + 1's score products first and computes step t's
+// maxima, probabilities and P.V while they run. Two ring stages are in use
+// at a time (step t's V, step t + 1's K), so NS - 3 steps of loads stay in
+// flight behind them.
 template <int D, int BS, int NS, bool NEG>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
   constexpr int KS = D / 32;           // 32-wide k steps of Q.K
   constexpr int DB = D / 16;           // 16-wide d blocks of P.V
   constexpr int NSEC = 2 * KS + DB;    // 1 KiB operand sections per step
-  constexpr int NW = 4;                // waves (each loads and computes)
-  constexpr int RBW = 4;               // 16-row blocks per wave
+  constexpr int NW = 8;                // waves (each loads and computes)
+  constexpr int RBW = 2;               // 16-row blocks per wave
+  constexpr int RPW = 16 * RBW;        // rows per wave
+  constexpr int NT = 64 * NW;          // threads
   constexpr int SPL = NSEC / NW;       // sections each wave loads per step
+  static_assert(NW * RPW == kTreeRows && 64 % RPW == 0 && RBW == 2, "rows per wave");
   static_assert(NSEC % NW == 0, "sections per wave");
-  static_assert(NS >= 3 && NS <= 6, "ring stages");
+  static_assert(NS >= 4 && NS <= 6, "ring stages");
   static_assert((NS - 1) * SPL < 64, "loads in flight per wave");
   static_assert(BS == 16 || BS == 32 || BS == 64, "block size");
   __shared__ u32x4 ring[NS][NSEC * 64];
-  __shared__ int32_t blk_s[kMaxTreeBlocks];
-  __shared__ TreeChunk ch_s[kMaxTreeChunks];
+  __shared__ int redo_s;
 
   const PlanArrays sp = plan_arrays(p, plan_bytes);
   const int lane = threadIdx.x & 63;
@@ -306,13 +381,13 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
   const int kvh = plane - li * p.Hkv;
   const int layer = p.layer0 + li;
   const TreeItem ti = sp.titems[item_idx];
-  for (int i = threadIdx.x; i < ti.n_blk; i += 256) blk_s[i] = sp.blk[ti.blk_off + i];
-  {
-    const int32_t* src = (const int32_t*)(sp.tchunks + ti.chunk_off);
-    int32_t* dst = (int32_t*)ch_s;
-    for (int i = threadIdx.x; i < ti.n_chunks * 12; i += 256) dst[i] = src[i];
-  }
-  __syncthreads();
+  // The item's block ids and chunk records are read with scalar loads
+  // (constant address space: wave-uniform, read-only): in LDS they would
+  // queue behind the operand traffic, on every wave's critical path.
+  typedef const __attribute__((address_space(4))) int32_t* CBlk;
+  typedef const __attribute__((address_space(4))) TreeChunk* CChunk;
+  const CBlk blk_c = (CBlk)(sp.blk + ti.blk_off);
+  const CChunk ch_c = (CChunk)(sp.tchunks + ti.chunk_off);
   const bool rev = plane & 1;
   const int n_chunks = ti.n_chunks;
   const int total = ti.n_steps;
@@ -321,9 +396,9 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
     c.i = i;
     c.ci = rev ? n_chunks - 1 - i : i;
     c.s = 0;
-    c.ntok = __builtin_amdgcn_readfirstlane(ch_s[c.ci].n_tok);
-    c.nst = __builtin_amdgcn_readfirstlane(ch_s[c.ci].n_steps);
-    c.blk = __builtin_amdgcn_readfirstlane(ch_s[c.ci].blk_off);
+    c.ntok = ch_c[c.ci].n_tok;
+    c.nst = ch_c[c.ci].n_steps;
+    c.blk = ch_c[c.ci].blk_off;
   };
   // next step; at the last step of the walk the cursor stays (loads issued
   // past the end re-read that step, in bounds, into a stage never read)
@@ -343,19 +418,29 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
   const uint16_t* Kp = (const uint16_t*)p.k_arena + ((int64_t)layer * p.num_blocks * p.Hkv + kvh) * BS * D;
   const uint16_t* Vp = (const uint16_t*)p.v_arena + ((int64_t)layer * p.num_blocks * p.Hkv + kvh) * BS * D;
   const uint32_t ring_base = (uint32_t)(uintptr_t)&ring[0][0];
-  // Sections wave + NW * k of the cursor's step into stage st: the first
-  // SPL / 2 of a wave's sections are K (2KS = NSEC / 2 of them in all), the
-  // rest V.
-  auto issue = [&](const Cursor& c, int st) __attribute__((always_inline)) {
+  // The block ids of the cursor's step (tokens tb .. tb + 15 and
+  // tb + 16 .. tb + 31), loaded a step before they are used.
+  struct Ids {
+    int a, b;
+  };
+  auto ids_of = [&](const Cursor& c) __attribute__((always_inline)) {
     const int tb = 32 * c.s;
-    const int bA = blk_s[c.blk + tb / BS];
-    const int bB = blk_s[c.blk + (tb + 16) / BS];
-    const int64_t oA = (int64_t)bA * tile_step, oB = (int64_t)bB * tile_step;
+    Ids r;
+    r.a = blk_c[c.blk + tb / BS];
+    r.b = blk_c[c.blk + (tb + 16) / BS];
+    return r;
+  };
+  // Sections wave + NW * k of the cursor's step into stage st: sections
+  // below 2KS are K, the rest V. The block ids are wave-uniform (scalar
+  // offsets); only the lane's place in the tile is per lane.
+  auto issue = [&](const Cursor& c, const Ids& id, int st) __attribute__((always_inline)) {
+    const int tb = 32 * c.s;
+    const int64_t oA = (int64_t)id.a * tile_step, oB = (int64_t)id.b * tile_step;
 #pragma unroll
     for (int k = 0; k < SPL; ++k) {
       const int sect = wave + NW * k;
       const uint16_t* src;
-      if (k < SPL / 2) {
+      if (sect < 2 * KS) {
         const int tau = sect / KS, ks = sect - (sect / KS) * KS;
         const int off = koff0 + 4 * tau;
         src = Kp + ((BS == 16 && off >= 16) ? oB : oA) + ((tb + off) % BS) * D + 32 * ks + 8 * g;
@@ -379,7 +464,13 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
       keep[w] = lo | hi;
     }
 #pragma unroll
-    for (int k = SPL / 2; k < SPL; ++k) ring[st][(wave + NW * k) * 64 + lane] &= keep;
+    for (int k = 0; k < SPL; ++k) {
+      const int sect = wave + NW * k;
+      if (sect >= 2 * KS) ring[st][sect * 64 + lane] &= keep;
+    }
+    // the writes land before the barrier that publishes them (s_barrier
+    // alone does not wait for them): lgkmcnt(0), no wait on the others
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   };
 
   // ----------------------------------------------------------- queries
@@ -388,7 +479,7 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
   bf16x8 qv[RBW][KS];
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
-    int row = 64 * wave + 16 * r + n;
+    int row = RPW * wave + 16 * r + n;
     if (row >= ti.n_rows) row = 0;
     const int hold = row / p.G;
     const int gq = row - hold * p.G;
@@ -405,99 +496,138 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
   float m_ref[RBW], m_max[RBW], l_run[RBW];
   const float cs = p.abs_scale_log2;
 
-  // ------------------------------------------------------------- math
-  // One 32-token step of the chunk for this wave's four row blocks. Rows
-  // outside the chunk's mask and tokens past its end get -inf scores
-  // (full: no masking needed); blocks with no row in the mask skip their
-  // products.
-  auto math = [&](const u32x4* buf, uint64_t m64, int tb, int ntok, bool full, bool first_pass)
-      __attribute__((always_inline)) {
-    auto on = [&](int r) { return full || ((m64 >> (16 * r)) & 0xFFFFull) != 0; };
-    uint32_t act[RBW];
+  // ------------------------------------------------------------- steps
+  // A step as one wave sees it: m holds the wave's rows in the chunk's
+  // mask (row 16 r + n at bit 16 r + n), tb the step's first token in the
+  // chunk, st its ring stage; full: every row in, no token past the end.
+  struct Step {
+    uint32_t m;
+    int tb, ntok, st;
+    bool full;
+  };
+  auto step_of = [&](const Cursor& c, int st) __attribute__((always_inline)) {
+    Step s;
+    const uint64_t rows = ch_c[c.ci].rows[(RPW * wave) >> 6];
+    s.m = (uint32_t)(rows >> ((RPW * wave) & 63));
+    s.tb = 32 * c.s;
+    s.ntok = c.ntok;
+    s.st = st;
+    s.full = s.m == ~0u && s.tb + 32 <= c.ntok;
+    return s;
+  };
+  auto block_on = [&](const Step& s, int r) __attribute__((always_inline)) {
+    return (s.full || ((s.m >> (16 * r)) & 0xFFFFu) != 0) ? 1u : 0u;
+  };
+  // Q.K^T of a step for both blocks, into sc (issued; read a step later).
+  // A wave with no row in the step reads no K (the products are skipped).
+  auto scores = [&](const Step& s, f32x4 (&sc)[RBW][2]) __attribute__((always_inline)) {
+    u32x4 kreg[2 * KS];
+    if (s.m != 0) {
+      const u32x4* buf = ring[s.st];
 #pragma unroll
-    for (int r = 0; r < RBW; ++r) act[r] = __builtin_amdgcn_readfirstlane((int)(on(r) ? 1 : 0));
-    u32x4 kreg[2 * KS], vreg[DB];
-#pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) kreg[i] = buf[i * 64 + lane];
-    f32x4 sc[RBW][2];
-    float s8[RBW][8], mu[RBW];
-    // scores of block r to masked, scaled maxima and the block's reference
-    auto row_max = [&](int r) __attribute__((always_inline)) {
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s8[r][4 * tau + i] = sc[r][tau][i];
-      if (NEG) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s8[r][e] = -s8[r][e];
-      }
-      // (after the negation: a masked score stays -inf)
-      if (!full) {
-        const int valid = ((m64 >> (16 * r + n)) & 1ull) ? ntok - (tb + voff) : 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s8[r][e] = e < valid ? s8[r][e] : kNegInf;
-      }
-      float m = fmaxf(fmaxf(s8[r][0], s8[r][1]), fmaxf(s8[r][2], s8[r][3]));
-      m = fmaxf(m, fmaxf(fmaxf(s8[r][4], s8[r][5]), fmaxf(s8[r][6], s8[r][7])));
-      const float mx = max_xor32(max_xor16(m)) * cs;
-      m_max[r] = fmaxf(m_max[r], mx);
-      // the first finite maximum becomes the reference (nothing has been
-      // accumulated yet, so nothing is rescaled)
-      if (first_pass && m_ref[r] == kNegInf) m_ref[r] = mx;
-      mu[r] = (m_ref[r] == kNegInf) ? 0.f : m_ref[r];
-    };
-    // block r + 1's products under block r's maxima
-    qk_block<KS>(sc[0][0], sc[0][1], kreg, qv[0], act[0]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int r = 1; r < RBW; ++r) {
-      qk_block<KS>(sc[r][0], sc[r][1], kreg, qv[r], act[r]);
-      __builtin_amdgcn_sched_barrier(0);
-      row_max(r - 1);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 2 * KS; ++i) kreg[i] = buf[i * 64 + lane];
     }
-    // the V operands now (the K operands are dead): their reads overlap the
-    // last block's maxima and the first probabilities
+    const uint32_t on0 = s.m != 0 ? block_on(s, 0) : 0u;
+    const uint32_t on1 = s.m != 0 ? block_on(s, 1) : 0u;
+    qk_pair<KS>(sc, kreg, qv[0], qv[1], on0, on1);
+  };
+  // block r's scores to masked values x and their reference mu; the row's
+  // running maximum and (first pass) its first finite maximum updated
+  auto row_max = [&](const Step& s, const f32x4 (&sc)[2], int r, float (&x)[8], float& mu,
+                     bool first_pass) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < DB; ++j) vreg[j] = buf[(2 * KS + j) * 64 + lane];
-    settle_v(sc[RBW - 1][0], sc[RBW - 1][1]);
-    row_max(RBW - 1);
-    // block r's products, each followed by a slice of block r + 1's
-    // probabilities (the next block's vector work under this block's
-    // matrix products)
-    Probs cur, nxt;
-    cur.psum = 0.f;
-    probs_slices<0, 8>(cur, s8[0], cs, mu[0]);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
-    for (int r = 0; r < RBW; ++r) {
-      nxt.psum = 0.f;
-      const int rn = r + 1 < RBW ? r + 1 : r;
-      if (r + 1 < RBW)
-        pv_interleaved<0, DB, true>(acc[r], vreg, cur, nxt, s8[rn], cs, mu[rn], act[r]);
-      else
-        pv_interleaved<0, DB, false>(acc[r], vreg, cur, nxt, s8[rn], cs, mu[rn], act[r]);
-      l_run[r] += cur.psum;
-      cur = nxt;
+      for (int i = 0; i < 4; ++i) x[4 * tau + i] = sc[tau][i];
+    if (NEG) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = -x[e];
     }
+    // (after the negation: a masked score stays -inf)
+    if (!s.full) {
+      const int valid = ((s.m >> (16 * r + n)) & 1u) ? s.ntok - (s.tb + voff) : 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = e < valid ? x[e] : kNegInf;
+    }
+    const float m = rmax(rmax3(x[0], x[1], x[2]), rmax3(x[3], x[4], rmax3(x[5], x[6], x[7])));
+    const float mx = rmax_rows(m) * cs;
+    m_max[r] = rmax(m_max[r], mx);
+    // the first finite maximum becomes the reference (nothing has been
+    // accumulated yet, so nothing is rescaled)
+    if (first_pass && m_ref[r] == kNegInf) m_ref[r] = mx;
+    mu = (m_ref[r] == kNegInf) ? 0.f : m_ref[r];
   };
 
-  // -------------------------------------------------------------- loop
-  // At step t: wait for this wave's loads of step t (the younger ones may
-  // stay in flight), zero the ragged tail, barrier (step t has landed for
-  // every wave, and every wave is done with step t - 1, whose stage is now
-  // free), load step t + NS - 1 into that stage, compute step t. The
-  // s_waitcnt immediate has vmcnt in bits 3:0 and 15:14; expcnt 7 and
-  // lgkmcnt 15 mean no wait on those.
-  constexpr int kWait = (NS - 2) * SPL;
+  // One iteration: make step t + 1 visible and load step t + NS - 1 into
+  // the stage step t - 1 used; issue step t + 1's score products; finish
+  // step t from its scores (cur): maxima, probabilities, P.V. nxt receives
+  // step t + 1's scores.
+  constexpr int kWait = (NS - 3) * SPL;
   constexpr int kWaitVm = 0x0F70 | (kWait & 0xF) | ((kWait >> 4) << 14);
-  __shared__ int redo_s;
+  Cursor ld, cq;
+  Step cur_s, nxt_s;  // steps t and t + 1 (nxt_s read a step ahead)
+  Ids ld_ids;         // block ids of ld's step, read a step ahead
+  int st_next = 0, st_free = 0;
+  auto iter = [&](int t, f32x4 (&cur)[RBW][2], f32x4 (&nxt)[RBW][2], bool first_pass)
+      __attribute__((always_inline)) {
+    const bool more = t + 1 < total;
+    __builtin_amdgcn_s_waitcnt(kWaitVm);
+    if (more && cq.s == cq.nst - 1 && (cq.ntok & 31) != 0) zero_tail(cq, st_next);
+    __builtin_amdgcn_s_barrier();
+    issue(ld, ld_ids, st_free);
+    advance(ld);
+    ld_ids = ids_of(ld);
+    Step nx_s = nxt_s;
+    if (!more) nx_s.m = 0u;
+    const Step s = cur_s;
+    float x[RBW][8], mu[RBW];
+    u32x4 vreg[DB];
+    uint32_t act[RBW];
+    if (s.m != 0) {
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) {
+        act[r] = block_on(s, r);
+        row_max(s, cur[r], r, x[r], mu[r], first_pass);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    scores(nx_s, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s.m != 0) {
+      // (the V operands after the K ones are dead; their reads overlap
+      // block 0's probabilities)
+      const u32x4* buf = ring[s.st];
+#pragma unroll
+      for (int j = 0; j < DB; ++j) vreg[j] = buf[(2 * KS + j) * 64 + lane];
+      // block 0's probabilities, then its products, each followed by a
+      // slice of block 1's probabilities, then block 1's products
+      Probs p0, p1;
+      p0.psum = 0.f;
+      p1.psum = 0.f;
+      probs_slices<0, 8>(p0, x[0], cs, mu[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_interleaved<0, DB, true>(acc[0], vreg, p0, p1, x[1], cs, mu[1], act[0]);
+      pv_interleaved<0, DB, false>(acc[1], vreg, p1, p1, x[1], cs, mu[1], act[1]);
+      l_run[0] += p0.psum;
+      l_run[1] += p1.psum;
+    }
+    advance(cq);
+    st_free = s.st;
+    cur_s = nx_s;
+    st_next = st_next + 1 == NS ? 0 : st_next + 1;
+    nxt_s = step_of(cq, st_next);
+  };
+
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
     m_ref[r] = kNegInf;
     m_max[r] = kNegInf;
   }
+  f32x4 scA[RBW][2], scB[RBW][2];
   for (int pass = 0; pass < 2; ++pass) {
+    // (a second pass: the first one's output stores are still counted in
+    // vmcnt; let them finish, so that the counted waits below see loads only)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < RBW; ++r) {
@@ -505,30 +635,32 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
       for (int j = 0; j < DB; ++j) zero_acc(acc[r][j], zero);
       l_run[r] = 0.f;
     }
-    Cursor ld, cp;
+#pragma unroll
+    for (int r = 0; r < RBW; ++r) settle<DB>(acc[r]);
+    // steps 0 .. NS - 2 into stages 0 .. NS - 2; step 0 visible; its scores
     enter(ld, 0);
-    enter(cp, 0);
 #pragma unroll
     for (int k = 0; k < NS - 1; ++k) {
-      issue(ld, k);
+      issue(ld, ids_of(ld), k);
       advance(ld);
     }
-    int st_cur = 0, st_nxt = NS - 1;
-    for (int t = 0; t < total; ++t) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm);
-      if (cp.s == cp.nst - 1 && (cp.ntok & 31) != 0) zero_tail(cp, st_cur);
-      __builtin_amdgcn_s_barrier();
-      issue(ld, st_nxt);
-      advance(ld);
-      const uint64_t rows = ch_s[cp.ci].rows[wave];
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)rows);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(rows >> 32));
-      const uint64_t m64 = ((uint64_t)hi << 32) | lo;
-      const int tb = 32 * cp.s;
-      if (m64 != 0) math(ring[st_cur], m64, tb, cp.ntok, m64 == ~0ull && tb + 32 <= cp.ntok, pass == 0);
-      advance(cp);
-      st_nxt = st_cur;
-      st_cur = st_cur + 1 == NS ? 0 : st_cur + 1;
+    ld_ids = ids_of(ld);
+    enter(cq, 0);
+    {
+      constexpr int kW0 = (NS - 2) * SPL;
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (kW0 & 0xF) | ((kW0 >> 4) << 14));
+    }
+    if (cq.s == cq.nst - 1 && (cq.ntok & 31) != 0) zero_tail(cq, 0);
+    __builtin_amdgcn_s_barrier();
+    cur_s = step_of(cq, 0);
+    scores(cur_s, scA);
+    advance(cq);
+    st_next = 1;
+    st_free = NS - 1;
+    nxt_s = step_of(cq, st_next);
+    for (int t = 0; t < total; t += 2) {
+      iter(t, scA, scB, pass == 0);
+      if (t + 1 < total) iter(t + 1, scB, scA, pass == 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the walk
 
@@ -538,7 +670,7 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
     for (int r = 0; r < RBW; ++r) {
       settle<DB>(acc[r]);
       const float l_tot = sum_xor32(sum_xor16(l_run[r]));
-      const int row = 64 * wave + 16 * r + n;
+      const int row = RPW * wave + 16 * r + n;
       if (row >= ti.n_rows) continue;
       const int hold = row / p.G;
       const int gq = row - hold * p.G;
@@ -578,9 +710,9 @@ bool tree_supported(int D, int BS) {
 
 hipError_t launch_attn_tree(int D, int BS, int stages, const AttnParams& p, int n_wg,
                             hipStream_t stream, const LaunchEvents& ev) {
-  if (!tree_supported(D, BS) || (stages != 3 && stages != 4)) return hipErrorInvalidValue;
+  if (!tree_supported(D, BS) || stages < 4 || stages > 6) return hipErrorInvalidValue;
   if (n_wg <= 0) return hipSuccess;
-  const dim3 grid((unsigned)n_wg), block(256);
+  const dim3 grid((unsigned)n_wg), block(512);
   const bool neg = p.q_flip != 0;  // a negative softmax scale
 #define PKV_TREE_NS(d, bs, ns)                                                                   \
   return neg ? launch_kernel(attn_tree_kernel<d, bs, ns, true>, grid, block, stream, ev,         \
@@ -589,10 +721,12 @@ hipError_t launch_attn_tree(int D, int BS, int stages, const AttnParams& p, int 
                              (const AttnCore&)p, p.meta);
 #define PKV_TREE(d, bs)               \
   if (D == d && BS == bs) {           \
-    if (stages == 3) {                \
-      PKV_TREE_NS(d, bs, 3)           \
-    } else {                          \
+    if (stages == 4) {                \
       PKV_TREE_NS(d, bs, 4)           \
+    } else if (stages == 5) {         \
+      PKV_TREE_NS(d, bs, 5)           \
+    } else {                          \
+      PKV_TREE_NS(d, bs, 6)           \
     }                                 \
   }
   PKV_TREE(64, 16)

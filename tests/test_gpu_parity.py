@@ -531,24 +531,34 @@ def test_single_token_returns_its_value(pkv):
 
 # ------------------------------------------------ full-size, sampled outputs
 
-def sampled_decode(name, n_samples=48, seed=0):
+def sampled_decode(name, n_samples=48, seed=0, tree=0):
+    """The full-size decode: one whole layer (every branch and query head,
+    drawn at random) and n_samples rows drawn from all layers, against the
+    oracle's float64 values."""
     w = get(name)
-    note(f"full-size {name}: generating inputs")
+    note(f"full-size {name} (tree {tree}): generating inputs")
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp)
+    c.set_option("tree", tree)
     seqs = [h[s] for s in w.query_sids]
     q = to_device(inp.q)
+    c.set_option("timing", 1)
     out = c.decode(seqs, q, scale=w.softmax_scale)
     torch.cuda.synchronize()
+    c.set_option("timing", 0)
+    n_tree = c.timing_read("attention_tree")[1]
     got = out.cpu().numpy()
     info = c.plan_info(seqs)
     c.close()
     note(f"full-size {name}: plan {info}")
+    assert (n_tree > 0) == (tree > 0 and info["n_items"] == 0)
     pool = build_oracle(w, inp)
     rng = np.random.default_rng(seed)
     qf = inp.q.f32()
     L, B, Hq, D = got.shape
-    worst = 0.0
+    layer = int(rng.integers(L))
+    want = oracle.decode(pool, list(w.query_sids), qf, w.softmax_scale, layers=[layer])[0]
+    check_close(got[layer], want, f"full-size {name}, layer {layer} ({B * Hq} rows)")
     gs, ws = [], []
     for _ in range(n_samples):
         l, b, hh = int(rng.integers(L)), int(rng.integers(B)), int(rng.integers(Hq))
@@ -564,7 +574,15 @@ def test_full_size_decode_sampled(name):
     sampled_decode(name)
 
 
+def test_full_size_mcts_tree_launch():
+    """The MCTS batch through the tree launch (option tree 1 selects it for
+    this batch): one whole layer and sampled rows against the oracle."""
+    sampled_decode("mcts", seed=3, tree=1)
+
+
 def test_full_size_verify_sampled():
+    """One whole verify request (every node and query head) and sampled
+    nodes of the others."""
     w = get("verify")
     note("full-size verify: generating inputs")
     inp = generate(w)
@@ -577,18 +595,28 @@ def test_full_size_verify_sampled():
     pool = build_oracle(w, inp)
     qf = inp.q.f32()
     rng = np.random.default_rng(1)
+    G = w.shape.G
+
+    def want_node(r, i, g, K, V, ctx):
+        idx = list(range(ctx)) + [ctx + j for j in oracle.ancestors(inp.parents[r], i)]
+        return oracle.attention._softmax_attend(qf[r, i, g * G:(g + 1) * G], K[idx, g], V[idx, g],
+                                                w.softmax_scale)
+
+    whole = int(rng.integers(len(reqs)))
+    K, V = pool.kv(w.query_sids[whole], layer=0)
+    ctx = K.shape[0] - w.n_nodes
+    gs = [got[whole, i, g * G:(g + 1) * G] for i in range(w.n_nodes) for g in range(w.shape.Hkv)]
+    ws = [want_node(whole, i, g, K, V, ctx) for i in range(w.n_nodes) for g in range(w.shape.Hkv)]
+    check_close(np.concatenate(gs), np.concatenate(ws),
+                f"full-size verify, request {whole} ({w.n_nodes * w.shape.Hq} rows)")
     gs, ws = [], []
     for _ in range(24):
-        r, i, hh = int(rng.integers(4)), int(rng.integers(w.n_nodes)), int(rng.integers(w.shape.Hq))
+        r, i, g = int(rng.integers(len(reqs))), int(rng.integers(w.n_nodes)), int(rng.integers(w.shape.Hkv))
         K, V = pool.kv(w.query_sids[r], layer=0)
         ctx = K.shape[0] - w.n_nodes
-        idx = list(range(ctx)) + [ctx + j for j in oracle.ancestors(inp.parents[r], i)]
-        g = hh // w.shape.G
-        want = oracle.attention._softmax_attend(qf[r, i, hh][None], K[idx, g], V[idx, g],
-                                                w.softmax_scale)[0]
-        gs.append(got[r, i, hh])
-        ws.append(want)
-    check_close(np.stack(gs), np.stack(ws), "full-size verify (24 sampled rows)")
+        gs.append(got[r, i, g * G:(g + 1) * G])
+        ws.append(want_node(r, i, g, K, V, ctx))
+    check_close(np.concatenate(gs), np.concatenate(ws), "full-size verify (24 sampled nodes)")
     assert np.all(np.isfinite(got))
 
 

@@ -573,24 +573,28 @@ def test_plan_folds_short_edges_per_leaf(pkv):
 
 def test_plan_tree_for_mcts(pkv):
     """The MCTS batch (64 leaves x G = 4 = 256 rows, 256 planes) takes the
-    tree plan by default: one item, the root cut into 8 pieces of 512 tokens
-    and the 126 edges whole (134 chunks), each token slot read once (unique
-    tokens as for the other plan), no partial states; off with tree 0, and
-    not taken when the planes do not fill the chip (a one-layer call) unless
-    forced (tree 2) or when the rows do not fit one workgroup."""
+    tree plan when asked (option tree 1): one item, the root cut into 8
+    pieces of 512 tokens and the 126 edges whole (134 chunks), each token
+    slot read once (unique tokens as for the other plan), no partial states.
+    Off by default (tree 0); with tree 1 not taken when the planes do not
+    fill the chip (a one-layer call) unless forced (tree 2), nor when the
+    rows do not fit one workgroup."""
     w = get("mcts")
     c, seqs = build_host_tree(pkv, w)
+    items = c.plan_info(seqs)
+    assert items["partial_rows"] > 0
+    c.set_option("tree", 1)
     tree = c.plan_info(seqs)
     assert tree["n_chunks"] == 4096 // 512 + 126
     assert tree["n_items"] == 0 and tree["partial_rows"] == 0
     assert tree["unique_tokens"] == distinct_tokens(c, seqs) == 4096 + 126 * 32
+    assert items["unique_tokens"] == tree["unique_tokens"]
     assert tree["workspace_bytes"] == (tree["plan_bytes"] + 255) // 256 * 256   # the plan alone
     c.set_option("tree_piece_tokens", 1024)
     assert c.plan_info(seqs)["n_chunks"] == 4 + 126
     c.set_option("tree_piece_tokens", 512)
     c.set_option("tree", 0)
-    items = c.plan_info(seqs)
-    assert items["partial_rows"] > 0 and items["unique_tokens"] == tree["unique_tokens"]
+    assert c.plan_info(seqs)["partial_rows"] > 0
     c.set_option("tree", 1)
     one_layer = c.plan_info(seqs, n_layers=1)         # 8 planes: the root is split for parallelism
     assert one_layer["partial_rows"] > 0
