@@ -54,7 +54,8 @@ def kernel_source_hash() -> str:
     work and the entry points that set its defaults (all decide the HBM
     traffic)."""
     h = hashlib.sha256()
-    for name in ("kernels.hip", "attn_plan.h", "schedule.hpp", "schedule.cpp", "api.cpp"):
+    for name in ("kernels.hip", "tree.hip", "kernel_common.h", "attn_plan.h", "schedule.hpp",
+                 "schedule.cpp", "api.cpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -100,7 +101,7 @@ def record_traffic(workload: str, fetch_dir: str, write_dir: str, source: str) -
         scale = round((1 << 30) / (copy_kib * 1024) * 4) / 4   # to a quarter: 2.0 / 1.0 here
         per = 0.0
         names = []
-        for kname in ("attn_mfma_kernel", "attn_wide_kernel"):
+        for kname in ("attn_mfma_kernel", "attn_wide_kernel", "attn_tree_kernel"):
             vals = [v for n, v in rr if kname in n]
             if vals:
                 names.append(kname)

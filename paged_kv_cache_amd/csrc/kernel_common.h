@@ -64,15 +64,48 @@ __device__ __forceinline__ void swap16(float& a, float& b) {
 __device__ __forceinline__ void swap32(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
 }
+// Maxima as written (v_max_f32, v_max3_f32): on values the compiler cannot
+// prove canonical (results of asm statements and matrix products, lanes
+// moved by the permutes) fmaxf quiets each input first, two more vector
+// instructions per maximum. Quiet NaN inputs are ignored as by fmaxf.
+__device__ __forceinline__ float rmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float rmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float rmax8(const float (&x)[8]) {
+  return rmax(rmax3(x[0], x[1], x[2]), rmax3(x[3], x[4], rmax3(x[5], x[6], x[7])));
+}
+// rmax8 of values that may come straight from matrix products: the compiler
+// does not add the wait states a product's result needs before a vector
+// instruction reads it when the reader is an asm statement, so the statement
+// waits them itself (s_nop 7: the 8 the compiler gives its own readers of a
+// v_mfma_f32_16x16x32_bf16 result).
+__device__ __forceinline__ float rmax8_fresh(const float (&x)[8]) {
+  float a, b;
+  asm("s_nop 7\n\t"
+      "v_max3_f32 %0, %2, %3, %4\n\t"
+      "v_max3_f32 %1, %5, %6, %7\n\t"
+      "v_max3_f32 %0, %0, %8, %9\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "=&v"(a), "=&v"(b)
+      : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]));
+  return a;
+}
 __device__ __forceinline__ float max_xor16(float x) {
   float a = x, b = x;
   swap16(a, b);
-  return fmaxf(a, b);
+  return rmax(a, b);
 }
 __device__ __forceinline__ float max_xor32(float x) {
   float a = x, b = x;
   swap32(a, b);
-  return fmaxf(a, b);
+  return rmax(a, b);
 }
 __device__ __forceinline__ float sum_xor16(float x) {
   float a = x, b = x;

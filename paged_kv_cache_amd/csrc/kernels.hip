@@ -340,10 +340,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
         }
         sc[e] = v;
       }
-    float mx = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-    mx = max_xor32(max_xor16(mx));
+    const float mx = max_xor32(max_xor16(rmax8(sc)));
     rebase(mx, m_run[r], l_run[r], acc[r]);
     const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
     float psum = 0.f;
@@ -788,10 +785,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
               sc[e] = kNegInf;
           }
         }
-        float mx = sc[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-        mx = max_xor32(max_xor16(mx)) * p.abs_scale_log2;
+        const float mx = max_xor32(max_xor16(rmax8_fresh(sc))) * p.abs_scale_log2;
         rebase(mx, m_run[r], l_run[r], acc[r]);
         const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
         l_run[r] += probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);
@@ -866,10 +860,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
               sc[e] = kNegInf;
           }
         }
-        float mx = sc[0];
-#pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-        mx = max_xor32(max_xor16(mx)) * p.abs_scale_log2;
+        const float mx = max_xor32(max_xor16(rmax8_fresh(sc))) * p.abs_scale_log2;
         rebase(mx, m_run[r], l_run[r], acc[r]);
         const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
         l_run[r] += probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);

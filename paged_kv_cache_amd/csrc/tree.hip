@@ -193,29 +193,6 @@ __device__ __forceinline__ void qk_pair<2>(f32x4 (&s)[2][2], const u32x4 (&k)[4]
       : "scc");
 }
 
-// Maxima as written (v_max_f32, v_max3_f32): the scores come out of asm
-// statements, and fmaxf on values the compiler cannot prove canonical
-// quiets each input first (two more instructions per maximum).
-__device__ __forceinline__ float rmax(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float rmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-// the maximum over the four lanes of a row (l, l ^ 16, l ^ 32, l ^ 48)
-__device__ __forceinline__ float rmax_rows(float x) {
-  float a = x, b = x;
-  swap16(a, b);
-  x = rmax(a, b);
-  a = x;
-  b = x;
-  swap32(a, b);
-  return rmax(a, b);
-}
 
 // A block's queries (KS 16-byte pieces per lane, 64 bytes apart) loaded
 // straight into AGPRs, the load waited for in the same statement: defined
@@ -549,8 +526,7 @@ void attn_tree_kernel(AttnCore p, PlanBytes plan_bytes) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = e < valid ? x[e] : kNegInf;
     }
-    const float m = rmax(rmax3(x[0], x[1], x[2]), rmax3(x[3], x[4], rmax3(x[5], x[6], x[7])));
-    const float mx = rmax_rows(m) * cs;
+    const float mx = max_xor32(max_xor16(rmax8(x))) * cs;
     m_max[r] = rmax(m_max[r], mx);
     // the first finite maximum becomes the reference (nothing has been
     // accumulated yet, so nothing is rescaled)
