@@ -49,15 +49,47 @@ METRIC = "unique-KV HBM GB/s (% of peak) and branch-queries/sec, paged decode at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """sha256 (first 16 hex) of the kernels, the planner that cuts their
-    work and the entry points that set its defaults (all decide the HBM
-    traffic)."""
+KERNEL_SOURCES = ("kernels.hip", "tree.hip", "kernel_common.h", "attn_plan.h", "schedule.hpp",
+                  "schedule.cpp", "api.cpp")
+
+
+def code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed, so
+    that a change to comments alone keeps the hash (string literals, which
+    hold the inline assembly, are kept as written)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_source_hash(read=None) -> str:
+    """sha256 (first 16 hex) of the code (comments dropped) of the kernels,
+    the planner that cuts their work and the entry points that set its
+    defaults: all of it decides the HBM traffic. read(name) returns a
+    file's text (default: the working tree)."""
+    if read is None:
+        def read(name):
+            with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", name), encoding="utf-8") as f:
+                return f.read()
     h = hashlib.sha256()
-    for name in ("kernels.hip", "tree.hip", "kernel_common.h", "attn_plan.h", "schedule.hpp",
-                 "schedule.cpp", "api.cpp"):
-        with open(os.path.join(ROOT, "paged_kv_cache_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+    for name in KERNEL_SOURCES:
+        h.update(code_only(read(name)).encode())
     return h.hexdigest()[:16]
 
 

@@ -3,31 +3,29 @@
 // and each of its edges -- exactly once, applies it to the rows that hold it
 // and writes the final output rows. For a deep tree (an MCTS tree: a root
 // held by all leaves, then edges held by fewer and fewer) the shared root is
-// a dense contraction over all rows and the edges are memory traffic; in one
-// workgroup per plane the two overlap across the chip, no partial state is
-// written and no second launch re-reads the edges per leaf.
+// a dense contraction over all rows and the edges are memory traffic; no
+// partial state is written and no second launch re-reads the edges per
+// leaf. (On the MCTS batch it measures slower than the wide root launch
+// followed by the narrow leaf launch: each step is one barrier-synchronised
+// walk of all eight waves, and on an edge only the waves holding its rows
+// work while the rest wait.)
 //
 // Shape: 8 waves, two per SIMD, each owning 32 rows (two 16-row blocks), so
 // every K/V operand read from LDS feeds two matrix products. Each wave also
 // moves its eighth of every 32-token step of K/V from global memory into
 // LDS (global_load_lds_dwordx4, operand order, as the wide kernel's loaders
-// do), keeping NS - 1 steps in flight in a ring of NS separate LDS arrays.
-// Two waves per SIMD leave each up to 256 registers (VGPRs and AGPRs), and
-// let the SIMD issue one wave's softmax while the other's matrix products
-// run: with one wave per SIMD, every vector instruction that waits on a
-// product's result, and every product that waits on the busy matrix unit,
-// stalls the SIMD.
+// do) into a ring of NS separate LDS arrays. Two waves per SIMD leave each
+// up to 256 registers (VGPRs and AGPRs).
 //
-// Per step and wave (both blocks active): Q.K^T for the two blocks from one
-// read of the K sections, the row maxima, then per block the probabilities
-// (bf16 hi + lo, as in the other kernels) and its P.V products from one
-// read of the V sections, the second block's probabilities placed between
-// the first block's products.
+// Per step and wave: the next step's Q.K^T for both blocks from one read of
+// its K sections (issued first), then this step's row maxima, per block the
+// probabilities (bf16 hi + lo, as in the other kernels) and its P.V
+// products from one read of the V sections, the second block's
+// probabilities placed between the first block's products.
 //
 // Chunks whose row mask leaves some rows out (the edges) skip the row blocks
 // with no row in the mask and give masked rows -inf scores. Odd planes walk
-// the chunk list backwards, so at any moment about half the workgroups are
-// in a compute-heavy stretch (the root) and half in a memory-heavy one.
+// the chunk list backwards.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -69,23 +67,13 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       : "memory");
 }
 
-// P.V for one 16-row block: acc[j] += V^T[16j .. 16j + 15][32 tokens] P^T,
-// P = hi + lo (two products per d block), with the accumulators held in
-// AGPRs: written as asm so that they stay there (given the builtin, the
-// compiler moves accumulators that the rare rescale multiplies into VGPRs,
-// and four blocks of them do not fit beside the rest). One statement per d
-// block, so that the scheduler can place the vector work of another block
-// between them. s_nop 1 gives the two wait states a VALU write of an
-// operand needs before a matrix product reads it; the two products into one
-// accumulator run back to back (same shape, exact overlap: no wait). An
+// P.V for one 16-row block is acc[j] += V^T[16j .. 16j + 15][32 tokens] P^T
+// with P = hi + lo (two products per d block) and the accumulators held in
+// AGPRs, written as asm (pv_step_if below) so that they stay there: given
+// the builtin, the compiler moves the accumulators into VGPRs, and the
+// blocks' accumulators do not fit beside the rest. The two products into
+// one accumulator run back to back (same shape, exact overlap: no wait). An
 // accumulator is read back by other code only after settle() below.
-__device__ __forceinline__ void pv_step(f32x4& acc, const u32x4& v, bf16x8 phi, bf16x8 plo) {
-  asm("s_nop 1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %1, %3, %0"
-      : "+a"(acc)
-      : "v"(v), "v"(phi), "v"(plo));
-}
 
 // Q.K^T for a wave's two 16-row blocks: per block the two 16-token score
 // tiles of a 32-token step, s[r][tau] = K[tau] Q_r^T (rows of the tile are
@@ -235,11 +223,12 @@ __device__ __forceinline__ void zero_acc(f32x4& acc, const u32x4& z) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(z));
 }
 
-// pv_step for a block that may have no row in the chunk's mask (on == 0:
-// skip both products). The skip is a branch inside the statement, so that
-// for the compiler the accumulator is always rewritten by it: a branch
-// around it in C++ would make the compiler copy every accumulator at the
-// join.
+// One d block of a row block's P.V, hi then lo, for a block that may have
+// no row in the chunk's mask (on == 0: skip both products). The skip is a
+// branch inside the statement, so that for the compiler the accumulator is
+// always rewritten by it: a branch around it in C++ would make the compiler
+// copy every accumulator at the join. s_nop 1 gives the two wait states a
+// vector write of an operand needs before a product reads it.
 __device__ __forceinline__ void pv_step_if(f32x4& acc, const u32x4& v, bf16x8 phi, bf16x8 plo,
                                            uint32_t on) {
   asm("s_cmp_eq_u32 %4, 0\n\t"
