@@ -2,8 +2,9 @@
 (its workspace is the library's static device array), against
 pkv_decode_attn with a caller's workspace: two calls in a row, the second
 on a smaller batch, each bit-identical to the ordinary entry point and
-within the oracle bar; a call that needs more than the array holds is
-refused with PKV_E_WORKSPACE."""
+within the oracle bar, through the item launches and through the tree
+launch; a call that needs more than the array holds is refused with
+PKV_E_WORKSPACE."""
 
 from __future__ import annotations
 
@@ -36,14 +37,18 @@ def note(msg):
     sys.stdout.flush()
 
 
-def test_noalloc_matches_the_workspace_entry_point(pkv):
+@pytest.mark.parametrize("tree", [0, 2])
+def test_noalloc_matches_the_workspace_entry_point(pkv, tree):
     from paged_kv_cache_amd import binding
     for w in (FIRST, SECOND):
         inp = generate(w)
         c, h = build_library(pkv, w, inp)
+        c.set_option("tree", tree)
         seqs = [h[s] for s in w.query_sids]
         info = c.plan_info(seqs)
-        note(f"noalloc {w.name}: plan {info['plan_bytes']} B, workspace {info['workspace_bytes']} B")
+        note(f"noalloc {w.name} (tree {tree}): plan {info['plan_bytes']} B, "
+             f"workspace {info['workspace_bytes']} B, items {info['n_items']}")
+        assert (info["n_items"] == 0) == (tree == 2)
         q = to_device(inp.q)
         ref = c.decode(seqs, q, scale=w.softmax_scale)
         got = torch.full_like(ref, float("nan"))
