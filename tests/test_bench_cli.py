@@ -86,3 +86,22 @@ def test_nested_records_keep_the_measured_fields():
     out = bench.nested(rec)
     assert out == {"workload": "x", "value": 1.0, "unit": "GB/s", "roofline": {"frac": 0.5},
                    "parity": {"ok": True}}
+
+
+def test_kernel_hash_ignores_comments_only():
+    """The stored HBM counters are keyed by the kernels' code: a comment or
+    layout edit keeps the key, a code edit (also inside an asm string)
+    changes it."""
+    src = {name: bench.code_only("") for name in bench.KERNEL_SOURCES}
+    text = ('// header\nint f(int a) { /* sum */ return a + 1; }  // tail\n'
+            'void g() { asm("s_nop 7\\n\\t// not a comment" : : ); }\n')
+    src[bench.KERNEL_SOURCES[0]] = text
+    base = bench.kernel_source_hash(lambda n: src[n])
+    commented = text.replace("int f(int a) {", "/* a new\n   comment */ int  f(int a)\n{")
+    src[bench.KERNEL_SOURCES[0]] = commented
+    assert bench.kernel_source_hash(lambda n: src[n]) == base
+    for edit in (text.replace("a + 1", "a + 2"), text.replace("s_nop 7", "s_nop 6"),
+                 text.replace("// not a comment", "// other text")):
+        src[bench.KERNEL_SOURCES[0]] = edit
+        assert bench.kernel_source_hash(lambda n: src[n]) != base
+    assert bench.code_only('x = "/* kept */"; // gone\ny;') == 'x = "/* kept */"; y;'
