@@ -218,6 +218,14 @@ typedef struct {
                              "inline_plan"), else copied into the workspace */
   int64_t wide_tokens;    /* of unique_tokens, those in chunks served by the
                              wide-row launch (the rest: the narrow launch) */
+  int64_t read_tokens;    /* token slots the work items read per (layer, KV
+                             head): each item's chunk, in whole blocks; above
+                             unique_tokens when short shared segments are read
+                             once per branch or per group (option "fold_tokens",
+                             "group_rows"); the tree launch reads unique_tokens */
+  int32_t grouped_items;  /* work items that serve a group of branches
+                             (option "group_rows") */
+  int32_t reserved;
 } pkv_plan_info;
 
 /* Plans decode attention for these sequences (as pkv_decode_workspace_size
@@ -400,6 +408,14 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       branch that holds it, together with the branch's
  *                       neighbouring short segments, instead of once for all
  *                       (its partial states would outweigh its K/V); 0: never
+ *   "group_rows"        16: after folding, sibling branches whose folded paths
+ *                       share blocks (the leaves under one MCTS node) are served
+ *                       by one item of up to this many rows (group_rows / G
+ *                       branches; at most 16 and at most "rows_per_item"), which
+ *                       reads each of their blocks once and masks it for the
+ *                       rows whose branch does not hold it; a group is formed
+ *                       only when its blocks are at most 3/4 of its members'
+ *                       (0: never; the vector path never groups)
  *   "prefix_cache_blocks" num_blocks: most entries the prompt cache holds
  *                       (0..num_blocks; applies to later inserts)
  *   "finalize"          1: when every branch has one chunk read by narrow items and

@@ -382,6 +382,7 @@ SchedOptions planner_options(const pkv_pool* p, bool mfma) {
     o.wide = false;
     o.max_row_blocks_per_wave = 1;
     o.short_items = false;
+    o.group_rows = 0;  // (the vector kernel has no per-block row masks)
   } else {
     o.tree_ok = p->pool.desc().kv_dtype == PKV_BF16 &&
                 tree_supported(p->pool.desc().head_dim, p->pool.desc().block_size);
@@ -494,6 +495,7 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.off_comb_rows = (int32_t)S.off_comb_rows;
   a.off_titems = (int32_t)S.off_titems;
   a.off_tchunks = (int32_t)S.off_tchunks;
+  a.off_binfo = (int32_t)S.off_binfo;
   a.n_order = S.n_order_narrow;
   a.n_long = (S.n_narrow - S.n_short) * S.n_layers * d.num_kv_heads;
   a.n_codes = S.n_narrow * S.n_layers * d.num_kv_heads;
@@ -1025,6 +1027,14 @@ int pkv_decode_plan_info(pkv_pool* pool, const pkv_seq* seqs, int32_t n_seqs, in
   info->wide_tokens = S.wide_tokens;
   info->workspace_bytes = (int64_t)S.total_bytes;
   info->plan_bytes = (int64_t)S.meta_bytes;
+  info->read_tokens = S.tree ? S.unique_tokens : 0;
+  info->grouped_items = 0;
+  const int32_t bs = pool->pool.desc().block_size;
+  for (const WorkItem& w : S.items) {
+    info->read_tokens += (int64_t)(w.n_tok + bs - 1) / bs * bs;
+    info->grouped_items += w.grouped ? 1 : 0;
+  }
+  info->reserved = 0;
   return PKV_OK;
   PKV_GUARD_END
 }
@@ -1135,6 +1145,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
   } else if (k == "fold_tokens") {
     if (value < 0 || value > 8192) return fail(PKV_E_INVALID, "fold_tokens must be 0..8192");
     pool->opt.fold_tokens = (int32_t)value;
+  } else if (k == "group_rows") {
+    if (value < 0 || value > 16) return fail(PKV_E_INVALID, "group_rows must be 0..16");
+    pool->opt.group_rows = (int32_t)value;
   } else if (k == "short_items") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "short_items must be 0 or 1");
     pool->opt.short_items = value != 0;

@@ -43,7 +43,9 @@ struct WorkItem {
   int32_t mask_from;  // first logical position under the draft-tree mask (INT32_MAX: none)
   int32_t reread;     // 1: another item (or another wave) reads the same chunk, so K/V
                       // go through the caches; 0: streaming loads
-  int32_t pad[3];
+  int32_t grouped;    // 0, or the holder bits of all the item's holders: the chunk is a
+                      // group of branches' blocks, each masked by its binfo word
+  int32_t pad[2];
 };
 static_assert(sizeof(WorkItem) == 48, "WorkItem layout");
 
@@ -96,10 +98,11 @@ struct AttnCore {
   //   order    wide launch: per workgroup item * (n_layers * Hkv) + layer * Hkv + head, or -1
   //   comb_ptr [n_branch + 1], comb_rows: each branch's partial rows (q-head offset 0) in logical order
   //   titems   TreeItem[], tchunks TreeChunk[] (tree launch only)
+  //   binfo    parallel to blk (grouped items only): holder bits | valid slots << 16
   const uint8_t* meta_dev;
   int32_t meta_inline;
   int32_t off_items, off_blk, off_holders, off_anc, off_order, off_comb_ptr, off_comb_rows;
-  int32_t off_titems, off_tchunks;
+  int32_t off_titems, off_tchunks, off_binfo;
   int32_t n_order;          // workgroups in the launch
   // Narrow launch (no order table): code = item * (n_layers * Hkv) + layer *
   // Hkv + head. Workgroups [0, n_long) take code = blockIdx; after them each

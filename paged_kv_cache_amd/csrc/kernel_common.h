@@ -147,6 +147,7 @@ struct PlanArrays {
   const int32_t* comb_rows;
   const TreeItem* titems;
   const TreeChunk* tchunks;
+  const int32_t* binfo;
 };
 typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;
 __device__ __forceinline__ PlanArrays plan_arrays(const AttnCore& p, const PlanBytes& m) {
@@ -155,7 +156,7 @@ __device__ __forceinline__ PlanArrays plan_arrays(const AttnCore& p, const PlanB
           (const int32_t*)(b + p.off_holders),    (const uint64_t*)(b + p.off_anc),
           (const int32_t*)(b + p.off_order),      (const int32_t*)(b + p.off_comb_ptr),
           (const int32_t*)(b + p.off_comb_rows),  (const TreeItem*)(b + p.off_titems),
-          (const TreeChunk*)(b + p.off_tchunks)};
+          (const TreeChunk*)(b + p.off_tchunks),  (const int32_t*)(b + p.off_binfo)};
 }
 
 // Online softmax with a lazy reference: a row's probabilities are taken as

@@ -217,6 +217,13 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
   bool row_ok[RW];
   uint64_t anc[RW];
   const bool tree = it.mask_from != 0x7fffffff && it.t0 + it.n_tok > it.mask_from;
+  // A grouped item holds several sibling branches' blocks, each once; a
+  // block's binfo word has bit h set when the item's holder h reads it and
+  // its valid slots in bits 16 and up: row r sees a token when its holder's
+  // bit is set and the token's slot is valid.
+  const bool grouped = it.grouped != 0;
+  const int32_t* binfo = sp.binfo + it.blk_off;
+  int32_t hbit[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int row = (rg * RW + r) * 16 + n;
@@ -224,6 +231,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
     const int crow = it.r0 + row;
     const int hold = crow / p.G;
     const int gq = crow - hold * p.G;
+    hbit[r] = grouped ? 1 << (hold & 31) : 0;
     const int branch = row_ok[r] ? sp.holders[it.hold_off + hold] : 0;
     const int qh = kvh * p.G + gq;
     const uint16_t* qp =
@@ -294,16 +302,32 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
     load_k(s, bA, bB, kr);
     load_v(s, bA, bB, vr);
   };
+  // binfo words of step s's two block slots (as ids reads the block ids;
+  // the same word twice when a block spans the step)
+  auto infos = [&](int s, int& a, int& b) {
+    a = b = 0;
+    if (grouped) {
+      a = binfo[(32 * s) / BS];
+      b = binfo[(32 * s + 16) / BS];
+    }
+  };
   // slots past the chunk may hold anything (even NaN): zero them in the
-  // chunk's last step so that 0 * V stays 0 in the P.V product
-  auto zero_tail = [&](int s, u32x4 (&vraw)[DB]) {
+  // chunk's last step so that 0 * V stays 0 in the P.V product (in a
+  // grouped item, the slots past each block's valid ones)
+  auto zero_tail = [&](int s, u32x4 (&vraw)[DB], int iA, int iB) {
     const int tv = s * 32 + voff;
-    if (s * 32 + 32 > it.n_tok) {
+    int lim = it.n_tok;
+    bool cut = s * 32 + 32 > it.n_tok;
+    if (grouped && ((iA >> 16) < BS || (iB >> 16) < BS)) {
+      lim = (tv & ~(BS - 1)) + ((v_in_b ? iB : iA) >> 16);
+      cut = true;
+    }
+    if (cut) {
       u32x4 keep;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = (tv + 2 * w < it.n_tok) ? 0x0000ffffu : 0u;
-        const uint32_t hi = (tv + 2 * w + 1 < it.n_tok) ? 0xffff0000u : 0u;
+        const uint32_t lo = (tv + 2 * w < lim) ? 0x0000ffffu : 0u;
+        const uint32_t hi = (tv + 2 * w + 1 < lim) ? 0xffff0000u : 0u;
         keep[w] = lo | hi;
       }
 #pragma unroll
@@ -321,10 +345,21 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
     }
   };
   // online softmax of row block r in step s, and its P.V products
-  auto softmax_pv_rb = [&](int s, int r, const f32x4 (&st)[2], const u32x4 (&vraw)[DB]) {
+  auto softmax_pv_rb = [&](int s, int r, const f32x4 (&st)[2], const u32x4 (&vraw)[DB], int iA,
+                           int iB) {
     const int tbase = s * 32;
-    const bool tail = tbase + 32 > it.n_tok;
     const int tv = tbase + voff;
+    // tokens at or past lim are masked: the chunk's end, or in a grouped
+    // item the end of the valid slots of the lane's block when the row's
+    // holder reads it, else the block's start (none); a step whose blocks
+    // every holder reads in full needs no mask
+    int lim = it.n_tok;
+    bool cut = tbase + 32 > it.n_tok;
+    if (grouped && ((iA & iB & 0xffff) != it.grouped || (iA >> 16) < BS || (iB >> 16) < BS)) {
+      const int info = v_in_b ? iB : iA;
+      lim = (tv & ~(BS - 1)) + ((info & hbit[r]) ? (info >> 16) : 0);
+      cut = true;
+    }
     float sc[8];
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
@@ -333,7 +368,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
         const int e = 4 * tau + i;
         const int t = tv + e;
         float v = st[tau][i] * p.scale_log2;
-        if (tail && t >= it.n_tok) v = kNegInf;
+        if (cut && t >= lim) v = kNegInf;
         if (tree) {
           const int pos = it.t0 + t;
           if (pos >= it.mask_from && !((anc[r] >> (pos - it.mask_from)) & 1ull)) v = kNegInf;
@@ -360,14 +395,14 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
       if (LO) acc[r][j] = mfma_bf16(as_bf16x8(vraw[j]), plo, acc[r][j]);
     }
   };
-  auto compute = [&](int s, const u32x4 (&kraw)[2][KS], u32x4 (&vraw)[DB]) {
-    zero_tail(s, vraw);
+  auto compute = [&](int s, const u32x4 (&kraw)[2][KS], u32x4 (&vraw)[DB], int iA, int iB) {
+    zero_tail(s, vraw, iA, iB);
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
       if (r > 0 && r >= nblk) continue;
       f32x4 st[2];
       scores_rb(r, kraw, st);
-      softmax_pv_rb(s, r, st, vraw);
+      softmax_pv_rb(s, r, st, vraw, iA, iB);
       // one row block at a time: interleaving the two would keep both
       // blocks' scores and probabilities live
       if (RW > 1) __builtin_amdgcn_sched_barrier(0);
@@ -386,14 +421,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
       }
     };
     if (!PF && D <= 128) {
-      int bA, bB;
+      int bA, bB, iA, iB;
       ids(phase, bA, bB);
+      infos(phase, iA, iB);
       for (int s = phase; s < n_steps; s += phases) {
-        const int cA = bA, cB = bB;
-        if (s + phases < n_steps) ids(s + phases, bA, bB);
+        const int cA = bA, cB = bB, jA = iA, jB = iB;
+        if (s + phases < n_steps) {
+          ids(s + phases, bA, bB);
+          infos(s + phases, iA, iB);
+        }
         u32x4 kr[2][KS], vr[DB];
         load_kv(s, cA, cB, kr, vr);
-        compute(s, kr, vr);
+        compute(s, kr, vr, jA, jB);
       }
     } else if (!PF) {
       // D = 256 (one wave per SIMD, a 32 KiB step per wave): one register
@@ -429,15 +468,19 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
         __builtin_amdgcn_sched_barrier(0);
         load_k(sn, bA, bB, kr);
         __builtin_amdgcn_sched_barrier(0);
-        zero_tail(s, vr);
+        int iA, iB;
+        infos(s, iA, iB);
+        zero_tail(s, vr, iA, iB);
 #pragma unroll
         for (int r = 0; r < RW; ++r)
-          if (r == 0 || r < nblk) softmax_pv_rb(s, r, st[r], vr);
+          if (r == 0 || r < nblk) softmax_pv_rb(s, r, st[r], vr, iA, iB);
         __builtin_amdgcn_sched_barrier(0);
         load_v(sn, bA, bB, vr);
         __builtin_amdgcn_sched_barrier(0);
       }
-      compute(s, kr, vr);
+      int iA, iB;
+      infos(s, iA, iB);
+      compute(s, kr, vr, iA, iB);
     } else {
       // loads of the wave's next step are in flight while this one computes
       // (two register sets, loop unrolled by two)
@@ -454,13 +497,16 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
         ids(min(s1, last), bA, bB);
         load_kv(min(s1, last), bA, bB, kb, vb);
         __builtin_amdgcn_sched_barrier(0);
-        compute(s, ka, va);
+        int iA, iB;
+        infos(s, iA, iB);
+        compute(s, ka, va, iA, iB);
         if (s1 >= n_steps) break;
         const int s2 = min(s1 + phases, last);
         ids(s2, bA, bB);
         load_kv(s2, bA, bB, ka, va);
         __builtin_amdgcn_sched_barrier(0);
-        compute(s1, kb, vb);
+        infos(s1, iA, iB);
+        compute(s1, kb, vb, iA, iB);
       }
     }
   }

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <stdexcept>
 #include <cstring>
+#include <unordered_map>
 
 namespace pkv {
 
@@ -28,6 +29,10 @@ struct Segment {
   int32_t n_hold = 0;
   int32_t chunk_begin = 0, chunk_end = 0;  // into the chunk list
   int32_t mask_from = 0x7fffffff;          // draft-tree mask start (verify)
+  // a group of branches (see group_runs): per block, the holder bits and
+  // valid slots (<< 16); n_tok is then blocks * block size
+  std::vector<int32_t> binfo;
+  int32_t all_bits = 0;                    // holder bits of all its holders
 };
 
 struct Chunk {
@@ -101,6 +106,10 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
       c.n_tok = std::min(s.n_tok, (b1 - b0) * bs + b0 * bs) - b0 * bs;
       for (int32_t b = b0; b < b1; ++b) S->blk.push_back(s.blocks[b]);
       while ((S->blk.size() - c.blk_off) % step_blocks) S->blk.push_back(s.blocks[b1 - 1]);
+      if (S->grouped) {
+        for (int32_t b = b0; b < b1; ++b) S->binfo.push_back(s.binfo.empty() ? 0 : s.binfo[b]);
+        S->binfo.resize(S->blk.size(), 0);  // padding: no holder, no valid slot
+      }
       c.part_base = S->P;
       S->P += s.n_hold * G;
       chunks.push_back(c);
@@ -121,6 +130,8 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
     w.t0 = c.t0;
     w.hold_off = s.hold_off;
     w.mask_from = s.mask_from;
+    w.grouped = s.all_bits;
+    if (s.all_bits && rows > rpi) throw std::logic_error("planner: a grouped item wider than a narrow one");
     if (opt.wide && rows > rpi) {
       S->wide_tokens += c.n_tok;
       // wide items of one chunk (siblings) read it through the shared L2
@@ -279,6 +290,92 @@ bool plan_tree(const std::vector<Segment>& segs, int32_t n, int32_t bs, int32_t 
   return true;
 }
 
+// Groups of sibling branches, after folding: a branch whose folded run is
+// its only single-holder segment is a candidate; candidates are sorted by
+// their runs' block ids, so that branches sharing a run prefix (siblings of
+// a tree) sit next to each other, and cut into groups of `per`. A group
+// whose union of blocks is at most 3/4 of its members' blocks becomes one
+// segment: its holders (ascending), the union in first-seen order, and per
+// block the bits of the holders that read it and its valid slots. Its items
+// read each shared block once for all members instead of once per member.
+// A block two members see with different valid counts (a kept, partly
+// filled block after a truncate) enters the union once per count.
+void group_runs(std::vector<Segment>& segs, std::vector<std::vector<int32_t>>& path,
+                const std::vector<const Seq*>& sv, int32_t bs, int32_t per, Schedule* S) {
+  const int32_t n = (int32_t)path.size();
+  std::vector<int32_t> run(n, -1), cand;
+  for (int32_t i = 0; i < n; ++i) {
+    int32_t runs = 0;
+    for (int32_t sgi : path[i])
+      if (segs[sgi].n_hold == 1) {
+        ++runs;
+        run[i] = sgi;
+      }
+    if (runs == 1) cand.push_back(i);
+  }
+  std::stable_sort(cand.begin(), cand.end(), [&](int32_t a, int32_t b) {
+    const std::vector<int32_t>& x = segs[run[a]].blocks;
+    const std::vector<int32_t>& y = segs[run[b]].blocks;
+    return std::lexicographical_compare(x.begin(), x.end(), y.begin(), y.end());
+  });
+  std::vector<int32_t> group_of(n, -1);
+  std::vector<char> dead(segs.size(), 0);
+  std::vector<Segment> groups;
+  std::unordered_map<int64_t, int32_t> seen;
+  for (size_t c0 = 0; c0 + 1 < cand.size(); c0 += per) {
+    const size_t c1 = std::min(cand.size(), c0 + per);
+    std::vector<int32_t> hs(cand.begin() + c0, cand.begin() + c1);
+    std::sort(hs.begin(), hs.end());
+    Segment g;
+    g.t0 = 0x7fffffff;
+    seen.clear();
+    int64_t total = 0;
+    for (size_t c = c0; c < c1; ++c) {
+      const int32_t i = cand[c];
+      const Segment& r = segs[run[i]];
+      const int32_t bit = 1 << (int32_t)(std::lower_bound(hs.begin(), hs.end(), i) - hs.begin());
+      const int32_t p0 = r.t0 / bs;
+      g.t0 = std::min(g.t0, r.t0);
+      for (size_t j = 0; j < r.blocks.size(); ++j) {
+        const int32_t v = std::min<int32_t>(bs, sv[i]->len - (p0 + (int32_t)j) * bs);
+        const int64_t key = (int64_t)r.blocks[j] * 128 + v;  // v <= 64
+        auto ins = seen.emplace(key, (int32_t)g.blocks.size());
+        if (ins.second) {
+          g.blocks.push_back(r.blocks[j]);
+          g.binfo.push_back(v << 16);
+        }
+        g.binfo[ins.first->second] |= bit;
+      }
+      total += (int64_t)r.blocks.size();
+    }
+    if (4 * (int64_t)g.blocks.size() > 3 * total) continue;  // too little shared
+    g.n_tok = (int32_t)g.blocks.size() * bs;
+    g.hold_off = (int32_t)S->holders.size();
+    g.n_hold = (int32_t)hs.size();
+    g.all_bits = (1 << g.n_hold) - 1;
+    S->holders.insert(S->holders.end(), hs.begin(), hs.end());
+    for (int32_t i : hs) {
+      dead[run[i]] = 1;
+      group_of[i] = (int32_t)groups.size();
+    }
+    groups.push_back(std::move(g));
+  }
+  if (groups.empty()) return;
+  std::vector<Segment> out;
+  std::vector<int32_t> remap(segs.size(), -1);
+  for (size_t k = 0; k < segs.size(); ++k) {
+    if (dead[k]) continue;
+    remap[k] = (int32_t)out.size();
+    out.push_back(std::move(segs[k]));
+  }
+  const int32_t g0 = (int32_t)out.size();
+  for (Segment& g : groups) out.push_back(std::move(g));
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t& sgi : path[i]) sgi = dead[sgi] ? g0 + group_of[i] : remap[sgi];
+  segs = std::move(out);
+  S->grouped = true;
+}
+
 }  // namespace
 
 void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
@@ -345,6 +442,8 @@ void Schedule::layout(int Hkv, int D) {
   o = align16(o + titems.size() * sizeof(TreeItem));
   off_tchunks = o;
   o = align16(o + tchunks.size() * sizeof(TreeChunk));
+  off_binfo = o;
+  o = align16(o + binfo.size() * sizeof(int32_t));
   meta_bytes = o;
   const size_t planes = (size_t)n_layers * Hkv;
   off_ml = align256(o);
@@ -366,6 +465,7 @@ void Schedule::pack_meta(uint8_t* dst) const {
   if (!titems.empty()) std::memcpy(dst + off_titems, titems.data(), titems.size() * sizeof(TreeItem));
   if (!tchunks.empty())
     std::memcpy(dst + off_tchunks, tchunks.data(), tchunks.size() * sizeof(TreeChunk));
+  if (!binfo.empty()) std::memcpy(dst + off_binfo, binfo.data(), binfo.size() * sizeof(int32_t));
 }
 
 void PlannerScratch::ensure(int nb) {
@@ -562,6 +662,8 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
       }
       segs = std::move(out);
       S->holders = std::move(holders);
+      const int32_t rows = std::min({opt.group_rows, 16, std::max<int32_t>(1, opt.rows_per_item)});
+      if (rows / G >= 2) group_runs(segs, path, sv, bs, rows / G, S);
     }
   }
   const std::vector<Chunk> chunks = emit_chunks(segs, bs, G, n_layers, d.num_kv_heads, opt, S);

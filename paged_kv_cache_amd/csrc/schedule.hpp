@@ -34,6 +34,12 @@ struct SchedOptions {
   int32_t short_tokens = kShortTokens;  // longest narrow item (of <= 16 rows) that counts as short
   int32_t fold_tokens = 64;        // shared segments shorter than this are read per branch (0: never)
   bool finalize = true;            // the narrow launch may write final outputs (see Schedule::finalize)
+  // Rows of one grouped item at most (0: no grouping): after folding, the
+  // runs of sibling branches that share blocks are served by one item of
+  // group_rows / G branches, which reads each of their blocks once and
+  // masks it for the rows whose branch does not hold it. At most 16 (one
+  // row block) and at most rows_per_item.
+  int32_t group_rows = 16;
   // Tree launch (one workgroup per plane holding every row and reading each
   // chunk once): 0 never, 1 when it applies and pays (all rows fit one
   // workgroup, some segment has more rows than a narrow item, and the planes
@@ -51,6 +57,7 @@ struct Schedule {
   int32_t n_narrow = 0;
   int32_t n_short = 0;             // short narrow items (the last n_short of the narrow ones)
   bool folded = false;             // short shared segments were folded into per-branch items
+  bool grouped = false;            // some item serves a group of branches (binfo is filled)
   // Every branch has exactly one chunk read by narrow items and its other
   // chunks by wide items: the wide launch runs first, so each narrow row can
   // merge its branch's wide partials itself and write the output (no combine).
@@ -65,6 +72,9 @@ struct Schedule {
   int32_t n_order_narrow = 0;      // workgroups of the narrow launch (no table)
   int32_t n_order_wide = 0;
   std::vector<int32_t> blk;
+  // parallel to blk when grouped: holder bits of the block within its item
+  // (bit h: the item's holder h reads it) | valid slots << 16; 0 on padding
+  std::vector<int32_t> binfo;
   std::vector<int32_t> holders;
   std::vector<int32_t> comb_ptr;
   std::vector<int32_t> comb_rows;
@@ -79,8 +89,8 @@ struct Schedule {
 
   // byte offsets inside the workspace
   size_t off_items = 0, off_blk = 0, off_holders = 0, off_comb_ptr = 0, off_comb_rows = 0,
-         off_anc = 0, off_order = 0, off_titems = 0, off_tchunks = 0, meta_bytes = 0, off_ml = 0,
-         off_acc = 0, total_bytes = 0;
+         off_anc = 0, off_order = 0, off_titems = 0, off_tchunks = 0, off_binfo = 0,
+         meta_bytes = 0, off_ml = 0, off_acc = 0, total_bytes = 0;
 
   void layout(int Hkv, int D);
   // Fills `order` for n_layers x Hkv planes (items must be final).

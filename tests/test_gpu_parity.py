@@ -70,13 +70,17 @@ SMALL_DECODE = [
 ]
 
 
+PLAN = {}   # plan_info of the last run_decode call
+
+
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
                row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256, fold=64,
-               scale=None, inline_plan=1):
+               scale=None, inline_plan=1, group=16):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("inline_plan", inline_plan)
     c.set_option("fold_tokens", fold)
+    c.set_option("group_rows", group)
     c.set_option("concurrent", concurrent)
     c.set_option("short_items", short_items)
     c.set_option("short_tokens", short_tokens)
@@ -95,6 +99,8 @@ def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1
     out = c.decode(seqs, q, scale=w.softmax_scale if scale is None else scale)
     torch.cuda.synchronize()
     res = out.cpu().numpy()
+    PLAN.clear()
+    PLAN.update(c.plan_info(seqs))
     c.close()
     return inp, res
 
@@ -181,6 +187,88 @@ def test_folded_short_segments_match_oracle(w, fold):
     pool = build_oracle(w, inp)
     want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
     check_close(a, want, f"{w.name} fold_tokens={fold}")
+
+
+GROUPED = [
+    SMALL_DECODE[3],   # G 4: groups of 4 leaves; 21-token edges: each leaf's last block part-filled
+    SMALL_DECODE[8],   # G 8: pairs of leaves, beside a wide root
+    scaled("mcts", "mcts_d64_bs32", shape=replace_shape(B16, L=2, Hq=8, Hkv=2, D=64, BS=32),
+           root_len=90, depth=4, edge_len=13),
+    # 64-token edges fill whole 64-token blocks (folded with fold_tokens 128)
+    scaled("mcts", "mcts_d256_bs64", shape=replace_shape(AG, L=1, Hq=8, Hkv=2, BS=64), root_len=100,
+           depth=3, edge_len=64),
+    scaled("mcts", "mcts_g1", shape=replace_shape(B16, L=1, Hq=2, Hkv=2), root_len=50, depth=5,
+           edge_len=9),
+]
+
+
+@pytest.mark.parametrize("w", GROUPED, ids=lambda w: w.name)
+@pytest.mark.parametrize("group,pf,st", [(16, 0, 256), (8, 0, 256), (16, 1, 256), (16, 0, 8192),
+                                         (16, 0, 32)],
+                         ids=["rows16", "rows8", "prefetch", "one_wave", "four_waves"])
+def test_grouped_siblings_match_oracle(w, group, pf, st):
+    """Sibling leaves served by one item that reads their blocks once, each
+    masked for the rows whose leaf does not hold it (option group_rows):
+    the oracle's outputs, and the per-leaf plan's to fp32 rounding; on one
+    wave or four (short_tokens) and with the prefetching loop."""
+    note(f"grouped {w.name} group_rows={group} prefetch={pf} short_tokens={st}")
+    fold = 128 if w.shape.BS == 64 else 64
+    inp, a = run_decode(w, group=group, prefetch=pf, short_tokens=st, fold=fold)
+    grouped = PLAN["grouped_items"]
+    G = w.shape.Hq // w.shape.Hkv
+    # (pairs of the 21-token-edge tree share too little to be grouped)
+    assert grouped > 0 if group == 16 else (grouped == 0 or group // G >= 2), (w.name, grouped)
+    _, b = run_decode(w, group=0, prefetch=pf, short_tokens=st, fold=fold)
+    assert PLAN["grouped_items"] == 0
+    assert errors(a, b)[0] <= 1e-4
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(a, want, f"{w.name} grouped rows={group}")
+
+
+def test_grouped_forks_with_unequal_valid_counts():
+    """Forks of a 40-token root truncated to 40, 39, 38 and 37 tokens hold the
+    root's third block (8 slots filled) with 8, 7, 6 and 5 valid slots: the
+    group's item reads that block once per valid count, each for its own
+    rows; two further forks add a block of their own. Against the oracle."""
+    L, Hkv, Hq, D, bs = 2, 2, 8, 128, 16
+    rng = np.random.default_rng(11)
+    c = pytest.pkv.PagedKVCache(64, bs, L, Hkv, Hq, D, dtype="bf16", device="cuda")
+    pool = oracle.OraclePool(64, bs)
+    h = {}
+    n = 40
+    k, v = draw(rng, (L, n, Hkv, D), "bf16"), draw(rng, (L, n, Hkv, D), "bf16")
+    a = pool.create()
+    h[a] = c.create()
+    pool.append(a, k.f32(), v.f32())
+    c.append([h[a]], [n], to_device(k), to_device(v))
+    sids = []
+    for j in range(4):
+        s = pool.fork(a)
+        h[s] = c.fork(h[a])
+        pool.truncate(s, n - j)
+        c.truncate(h[s], n - j)
+        sids.append(s)
+    for j in range(2):
+        s = pool.fork(a)
+        h[s] = c.fork(h[a])
+        k1, v1 = draw(rng, (L, 12, Hkv, D), "bf16"), draw(rng, (L, 12, Hkv, D), "bf16")
+        pool.append(s, k1.f32(), v1.f32())
+        c.append([h[s]], [12], to_device(k1), to_device(v1))
+        sids.append(s)
+    seqs = [h[s] for s in sids]
+    info = c.plan_info(seqs)
+    note(f"unequal valid counts: {info}")
+    assert info["grouped_items"] >= 1
+    q = draw(rng, (L, len(sids), Hq, D), "bf16")
+    got = c.decode(seqs, to_device(q), scale=D ** -0.5).cpu().numpy()
+    want = oracle.decode(pool, sids, q.f32(), D ** -0.5)
+    check_close(got, want, "grouped forks with unequal valid counts")
+    c.set_option("group_rows", 0)
+    assert c.plan_info(seqs)["grouped_items"] == 0
+    base = c.decode(seqs, to_device(q), scale=D ** -0.5).cpu().numpy()
+    assert errors(got, base)[0] <= 1e-4
+    c.close()
 
 
 @pytest.mark.parametrize("w", [SMALL_DECODE[2], SMALL_DECODE[8]], ids=lambda w: w.name)

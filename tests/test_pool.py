@@ -557,6 +557,7 @@ def test_plan_folds_short_edges_per_leaf(pkv):
     c, seqs = build_host_tree(pkv, w)
     G = w.shape.Hq // w.shape.Hkv
     c.set_option("tree", 0)          # (the narrow / wide items' plan)
+    c.set_option("group_rows", 0)    # (one item per leaf)
     c.set_option("fold_tokens", 0)
     plain = c.plan_info(seqs)
     c.set_option("fold_tokens", 64)
@@ -567,8 +568,76 @@ def test_plan_folds_short_edges_per_leaf(pkv):
     assert folded["n_chunks"] == root_chunks + 64
     assert plain["partial_rows"] == root_chunks * 64 * G + 6 * 64 * G
     assert folded["partial_rows"] == root_chunks * 64 * G + 64 * G
+    # every token slot once, then the root once and each leaf's 6 edges
+    assert plain["read_tokens"] == plain["unique_tokens"] == 4096 + 126 * 32
+    assert folded["read_tokens"] == 4096 + 64 * 6 * 32
+    assert plain["grouped_items"] == folded["grouped_items"] == 0
     c.set_option("fold_tokens", 16)                    # shorter than the edges: no folding
     assert c.plan_info(seqs) == plain
+
+
+def test_plan_groups_sibling_leaves(pkv):
+    """With grouping (option group_rows, 16 by default), the four leaves under
+    each depth-4 node of the MCTS tree (4 x G = 16 rows) share one item that
+    reads their path's 10 distinct edges once (4 shared, 2 at depth 5, 4 at
+    depth 6) instead of 4 x 6: 16 items, 16 chunks and 320 tokens each, and
+    one partial row per leaf row as with one item per leaf. With 8 rows,
+    pairs of sibling leaves (7 edges for 2 x 6); with 4 rows (one leaf), no
+    group. The order of the batch does not matter: siblings are found by
+    their blocks."""
+    w = get("mcts")
+    c, seqs = build_host_tree(pkv, w)
+    G = w.shape.Hq // w.shape.Hkv
+    assert G == 4
+    c.set_option("tree", 0)
+    c.set_option("group_rows", 0)
+    single = c.plan_info(seqs)
+    c.set_option("group_rows", 16)
+    quads = c.plan_info(seqs)
+    root_chunks = single["n_chunks"] - 64
+    assert quads["grouped_items"] == 16
+    assert quads["n_chunks"] == root_chunks + 16
+    assert quads["partial_rows"] == single["partial_rows"]
+    assert quads["read_tokens"] == 4096 + 16 * 10 * 32
+    assert quads["unique_tokens"] == single["unique_tokens"]
+    c.set_option("group_rows", 8)
+    pairs = c.plan_info(seqs)
+    assert pairs["grouped_items"] == 32
+    assert pairs["read_tokens"] == 4096 + 32 * 7 * 32
+    c.set_option("group_rows", 4)
+    assert c.plan_info(seqs) == single
+    c.set_option("group_rows", 16)
+    shuffled = [seqs[i] for i in np.random.default_rng(3).permutation(len(seqs))]
+    again = c.plan_info(shuffled)
+    assert again["grouped_items"] == 16 and again["read_tokens"] == quads["read_tokens"]
+    c.set_option("rows_per_item", 8)                   # groups fit a narrow item
+    assert c.plan_info(seqs)["read_tokens"] == 4096 + 32 * 7 * 32
+
+
+def test_plan_groups_only_what_shares(pkv):
+    """Branches whose folded paths share less than a quarter of their blocks
+    stay one item each: 8 forks of a 40-token root (its 2 full blocks shared,
+    32 tokens, folded) that each append 400 tokens read 2 + 26 blocks each
+    (the root's partly filled block copied, then 25 more), a group of four
+    2 + 104 of 112 blocks. Forks of a 60-token root (3 shared blocks) that
+    append 20 tokens (2 blocks of their own) form groups: 3 + 8 of 20."""
+    c = pkv.PagedKVCache(512, 16, 1, 2, 8, 64, dtype="bf16", device=None)
+    root = c.create()
+    c.plan(root, 40)
+    kids = [c.fork(root) for _ in range(8)]
+    for k in kids:
+        c.plan(k, 400)
+    info = c.plan_info(kids)
+    assert info["grouped_items"] == 0
+    assert info["read_tokens"] == 8 * (48 + 400)
+    c2 = pkv.PagedKVCache(512, 16, 1, 2, 8, 64, dtype="bf16", device=None)
+    r2 = c2.create()
+    c2.plan(r2, 60)
+    kids2 = [c2.fork(r2) for _ in range(8)]
+    for k in kids2:
+        c2.plan(k, 20)
+    info2 = c2.plan_info(kids2)
+    assert info2["grouped_items"] == 2
 
 
 def test_plan_tree_for_mcts(pkv):
