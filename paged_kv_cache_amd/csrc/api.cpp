@@ -498,6 +498,8 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
   a.off_binfo = (int32_t)S.off_binfo;
   a.n_order = S.n_order_narrow;
   a.n_long = (S.n_narrow - S.n_short) * S.n_layers * d.num_kv_heads;
+  a.n_long_wgs = S.n_long_wgs;
+  a.long_by_plane = S.long_by_plane ? 1 : 0;
   a.n_codes = S.n_narrow * S.n_layers * d.num_kv_heads;
   a.short_by_plane = S.folded ? 1 : 0;
   a.out = out;

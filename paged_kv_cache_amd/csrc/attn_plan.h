@@ -108,6 +108,8 @@ struct AttnCore {
   // Hkv + head. Workgroups [0, n_long) take code = blockIdx; after them each
   // workgroup takes four codes of short items, one per wave.
   int32_t n_long;
+  int32_t n_long_wgs;       // workgroups of the long items (padded when long_by_plane)
+  int32_t long_by_plane;    // long items: a plane's items in consecutive rounds of one XCD
   int32_t n_codes;
   int32_t short_by_plane;   // short workgroups take four items of one plane (else four planes of one item)
   // With finalize, the narrow launch runs after the wide one and each of its

@@ -180,22 +180,32 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnCore p, PlanBytes pl
   // shared edges in one L2 (MCTS leaves: 148 -> 141 us; four planes of one
   // item read adjacent tiles and stayed faster for unshared items, 95 us
   // against 96 for the beam).
-  const bool solo = (int)blockIdx.x >= p.n_long;
+  const bool solo = (int)blockIdx.x >= p.n_long_wgs;
   int code = (int)blockIdx.x;
-  if (solo && !p.short_by_plane) {
-    code = p.n_long + ((int)blockIdx.x - p.n_long) * 4 + wave;
+  if (!solo && p.long_by_plane) {
+    // long items of a folded plan, dealt the same way: a plane's items in
+    // consecutive rounds of one XCD, so that items reading the same edges
+    // meet them in its L2
+    const int planes = p.n_layers * p.Hkv;
+    const int n_li = p.n_long / planes;
+    const int r = (int)blockIdx.x >> 3;
+    const int grp = r / n_li, k = r - grp * n_li;
+    const int plane = grp * 8 + ((int)blockIdx.x & 7);
+    code = plane < planes ? k * planes + plane : p.n_codes;
+  } else if (solo && !p.short_by_plane) {
+    code = p.n_long + ((int)blockIdx.x - p.n_long_wgs) * 4 + wave;
   } else if (solo) {
     const int planes = p.n_layers * p.Hkv;
     const int n_short = (p.n_codes - p.n_long) / planes;
     const int wpp = (n_short + 3) >> 2;  // workgroups per plane
-    const int w = (int)blockIdx.x - p.n_long;
+    const int w = (int)blockIdx.x - p.n_long_wgs;
     const int r = w >> 3;
     const int grp = r / wpp, k = r - grp * wpp;
     const int plane = grp * 8 + (w & 7);
     const int s_item = 4 * k + wave;
     code = (plane < planes && s_item < n_short) ? p.n_long + s_item * planes + plane : p.n_codes;
   }
-  if (code >= p.n_codes) return;  // only whole waves of a solo workgroup
+  if (code >= p.n_codes) return;  // whole waves of a solo workgroup, or a padding workgroup
   const int per_item = p.n_layers * p.Hkv;
   const int item_idx = code / per_item;
   const int rem = code - item_idx * per_item;

@@ -191,6 +191,7 @@ std::vector<Chunk> emit_chunks(std::vector<Segment>& segs, int32_t bs, int32_t G
   });
   S->n_short = 0;
   for (const WorkItem& w : narrow) S->n_short += is_short(w) ? 1 : 0;
+  S->long_by_plane = S->folded && opt.short_items;
   std::stable_sort(wide_groups.begin(), wide_groups.end(),
                    [](const std::vector<WorkItem>& a, const std::vector<WorkItem>& b) {
                      if (a.size() != b.size()) return a.size() > b.size();
@@ -391,7 +392,10 @@ void Schedule::build_order(int32_t n_layers, int32_t Hkv) {
   const int64_t short_wgs = n_short == 0 ? 0
                             : folded  ? (int64_t)((LH + 7) / 8) * 8 * ((n_short + 3) / 4)
                                       : (short_codes + 3) / 4;
-  n_order_narrow = (int32_t)(long_codes + short_wgs);
+  const int64_t long_wgs = long_by_plane ? (int64_t)((LH + 7) / 8) * 8 * (n_narrow - n_short)
+                                         : long_codes;
+  n_long_wgs = (int32_t)long_wgs;
+  n_order_narrow = (int32_t)(long_wgs + short_wgs);
   // wide launch: a unit is (sibling group, plane); the R siblings of a unit
   // are placed 8 workgroups apart, so that with workgroups dealt round-robin
   // to the 8 XCDs they share one XCD (and its L2) and start together

@@ -58,6 +58,10 @@ struct Schedule {
   int32_t n_short = 0;             // short narrow items (the last n_short of the narrow ones)
   bool folded = false;             // short shared segments were folded into per-branch items
   bool grouped = false;            // some item serves a group of branches (binfo is filled)
+  // long narrow items dealt by plane as the short ones of a folded plan are
+  // (n_long_wgs counts the padded grid part); matrix-core launch only
+  bool long_by_plane = false;
+  int32_t n_long_wgs = 0;
   // Every branch has exactly one chunk read by narrow items and its other
   // chunks by wide items: the wide launch runs first, so each narrow row can
   // merge its branch's wide partials itself and write the output (no combine).
