@@ -293,8 +293,10 @@ bool plan_tree(const std::vector<Segment>& segs, int32_t n, int32_t bs, int32_t 
 
 // Groups of sibling branches, after folding: a branch whose folded run is
 // its only single-holder segment is a candidate; candidates are sorted by
-// their runs' block ids, so that branches sharing a run prefix (siblings of
-// a tree) sit next to each other, and cut into groups of `per`. A group
+// their paths of segments before folding (`key`: segment numbers, given in
+// the order the batch meets them, so the groups do not depend on where the
+// blocks sit in the pool), so that branches sharing a path prefix (siblings
+// of a tree) sit next to each other, and cut into groups of `per`. A group
 // whose union of blocks is at most 3/4 of its members' blocks becomes one
 // segment: its holders (ascending), the union in first-seen order, and per
 // block the bits of the holders that read it and its valid slots. Its items
@@ -302,7 +304,8 @@ bool plan_tree(const std::vector<Segment>& segs, int32_t n, int32_t bs, int32_t 
 // A block two members see with different valid counts (a kept, partly
 // filled block after a truncate) enters the union once per count.
 void group_runs(std::vector<Segment>& segs, std::vector<std::vector<int32_t>>& path,
-                const std::vector<const Seq*>& sv, int32_t bs, int32_t per, Schedule* S) {
+                const std::vector<std::vector<int32_t>>& key, const std::vector<const Seq*>& sv,
+                int32_t bs, int32_t per, Schedule* S) {
   const int32_t n = (int32_t)path.size();
   std::vector<int32_t> run(n, -1), cand;
   for (int32_t i = 0; i < n; ++i) {
@@ -315,9 +318,7 @@ void group_runs(std::vector<Segment>& segs, std::vector<std::vector<int32_t>>& p
     if (runs == 1) cand.push_back(i);
   }
   std::stable_sort(cand.begin(), cand.end(), [&](int32_t a, int32_t b) {
-    const std::vector<int32_t>& x = segs[run[a]].blocks;
-    const std::vector<int32_t>& y = segs[run[b]].blocks;
-    return std::lexicographical_compare(x.begin(), x.end(), y.begin(), y.end());
+    return std::lexicographical_compare(key[a].begin(), key[a].end(), key[b].begin(), key[b].end());
   });
   std::vector<int32_t> group_of(n, -1);
   std::vector<char> dead(segs.size(), 0);
@@ -617,6 +618,7 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
   // from the caches, siblings run side by side) and merging it into one
   // state per branch with the branch's other short segments costs less.
   if (opt.fold_tokens > 0) {
+    const std::vector<std::vector<int32_t>> path0 = opt.group_rows > 0 ? path : decltype(path)();
     std::vector<char> fold(segs.size(), 0);
     bool any = false;
     for (size_t k = 0; k < segs.size(); ++k) {
@@ -667,7 +669,7 @@ int build_decode_schedule(const Pool& pool, const pkv_seq* seqs, int32_t n, int3
       segs = std::move(out);
       S->holders = std::move(holders);
       const int32_t rows = std::min({opt.group_rows, 16, std::max<int32_t>(1, opt.rows_per_item)});
-      if (rows / G >= 2) group_runs(segs, path, sv, bs, rows / G, S);
+      if (rows / G >= 2) group_runs(segs, path, path0, sv, bs, rows / G, S);
     }
   }
   const std::vector<Chunk> chunks = emit_chunks(segs, bs, G, n_layers, d.num_kv_heads, opt, S);
