@@ -203,22 +203,24 @@ GROUPED = [
 
 
 @pytest.mark.parametrize("w", GROUPED, ids=lambda w: w.name)
-@pytest.mark.parametrize("group,pf,st", [(16, 0, 256), (8, 0, 256), (16, 1, 256), (16, 0, 8192),
-                                         (16, 0, 32)],
-                         ids=["rows16", "rows8", "prefetch", "one_wave", "four_waves"])
-def test_grouped_siblings_match_oracle(w, group, pf, st):
+@pytest.mark.parametrize("group,pf,st,chunk", [(16, 0, 256, 0), (8, 0, 256, 0), (16, 1, 256, 0),
+                                               (16, 0, 8192, 0), (16, 0, 32, 0), (16, 0, 256, 64)],
+                         ids=["rows16", "rows8", "prefetch", "one_wave", "four_waves", "split64"])
+def test_grouped_siblings_match_oracle(w, group, pf, st, chunk):
     """Sibling leaves served by one item that reads their blocks once, each
     masked for the rows whose leaf does not hold it (option group_rows):
     the oracle's outputs, and the per-leaf plan's to fp32 rounding; on one
-    wave or four (short_tokens) and with the prefetching loop."""
-    note(f"grouped {w.name} group_rows={group} prefetch={pf} short_tokens={st}")
+    wave or four (short_tokens), with the prefetching loop, and with each
+    group cut into 64-token chunks (each chunk's slice of the block words,
+    partial states and a combine)."""
+    note(f"grouped {w.name} group_rows={group} prefetch={pf} short_tokens={st} chunk={chunk}")
     fold = 128 if w.shape.BS == 64 else 64
-    inp, a = run_decode(w, group=group, prefetch=pf, short_tokens=st, fold=fold)
+    inp, a = run_decode(w, group=group, prefetch=pf, short_tokens=st, fold=fold, chunk_tokens=chunk)
     grouped = PLAN["grouped_items"]
     G = w.shape.Hq // w.shape.Hkv
     # (pairs of the 21-token-edge tree share too little to be grouped)
     assert grouped > 0 if group == 16 else (grouped == 0 or group // G >= 2), (w.name, grouped)
-    _, b = run_decode(w, group=0, prefetch=pf, short_tokens=st, fold=fold)
+    _, b = run_decode(w, group=0, prefetch=pf, short_tokens=st, fold=fold, chunk_tokens=chunk)
     assert PLAN["grouped_items"] == 0
     assert errors(a, b)[0] <= 1e-4
     pool = build_oracle(w, inp)
