@@ -209,7 +209,7 @@ def percentiles(xs):
 
 
 # largest plan the library passes in the kernel launches' own arguments
-INLINE_PLAN_BYTES = 3072
+INLINE_PLAN_BYTES = 12288
 
 
 def side_bytes(sh, n_layers, n_rows, info):
@@ -217,8 +217,9 @@ def side_bytes(sh, n_layers, n_rows, info):
     (n_layers x n_rows x Hq x D in the K/V dtype), the float32 output, the
     float32 partial states (D values + running max and sum per partial row
     and plane, written by attention and read by the combine) and the plan
-    records (in the launch arguments when they fit in 3072 bytes, else
-    copied to the device before the launches)."""
+    records (in the launch arguments when they fit in 12,288 bytes and the
+    combine's lists in 1,024, else copied to the device before the
+    launches)."""
     eb = 2 if sh.dtype == "bf16" else 4
     q = n_layers * n_rows * sh.Hq * sh.D * eb
     out = n_layers * n_rows * sh.Hq * sh.D * 4

@@ -214,7 +214,7 @@ typedef struct {
   int64_t unique_tokens;  /* distinct token slots read per (layer, KV head) */
   int64_t workspace_bytes;
   int64_t plan_bytes;     /* the plan's arrays: carried in the kernel launches'
-                             arguments when at most 3072 bytes (option
+                             arguments when at most 12,288 bytes (option
                              "inline_plan"), else copied into the workspace */
   int64_t wide_tokens;    /* of unique_tokens, those in chunks served by the
                              wide-row launch (the rest: the narrow launch) */
@@ -425,7 +425,7 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       writes the output rows itself: no combine launch; the
  *                       outputs are bit-identical to the combine's (0: always
  *                       combine; also off with "concurrent" 1)
- *   "inline_plan"       1: a decode or verify plan whose arrays fit in 3 KiB (and
+ *   "inline_plan"       1: a decode or verify plan whose arrays fit in 12 KiB (and
  *                       whose combine lists fit in 1 KiB) travels in the kernel
  *                       launches' own arguments, so no host-to-device copy of
  *                       the plan precedes them; outputs are bit-identical either

@@ -40,7 +40,9 @@ def test_side_bytes_of_a_decode():
     assert b["out"] == 32 * 8 * 32 * 128 * 4
     assert b["partials"] == 2 * 64 * 32 * 8 * 130 * 4
     assert b["plan"] == 1632 and b["plan_in_launch_args"]
-    info["plan_bytes"] = 9000
+    info["plan_bytes"] = 12288
+    assert bench.side_bytes(sh, 32, 8, info)["plan_in_launch_args"]
+    info["plan_bytes"] = 12304
     assert not bench.side_bytes(sh, 32, 8, info)["plan_in_launch_args"]
 
 
