@@ -8,6 +8,7 @@ outputs are small (|o| ~ sqrt(e/N)) and 2e-3 alone would be loose.
 
 from __future__ import annotations
 
+import dataclasses
 import sys
 
 import numpy as np
@@ -226,6 +227,24 @@ def test_grouped_siblings_match_oracle(w, group, pf, st, chunk):
     pool = build_oracle(w, inp)
     want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
     check_close(a, want, f"{w.name} grouped rows={group}")
+
+
+def test_grouped_with_repeated_and_reordered_branches():
+    """The batch of the 21-token-edge tree in reverse order with three leaves
+    listed twice: groups follow the leaves' paths, not the batch order, and a
+    repeated leaf is one more holder of the same blocks; the oracle's
+    outputs, and the ungrouped plan's to fp32 rounding."""
+    base = SMALL_DECODE[3]
+    w = dataclasses.replace(base, name="mcts_s_repeated",
+                            query_sids=tuple(reversed(base.query_sids)) + base.query_sids[:3])
+    note(f"grouped {w.name}: {len(w.query_sids)} branches")
+    inp, a = run_decode(w)
+    assert PLAN["grouped_items"] > 0
+    _, b = run_decode(w, group=0)
+    assert errors(a, b)[0] <= 1e-4
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(a, want, f"{w.name} grouped")
 
 
 def test_grouped_forks_with_unequal_valid_counts():
