@@ -336,6 +336,7 @@ def setup_beam(pkv, torch):
     inp = generate(w)
     nb = 128 + 8 * 16 + 8 + 16
     c = pkv.PagedKVCache(nb, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D, dtype=sh.dtype)
+    apply_options(c)
     root_k, root_v = inp.appends[0][2], inp.appends[0][3]
     root = c.create()
     c.append([root], [2048], to_dev(root_k), to_dev(root_v))
@@ -575,6 +576,7 @@ def build_tree(pkv, w, inp, extra_blocks=0):
     sh = w.shape
     c = pkv.PagedKVCache(w.num_blocks_bound() + 8 + extra_blocks, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D,
                          dtype=sh.dtype)
+    apply_options(c)
     kv = {i: (k, v) for i, _s, k, v in inp.appends}
     h = {}
     for i, op in enumerate(w.ops):
@@ -752,6 +754,7 @@ def run_prompt_cache(args, pkv, torch):
     sh = w.shape
     n_sys, n_agents, n_priv = 13312, 4, 32768
     c = pkv.PagedKVCache(w.num_blocks_bound() + 8, sh.BS, sh.L, sh.Hkv, sh.Hq, sh.D, dtype=sh.dtype)
+    apply_options(c)
     rng = np.random.default_rng(3)
     system = rng.integers(0, 32000, size=n_sys).astype(np.int32)
     prompts = [np.concatenate([system, rng.integers(0, 32000, size=n_priv).astype(np.int32)])
@@ -870,6 +873,16 @@ def run_all(args, pkv, torch):
     return head
 
 
+OPTIONS: list = []   # --option key=value, applied to every pool the bench makes
+
+
+def apply_options(c) -> None:
+    """Planner and kernel options given as --option key=value."""
+    for kv in OPTIONS:
+        k, v = kv.split("=", 1)
+        c.set_option(k, int(v))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -878,6 +891,8 @@ def main():
     ap.add_argument("--workload", default="all",
                     choices=["all", "beam", "mcts", "agent", "verify", "prompt_cache"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--option", action="append", default=[], metavar="KEY=VALUE",
+                    help="a pool option (pkv_pool_set_option) for every pool the bench makes")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--secondary", action="store_true",
                     help="also time the same decode as single-layer launches (its launches "
@@ -889,6 +904,7 @@ def main():
                          "of this workload in profiles/traffic.json, then exit (no GPU needed)")
     ap.add_argument("--traffic-source", default="", help="the profile summary to cite")
     args = ap.parse_args()
+    OPTIONS.extend(args.option)
     if args.record_traffic:
         print(json.dumps(record_traffic(args.workload, *args.record_traffic, args.traffic_source)))
         return

@@ -442,6 +442,11 @@ int pkv_prefix_info(const pkv_pool* pool, int32_t* entries, int32_t* evictable);
  *                       picks 2 up to head_dim 128 and 1 at 256 (6 waves, and 8
  *                       at head_dim 256, always own one); a wide item holds at
  *                       most 16 * waves * row blocks rows
+ *   "wide_spec"         0: 1 runs wide items on the kernel whose softmax and P.V
+ *                       run on separate waves of each SIMD (head_dim 64 / 128,
+ *                       bf16, the automatic wide shape) when every wide item
+ *                       holds more than 192 rows; 2 whenever the shape allows;
+ *                       the same partial states to fp32 rounding
  *   "target_workgroups" 256: chunks are shortened (down to 1024 tokens) while the
  *                       grid has fewer than 3/4 of this many workgroups
  *   "tree"              0: never; 1: a decode whose rows all fit one workgroup

@@ -127,6 +127,10 @@ struct pkv_pool {
   int concurrent = 0;  // narrow and wide launches on two streams
   int inline_plan = 1;  // small schedules travel in the launch arguments (no upload)
   int tree_stages = 5;  // LDS ring depth of the tree kernel (4 to 6)
+  // wide items on the kernel with specialised waves (head_dim 64 / 128, the
+  // automatic wide shape): 1 when every wide item fills more than 3/4 of its
+  // 256 rows, 2 whenever the shape allows
+  int wide_spec = 0;
 
   // A second stream (default priority) for the wide launch, so that it runs
   // beside the narrow one; created on first use, on the device current then.
@@ -560,6 +564,17 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
       return hip_fail(e, "hipStreamWaitEvent");
   }
   if (S.n_order_wide > 0) {
+    // the specialised kernel serves 256 rows per workgroup in four pairs of
+    // waves, each pair computing four 16-row blocks whether or not they hold
+    // rows: taken only when every wide item is more than 3/4 full
+    bool use_spec = false;
+    if (p->wide_spec && d.kv_dtype == PKV_BF16 && spec_supported(d.head_dim, d.block_size)) {
+      int w = p->wide_waves, r = p->wide_row_blocks;
+      attn_wide_shape(d.head_dim, &w, &r);
+      use_spec = 16 * w * r == spec_rows();
+      for (size_t i = (size_t)S.n_narrow; use_spec && p->wide_spec == 1 && i < S.items.size(); ++i)
+        use_spec = 4 * S.items[i].n_rows > 3 * spec_rows();
+    }
     AttnParams aw = a;
     aw.n_order = S.n_order_wide;
     rc = p->timed(
@@ -567,6 +582,7 @@ int run_attention(pkv_pool* p, bool mfma, int32_t layer0, const void* q, float* 
         [&](const LaunchEvents& ev) {
           int w = p->wide_waves, r = p->wide_row_blocks;
           attn_wide_shape(d.head_dim, &w, &r);
+          if (use_spec) return launch_attn_spec(d.head_dim, d.block_size, aw, wstream, ev);
           return launch_attn_wide(d.head_dim, d.block_size, w, r, aw, wstream, ev);
         },
         "wide attention launch");
@@ -1175,6 +1191,9 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value) {
     if (value < 0 || value > 2)
       return fail(PKV_E_INVALID, "wide_row_blocks must be 0 (automatic), 1 or 2");
     pool->wide_row_blocks = (int)value;
+  } else if (k == "wide_spec") {
+    if (value < 0 || value > 2) return fail(PKV_E_INVALID, "wide_spec must be 0, 1 or 2");
+    pool->wide_spec = (int)value;
   } else if (k == "wide_fill") {
     if (value < 0 || value > 1) return fail(PKV_E_INVALID, "wide_fill must be 0 or 1");
     pool->opt.wide_fill = value != 0;

@@ -107,6 +107,15 @@ hipError_t launch_attn_wide(int D, int BS, int waves, int row_blocks, const Attn
 // block each. The kernel adds its loader waves.
 void attn_wide_shape(int D, int* waves, int* row_blocks);
 
+// The wide kernel with specialised waves (wide_spec.hip): the same items,
+// grid and partial states as launch_attn_wide, for head_dim 64 / 128 (bf16);
+// each SIMD pairs a wave doing Q.K^T and the softmax with a wave doing P.V
+// and the K/V loads. A workgroup serves up to spec_rows() rows (256).
+bool spec_supported(int D, int BS);
+int spec_rows();
+hipError_t launch_attn_spec(int D, int BS, const AttnParams& p, hipStream_t stream,
+                            const LaunchEvents& ev);
+
 // The tree kernel (tree.hip): one workgroup per (tree item, layer, KV head)
 // reads each chunk of the item once for all rows that hold it and writes
 // the final output rows. stages: LDS ring depth (3 or 4). Built for bf16,

@@ -76,10 +76,11 @@ PLAN = {}   # plan_info of the last run_decode call
 
 def run_decode(w, path=0, chunk_tokens=0, order=None, rows_per_item=None, wide=1, prefetch=0,
                row_blocks=1, wide_shape=None, concurrent=0, short_items=1, short_tokens=256, fold=64,
-               scale=None, inline_plan=1, group=16):
+               scale=None, inline_plan=1, group=16, spec=0):
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("inline_plan", inline_plan)
+    c.set_option("wide_spec", spec)
     c.set_option("fold_tokens", fold)
     c.set_option("group_rows", group)
     c.set_option("concurrent", concurrent)
@@ -497,12 +498,13 @@ def test_random_traces_device_bit_exact(pkv, seed, dtype, bs):
 # ------------------------------------------------------------------ verify
 
 def run_verify(w, order=None, chunk_tokens=0, parents=None, wide_shape=None, scale=None,
-               inline_plan=1):
+               inline_plan=1, spec=0):
     inp = generate(w)
     if parents is not None:
         inp.parents = parents
     c, h = build_library(pytest.pkv, w, inp, alloc_order=order)
     c.set_option("inline_plan", inline_plan)
+    c.set_option("wide_spec", spec)
     if wide_shape:
         c.set_option("wide_waves", wide_shape[0])
         c.set_option("wide_row_blocks", wide_shape[1])
@@ -583,6 +585,60 @@ def test_verify_chain_and_star_trees():
         pool = build_oracle(w, inp)
         want = oracle.verify(pool, w.query_sids, parents, inp.q.f32(), w.softmax_scale)
         check_close(got, want, f"verify {name}")
+
+
+# ------------------------------------- wide kernel with specialised waves
+
+SPEC_DECODE = [
+    SMALL_DECODE[8],   # mcts_wide: a 128-row root (the kernel only when forced)
+    # 32 leaves x G 8: a 256-row root of 301 tokens (ragged last step), 16-token blocks
+    scaled("mcts", "mcts_spec_256rows", shape=replace_shape(B16, L=2, Hq=16, Hkv=2), root_len=301,
+           depth=5, edge_len=19),
+    # 64 leaves x G 4 at head_dim 64, 32-token blocks
+    scaled("mcts", "mcts_spec_d64_bs32", shape=replace_shape(B16, L=2, Hq=8, Hkv=2, D=64, BS=32),
+           root_len=90, depth=6, edge_len=13),
+    # 13 beams x G 16 = 208 rows (three pairs hold a row past the item), 64-token blocks
+    scaled("beam", "beam_spec_bs64", shape=replace_shape(B16, L=1, Hq=16, Hkv=1, BS=64), root_len=200,
+           n_branches=13, branch_len=40),
+]
+
+
+@pytest.mark.parametrize("w", SPEC_DECODE, ids=lambda w: w.name)
+@pytest.mark.parametrize("spec,chunk", [(1, 0), (2, 0), (2, 64)], ids=["auto", "forced", "forced_split64"])
+def test_spec_wide_kernel_matches_oracle(w, spec, chunk):
+    """Wide items on the kernel whose softmax and P.V run on separate waves:
+    the oracle's outputs to tolerance, and the wide kernel's to fp32
+    rounding."""
+    note(f"spec decode {w.name} wide_spec={spec} chunk={chunk}")
+    inp, got = run_decode(w, chunk_tokens=chunk, spec=spec)
+    assert PLAN["n_items"] > 0
+    pool = build_oracle(w, inp)
+    want = oracle.decode(pool, w.query_sids, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"{w.name} wide_spec={spec} chunk={chunk}")
+    _, ref = run_decode(w, chunk_tokens=chunk, spec=0)
+    assert errors(got, ref)[0] <= 1e-4
+
+
+VERIFY_SPEC = scaled("verify", "verify_spec_d128_64nodes", shape=replace_shape(B16, L=1, Hq=8, Hkv=2),
+                     n_req=2, ctx_len=150, n_nodes=64, max_depth=64)
+
+
+@pytest.mark.parametrize("w", [SMALL_VERIFY[1], SMALL_VERIFY[2], SMALL_VERIFY[4], VERIFY_SPEC],
+                         ids=lambda w: w.name)
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_spec_wide_kernel_verify(w, chunk):
+    """Draft-tree verify (ancestor masks) on the kernel with specialised
+    waves, forced for every wide item."""
+    note(f"spec verify {w.name} chunk={chunk}")
+    inp, got = run_verify(w, chunk_tokens=chunk, spec=2)
+    pool = build_oracle(w, inp)
+    want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), w.softmax_scale)
+    check_close(got, want, f"spec verify {w.name} chunk={chunk}")
+    for factor in (-1.0, 0.0):
+        scale = factor * w.softmax_scale
+        inp, got = run_verify(w, chunk_tokens=chunk, spec=2, scale=scale)
+        want = oracle.verify(pool, w.query_sids, inp.parents, inp.q.f32(), scale)
+        check_close(got, want, f"spec verify {w.name} scale {scale:+.4f}")
 
 
 # --------------------------------------------------------- errors, edges

@@ -458,6 +458,11 @@ def test_invalid_handles_and_arguments(pkv):
         binding.pkv_block_refcount(c.handle, 8)    # out of range
     with pytest.raises(pkv.PkvError):
         binding.pkv_pool_set_option(c.handle, "no_such_option", 1)
+    for v in (0, 1, 2):
+        binding.pkv_pool_set_option(c.handle, "wide_spec", v)
+    for v in (-1, 3):
+        with pytest.raises(pkv.PkvError):
+            binding.pkv_pool_set_option(c.handle, "wide_spec", v)
     t = c.create()
     with pytest.raises(pkv.PkvError):
         c.plan(t, -1)
