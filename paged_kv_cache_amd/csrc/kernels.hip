@@ -788,17 +788,32 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
     anc[r] = (tree && row_ok[r]) ? sp.anc[branch] : ~0ull;
   }
 
-  f32x4 acc[RBW][DB];
+  // acc[r][DB] holds the row sums: the products of P against a ones
+  // operand (every output row of such a product is the row sum of P), so
+  // the softmax adds no probabilities itself and the lazy rescale covers
+  // the sums with the accumulators
+  f32x4 acc[RBW][DB + 1];
 #pragma unroll
   for (int r = 0; r < RBW; ++r)
 #pragma unroll
-    for (int j = 0; j < DB; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[RBW], l_run[RBW];
+    for (int j = 0; j <= DB; ++j) acc[r][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[RBW], l_unused[RBW];
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
     m_run[r] = kNegInf;
-    l_run[r] = 0.f;
+    l_unused[r] = 0.f;
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.f;
+  // The row maximum across a row's four lanes is needed only when the
+  // reference moves: when some lane's own maximum passes it by more than 8
+  // (and on a row's first finite scores, where it is -inf).
+  auto reference = [&](const float (&sc)[8], int r) __attribute__((always_inline)) {
+    const float mxl = rmax8_fresh(sc) * p.abs_scale_log2;
+    if (__any(mxl > m_run[r] + 8.f))
+      rebase(max_xor32(max_xor16(mxl)), m_run[r], l_unused[r], acc[r]);
+  };
 
   // Every row block of the wave is computed, also one past the item's last
   // (its query is zero and its state is never stored): a guard per product
@@ -841,10 +856,9 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
               sc[e] = kNegInf;
           }
         }
-        const float mx = max_xor32(max_xor16(rmax8_fresh(sc))) * p.abs_scale_log2;
-        rebase(mx, m_run[r], l_run[r], acc[r]);
+        reference(sc, r);
         const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
-        l_run[r] += probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);
+        (void)probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);
       }
 #pragma unroll
       for (int j = 0; j < DB; ++j) {
@@ -854,6 +868,11 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
           acc[r][j] = mfma_bf16(a, phi[r], acc[r][j]);
           acc[r][j] = mfma_bf16(a, plo[r], acc[r][j]);
         }
+      }
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) {
+        acc[r][DB] = mfma_bf16(ones, phi[r], acc[r][DB]);
+        acc[r][DB] = mfma_bf16(ones, plo[r], acc[r][DB]);
       }
     }
   };
@@ -916,10 +935,9 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
               sc[e] = kNegInf;
           }
         }
-        const float mx = max_xor32(max_xor16(rmax8_fresh(sc))) * p.abs_scale_log2;
-        rebase(mx, m_run[r], l_run[r], acc[r]);
+        reference(sc, r);
         const float m_use = (m_run[r] == kNegInf) ? 0.f : m_run[r];
-        l_run[r] += probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);
+        (void)probs8<true>(sc, p.abs_scale_log2, m_use, phi[r], plo[r]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -933,6 +951,11 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
         }
         if (j + VD < DB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2 * RBW, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < RBW; ++r) {
+        acc[r][DB] = mfma_bf16(ones, phi[r], acc[r][DB]);
+        acc[r][DB] = mfma_bf16(ones, plo[r], acc[r][DB]);
       }
     }
   };
@@ -956,7 +979,7 @@ __global__ __launch_bounds__((NC + wide_loaders<D>()) * 64) void attn_wide_kerne
 #pragma unroll
   for (int r = 0; r < RBW; ++r) {
     if (r >= nrb) continue;
-    const float l_tot = sum_xor32(sum_xor16(l_run[r]));
+    const float l_tot = acc[r][DB][0];
     if (!row_ok[r]) continue;
     const int row = (wave + NC * r) * 16 + n;
     const int64_t prow = (int64_t)(li * p.Hkv + kvh) * p.P + it.part_row + row;
