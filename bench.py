@@ -49,7 +49,7 @@ METRIC = "unique-KV HBM GB/s (% of peak) and branch-queries/sec, paged decode at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-KERNEL_SOURCES = ("kernels.hip", "tree.hip", "kernel_common.h", "attn_plan.h", "schedule.hpp",
+KERNEL_SOURCES = ("kernels.hip", "tree.hip", "wide_spec.hip", "kernel_common.h", "attn_plan.h", "schedule.hpp",
                   "schedule.cpp", "api.cpp")
 
 
