@@ -541,11 +541,13 @@ def calibrate_copy(torch):
     del a, b, flush
 
 
-def ceiling(torch, reps=10) -> dict:
+def ceiling(torch, pkv=None, reps=10) -> dict:
     """What plain device streaming reaches on this GPU, for scale beside the
-    8 TB/s peak: a 2 GiB bf16 reduction (reads 2 GiB) and a 2 GiB copy
-    (reads and writes 2 GiB), torch's own kernels, HIP events, best of reps.
-    Buffers far larger than the 256 MB last-level cache."""
+    8 TB/s peak: the library's streaming read of 2 GiB (pkv_stream_read,
+    16-byte loads over every CU, non-temporal and ordinary), a 2 GiB bf16
+    reduction (reads 2 GiB) and a 2 GiB copy (reads and writes 2 GiB), torch's
+    own kernels; HIP events, best of reps. Buffers far larger than the 256 MB
+    last-level cache."""
     n = 1 << 30
     a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
     b = torch.empty_like(a)
@@ -564,10 +566,20 @@ def ceiling(torch, reps=10) -> dict:
 
     t_read = best(lambda: a.sum(dtype=torch.float32))
     t_copy = best(lambda: b.copy_(a))
+    out = {"read_GB_s": round(2 * n / t_read / 1e9, 1), "copy_GB_s": round(4 * n / t_copy / 1e9, 1),
+           "bytes": 2 * n, "how": "torch.sum over 2 GiB bf16 (read) and a 2 GiB copy (read + write), "
+                                  "best of 10, HIP events"}
+    if pkv is not None:
+        from paged_kv_cache_amd import binding
+        sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+        for key, nt in (("stream_read_nt_GB_s", True), ("stream_read_GB_s", False)):
+            t = best(lambda: binding.pkv_stream_read(a, sink, streaming=nt))
+            out[key] = round(2 * n / t / 1e9, 1)
+        out["how_stream"] = ("pkv_stream_read over the same 2 GiB: 16-byte loads, four in flight per "
+                             "lane, 8192 workgroups each reading a contiguous range; non-temporal (as "
+                             "the attention kernels read K/V that one wave uses) and ordinary loads")
     del a, b
-    return {"read_GB_s": round(2 * n / t_read / 1e9, 1), "copy_GB_s": round(4 * n / t_copy / 1e9, 1),
-            "bytes": 2 * n, "how": "torch.sum over 2 GiB bf16 (read) and a 2 GiB copy (read + write), "
-                                   "best of 10, HIP events"}
+    return out
 
 
 # --------------------------------------------------------- other trees
@@ -869,7 +881,7 @@ def run_all(args, pkv, torch):
         torch.cuda.empty_cache()
     head["configs"] = configs
     note("bench: ceiling")
-    head["ceiling"] = ceiling(torch)
+    head["ceiling"] = ceiling(torch, pkv)
     return head
 
 

@@ -478,6 +478,18 @@ int pkv_pool_set_option(pkv_pool* pool, const char* key, int64_t value);
  * (or call) count, and resets both. */
 int pkv_timing_read(pkv_pool* pool, const char* kernel, double* total_ms, int64_t* launches);
 
+/* Device: reads `bytes` bytes of device memory at src once, with 16-byte
+ * vector loads spread over every CU (8192 workgroups, each a contiguous
+ * range, four loads in flight per lane), on the stream; streaming = 1 uses non-temporal loads (as the attention kernels do
+ * for K/V that only one wave reads), 0 ordinary ones. A measuring aid, not
+ * part of the method: it gives the practical HBM read rate of this GPU to
+ * set the attention launches' rates beside. sink: device memory of at least
+ * 4096 bytes that the kernel may write (its contents afterwards mean
+ * nothing; it keeps the loads from being optimised away). bytes must be a
+ * positive multiple of 16 and src 16-byte aligned (else PKV_E_INVALID,
+ * checked before any device work). */
+int pkv_stream_read(const void* src, int64_t bytes, int32_t streaming, void* sink, void* stream);
+
 /* Last error message of this thread ("" if none). */
 const char* pkv_last_error(void);
 /* Library version string. */

@@ -115,6 +115,7 @@ _PROTOS = {
     "pkv_prefix_info": [c_void_p, POINTER(c_int32), POINTER(c_int32)],
     "pkv_pool_set_option": [c_void_p, c_char_p, c_int64],
     "pkv_timing_read": [c_void_p, c_char_p, POINTER(ctypes.c_double), POINTER(c_int64)],
+    "pkv_stream_read": [c_void_p, c_int64, c_int32, c_void_p, c_void_p],
 }
 _STRING_FUNCS = ("pkv_last_error", "pkv_version")
 

@@ -192,6 +192,14 @@ def pkv_timing_read(pool, kernel: str) -> Tuple[float, int]:
     return ms.value, n.value
 
 
+def pkv_stream_read(src, sink, streaming: bool = True, stream=None) -> None:
+    """Reads the whole of the contiguous device tensor src once (a measuring
+    aid: the practical HBM read rate); sink: a device tensor of >= 4096
+    bytes."""
+    check(lib.pkv_stream_read(_dev_ptr(src), src.numel() * src.element_size(), 1 if streaming else 0,
+                              _dev_ptr(sink), _stream(stream)))
+
+
 def pkv_decode_plan_info(pool, seqs: Sequence[PkvSeq], n_layers: int) -> dict:
     info = PkvPlanInfo()
     check(lib.pkv_decode_plan_info(pool, _seq_array(seqs), len(seqs), n_layers, byref(info)))

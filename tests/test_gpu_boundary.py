@@ -306,3 +306,17 @@ def test_branch_output_does_not_depend_on_the_batch(pkv, w):
     note(f"{w.name}: alone vs batch max |diff| {worst:.3e}")
     assert worst <= 1e-4
     c.close()
+
+
+@pytest.mark.gpu
+def test_stream_read_measuring_aid():
+    """pkv_stream_read reads a whole buffer (ordinary and non-temporal loads)
+    and leaves it unchanged; the bench's read ceiling comes from it."""
+    import torch
+    from paged_kv_cache_amd import binding
+    a = torch.arange(1 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    for nt in (True, False):
+        binding.pkv_stream_read(a, sink, streaming=nt)
+    torch.cuda.synchronize()
+    assert torch.equal(a, torch.arange(1 << 20, dtype=torch.int32, device="cuda"))

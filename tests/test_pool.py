@@ -458,6 +458,10 @@ def test_invalid_handles_and_arguments(pkv):
         binding.pkv_block_refcount(c.handle, 8)    # out of range
     with pytest.raises(pkv.PkvError):
         binding.pkv_pool_set_option(c.handle, "no_such_option", 1)
+    # the streaming-read measuring aid checks its arguments before any device work
+    from paged_kv_cache_amd import _lib
+    for src, nbytes, nt in ((4096, 17, 1), (4096, 0, 1), (4104, 4096, 1), (4096, 4096, 2), (None, 4096, 1)):
+        assert _lib.lib.pkv_stream_read(src, nbytes, nt, 4096, None) == pkv.PKV_E_INVALID
     for v in (0, 1, 2):
         binding.pkv_pool_set_option(c.handle, "wide_spec", v)
     for v in (-1, 3):
