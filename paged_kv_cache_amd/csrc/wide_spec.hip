@@ -11,27 +11,34 @@
 // same four 16-row blocks (64 rows; four pairs, 256 rows):
 //
 //   softmax wave  Q.K^T of step i for its four blocks (each K operand read
-//                 from LDS feeds four products), then per block the row
-//                 maxima, the lazy rebase of the reference (its factor
-//                 alpha per row), the probabilities p = 2^(s c - m) as bf16
-//                 hi + lo, written to LDS with alpha;
+//                 from LDS feeds four products), then the four blocks'
+//                 softmax side by side: the reference moves (with its
+//                 factor alpha per row) only when some lane's own maximum
+//                 passes it by more than 8, the cross-lane row maximum is
+//                 taken only then, and p = 2^(s c - m) goes to LDS as bf16
+//                 hi + lo, with alpha;
 //   P.V wave      in the same interval, P.V of step i - 1: per block the
 //                 accumulators rescaled by alpha when some row moved its
 //                 reference, then hi and lo products against each V
-//                 operand read (each read feeds eight products).
+//                 operand read (each read feeds eight products), and two
+//                 products against a ones operand that give the row sums.
 //
 // Each wave also moves a quarter of the operands the other wave of its pair
 // reads from global memory into LDS (global_load_lds_dwordx4, in operand
 // order, as the wide kernel's loader waves do): P.V waves the K sections,
 // softmax waves the V sections, into two rings of five stages with three
-// steps in flight (one workgroup per CU: with two steps in flight the loads
-// alone held this kernel near 3.2 TB/s). No wave reads the ring its
-// own loads write, so the compiler (which makes a wave wait for its loads
-// into LDS before it reads memory they may write) never holds a read behind
-// loads still in flight. One barrier per step. P and alpha are double-buffered. Softmax waves are the
-// lower wave ids (the SIMD's issue arbiter favours older waves), so a step's
-// score products start first and the P.V products fill the matrix cores
-// while the softmax runs.
+// steps in flight. No wave reads the ring its own loads write, so the
+// compiler (which makes a wave wait for its loads into LDS before it reads
+// memory they may write) never holds a read behind loads still in flight.
+// One barrier per step; P and alpha are double-buffered. Softmax waves take
+// the lower wave ids, so that an arbiter favouring older waves starts a
+// step's score products first.
+//
+// On the MCTS root this measures within 2% of the wide kernel (217.7 against
+// 213.7-214.7 us), so it is an option (wide_spec), not the default: copies
+// with parts removed put the loads and barriers alone at 106 us and the
+// loads with the per-step LDS traffic (operand reads, the P exchange) at
+// 168 us, with the softmax wave's chain on top.
 //
 // Numerics are the wide kernel's: scores unscaled until one FMA folds the
 // scale into the exponent, the reference moved only when a row's maximum
