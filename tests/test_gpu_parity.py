@@ -696,15 +696,16 @@ def test_single_token_returns_its_value(pkv):
 
 # ------------------------------------------------ full-size, sampled outputs
 
-def sampled_decode(name, n_samples=48, seed=0, tree=0):
+def sampled_decode(name, n_samples=48, seed=0, tree=0, spec=0):
     """The full-size decode: one whole layer (every branch and query head,
     drawn at random) and n_samples rows drawn from all layers, against the
     oracle's float64 values."""
     w = get(name)
-    note(f"full-size {name} (tree {tree}): generating inputs")
+    note(f"full-size {name} (tree {tree}, wide_spec {spec}): generating inputs")
     inp = generate(w)
     c, h = build_library(pytest.pkv, w, inp)
     c.set_option("tree", tree)
+    c.set_option("wide_spec", spec)
     seqs = [h[s] for s in w.query_sids]
     q = to_device(inp.q)
     c.set_option("timing", 1)
@@ -743,6 +744,13 @@ def test_full_size_mcts_tree_launch():
     """The MCTS batch through the tree launch (option tree 1 selects it for
     this batch): one whole layer and sampled rows against the oracle."""
     sampled_decode("mcts", seed=3, tree=1)
+
+
+def test_full_size_mcts_specialised_waves():
+    """The MCTS root (256 rows x 4096 tokens per plane) on the kernel with
+    separate softmax and P.V waves (option wide_spec 1 takes it for this
+    batch): one whole layer and sampled rows against the oracle."""
+    sampled_decode("mcts", seed=5, spec=1)
 
 
 def test_full_size_verify_sampled():
