@@ -107,3 +107,22 @@ def test_kernel_hash_ignores_comments_only():
         src[bench.KERNEL_SOURCES[0]] = edit
         assert bench.kernel_source_hash(lambda n: src[n]) != base
     assert bench.code_only('x = "/* kept */"; // gone\ny;') == 'x = "/* kept */"; y;'
+
+
+def test_pool_options_from_the_command_line():
+    """--option key=value (repeatable) reaches every pool the bench makes."""
+    class _Pool:
+        def __init__(self):
+            self.set = []
+
+        def set_option(self, key, value):
+            self.set.append((key, value))
+
+    saved = list(bench.OPTIONS)
+    try:
+        bench.OPTIONS[:] = ["wide_spec=1", "chunk_tokens=64"]
+        c = _Pool()
+        bench.apply_options(c)
+        assert c.set == [("wide_spec", 1), ("chunk_tokens", 64)]
+    finally:
+        bench.OPTIONS[:] = saved
